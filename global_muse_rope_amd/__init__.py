@@ -1,0 +1,212 @@
+"""Python binding of libmuse_attn.so: the Muse Glimmer / Muse Spark Open
+attention layer on MI355X (gfx950).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  There is no
+fallback: without the built library every call raises.
+
+Entry points (same names as the C ABI in include/muse_attn.h):
+    rope_qknorm(layer, q, k, positions=None, out_dtype=torch.bfloat16)
+    prefill(layer, q, k, v, gate, positions=None, out=None, workspace=None)
+    decode(layer, q_new, k_new, v_new, gate, kv_len, max_kv_len, cache, out=None, workspace=None)
+    layer_is_global(i, n_layers)
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+from . import _capi
+from ._capi import MuseError, MUSE_KV_PAGED, MUSE_KV_RING  # noqa: F401
+
+__all__ = ["LayerParams", "KvCache", "rope_qknorm", "prefill", "decode", "layer_is_global",
+           "prefill_workspace_size", "decode_workspace_size", "version", "MuseError"]
+
+
+@dataclass(frozen=True)
+class LayerParams:
+    """One layer's settings; field meanings as muse_attn_params."""
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    sliding_window: int = 0        # 0 = global layer
+    rope_theta: float = 0.0        # 0 = NoPE
+    qk_scale: float = 1.0
+    qk_norm_eps: float = 1e-5
+    out_norm: bool = False
+    out_norm_eps: float = 1e-6
+
+    @classmethod
+    def from_layer(cls, layer) -> "LayerParams":
+        """From an object with hq/hkv/d/window/theta/scale/qk_eps/out_norm/out_eps."""
+        return cls(layer.hq, layer.hkv, layer.d, layer.window, layer.theta, layer.scale,
+                   layer.qk_eps, bool(layer.out_norm), layer.out_eps)
+
+    def c(self) -> _capi.MuseAttnParams:
+        return _capi.MuseAttnParams(self.num_q_heads, self.num_kv_heads, self.head_dim,
+                                    self.sliding_window, self.rope_theta, self.qk_scale,
+                                    self.qk_norm_eps, 1 if self.out_norm else 0, self.out_norm_eps)
+
+
+@dataclass
+class KvCache:
+    """A caller-owned KV cache (see muse_kv_cache).
+
+    ring:  k [B, Hkv, W, D], v [B, Hkv, D, W]
+    paged: k [num_pages, Hkv, page_tokens, D], v [num_pages, Hkv, D, page_tokens],
+           block_table int32 [B, max_pages_per_seq]
+    """
+    kind: int
+    k: "object"
+    v: "object"
+    block_table: Optional["object"] = None
+    page_tokens: int = 0
+
+    @classmethod
+    def ring(cls, k, v):
+        return cls(MUSE_KV_RING, k, v)
+
+    @classmethod
+    def paged(cls, k, v, block_table, page_tokens):
+        return cls(MUSE_KV_PAGED, k, v, block_table, page_tokens)
+
+    def c(self) -> _capi.MuseKvCache:
+        if self.kind == MUSE_KV_RING:
+            return _capi.MuseKvCache(MUSE_KV_RING, int(self.k.shape[2]), self.k.data_ptr(), self.v.data_ptr(),
+                                     None, 0, 0, 0)
+        return _capi.MuseKvCache(MUSE_KV_PAGED, 0, self.k.data_ptr(), self.v.data_ptr(),
+                                 self.block_table.data_ptr(), int(self.block_table.shape[1]),
+                                 int(self.page_tokens), int(self.k.shape[0]))
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _check_bf16(name, t, heads, d):
+    torch = _torch()
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.shape[-1] != d or t.shape[-2] != heads:
+        raise ValueError(f"{name} must end in [{heads}, {d}], got {tuple(t.shape)}")
+    if t.stride(-1) != 1 or t.stride(-2) != d:
+        raise ValueError(f"{name}: heads and dims must be contiguous")
+
+
+def version() -> int:
+    return _capi.load().muse_version()
+
+
+def layer_is_global(i: int, n_layers: int) -> bool:
+    r = _capi.load().muse_layer_is_global(i, n_layers)
+    if r < 0:
+        raise ValueError("layer index out of range")
+    return bool(r)
+
+
+def rope_qknorm(layer: LayerParams, q=None, k=None, positions=None, out_dtype=None):
+    """Weightless QK-norm, query multiplier and (if rope_theta) RoPE.
+    q [T, Hq, D], k [T, Hkv, D] bf16 (token stride free).  Returns (q_hat, k_hat)."""
+    torch = _torch()
+    lib = _capi.load()
+    out_dtype = out_dtype or torch.bfloat16
+    code = {torch.bfloat16: _capi.MUSE_DTYPE_BF16, torch.float16: _capi.MUSE_DTYPE_F16,
+            torch.float32: _capi.MUSE_DTYPE_F32}[out_dtype]
+    ref = q if q is not None else k
+    n = int(ref.shape[0])
+    qo = ko = None
+    if q is not None:
+        _check_bf16("q", q, layer.num_q_heads, layer.head_dim)
+        qo = torch.empty((n, layer.num_q_heads, layer.head_dim), dtype=out_dtype, device=q.device)
+    if k is not None:
+        _check_bf16("k", k, layer.num_kv_heads, layer.head_dim)
+        ko = torch.empty((n, layer.num_kv_heads, layer.head_dim), dtype=out_dtype, device=k.device)
+    if positions is not None:
+        positions = positions.to(dtype=torch.int32).contiguous()
+    p = layer.c()
+    _capi.check(lib.muse_rope_qknorm(
+        ctypes.byref(p), n,
+        q.data_ptr() if q is not None else None, q.stride(0) if q is not None else 0,
+        k.data_ptr() if k is not None else None, k.stride(0) if k is not None else 0,
+        positions.data_ptr() if positions is not None else None,
+        qo.data_ptr() if qo is not None else None, ko.data_ptr() if ko is not None else None,
+        code, _stream()))
+    return qo, ko
+
+
+def prefill_workspace_size(layer: LayerParams, batch: int, seq: int) -> int:
+    p = layer.c()
+    return int(_capi.load().muse_attn_prefill_workspace_size(ctypes.byref(p), batch, seq))
+
+
+def prefill(layer: LayerParams, q, k, v, gate, positions=None, out=None, workspace=None):
+    """The layer over [B, T] tokens: q, gate [B, T, Hq, D]; k, v [B, T, Hkv, D] (bf16).
+    Returns out [B, T, Hq, D] bf16."""
+    torch = _torch()
+    lib = _capi.load()
+    B, T = int(q.shape[0]), int(q.shape[1])
+    _check_bf16("q", q, layer.num_q_heads, layer.head_dim)
+    _check_bf16("k", k, layer.num_kv_heads, layer.head_dim)
+    _check_bf16("v", v, layer.num_kv_heads, layer.head_dim)
+    _check_bf16("gate", gate, layer.num_q_heads, layer.head_dim)
+    for name, t in (("k", k), ("v", v), ("gate", gate)):
+        if int(t.shape[0]) != B or int(t.shape[1]) != T:
+            raise ValueError(f"{name} batch/sequence shape mismatch")
+    if out is None:
+        out = torch.empty((B, T, layer.num_q_heads, layer.head_dim), dtype=torch.bfloat16, device=q.device)
+    _check_bf16("out", out, layer.num_q_heads, layer.head_dim)
+    need = prefill_workspace_size(layer, B, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    strides = (ctypes.c_int64 * 10)(*[int(s) for t in (q, k, v, gate, out) for s in (t.stride(0), t.stride(1))])
+    if positions is not None:
+        positions = positions.to(dtype=torch.int32).contiguous()
+    p = layer.c()
+    _capi.check(lib.muse_attn_prefill(
+        ctypes.byref(p), B, T, q.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr(), strides,
+        positions.data_ptr() if positions is not None else None, out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
+def decode_workspace_size(layer: LayerParams, batch: int, max_kv_len: int, cache: KvCache) -> int:
+    p = layer.c()
+    c = cache.c()
+    return int(_capi.load().muse_attn_decode_workspace_size(ctypes.byref(p), batch, max_kv_len, ctypes.byref(c)))
+
+
+def decode(layer: LayerParams, q_new, k_new, v_new, gate, kv_len, max_kv_len: int, cache: KvCache,
+           out=None, workspace=None):
+    """One decode step: q_new, gate [B, Hq, D]; k_new, v_new [B, Hkv, D] (bf16, contiguous);
+    kv_len int32 device [B] including the new token.  Writes the new entry into the cache
+    and returns out [B, Hq, D] bf16."""
+    torch = _torch()
+    lib = _capi.load()
+    B = int(q_new.shape[0])
+    for name, t, h in (("q_new", q_new, layer.num_q_heads), ("k_new", k_new, layer.num_kv_heads),
+                       ("v_new", v_new, layer.num_kv_heads), ("gate", gate, layer.num_q_heads)):
+        _check_bf16(name, t, h, layer.head_dim)
+        if not t.is_contiguous() or int(t.shape[0]) != B:
+            raise ValueError(f"{name} must be contiguous [B, H, D]")
+    if kv_len.dtype != torch.int32 or not kv_len.is_cuda or kv_len.numel() != B:
+        raise ValueError("kv_len must be a device int32 tensor of B entries")
+    if out is None:
+        out = torch.empty((B, layer.num_q_heads, layer.head_dim), dtype=torch.bfloat16, device=q_new.device)
+    need = decode_workspace_size(layer, B, max_kv_len, cache)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_new.device)
+    p = layer.c()
+    c = cache.c()
+    _capi.check(lib.muse_attn_decode(
+        ctypes.byref(p), B, q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), gate.data_ptr(),
+        kv_len.data_ptr(), int(max_kv_len), ctypes.byref(c), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
+    return out

@@ -1,0 +1,378 @@
+// C ABI: host-side argument checks, workspace sizing and kernel dispatch.
+// Every check runs before any launch; the library keeps no device state.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "kernels.h"
+
+using namespace muse;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t ok() {
+  g_err[0] = '\0';
+  return MUSE_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_arch_mu;
+int g_arch_state[kMaxDevices] = {0};  // 0 unknown, 1 gfx950, 2 other
+
+int32_t check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MUSE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (g_arch_state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    g_arch_state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  if (g_arch_state[dev] != 1) return fail(MUSE_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+  return MUSE_OK;
+}
+
+bool pow2_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8 || g == 16; }
+
+int32_t check_params(const muse_attn_params* p) {
+  if (!p) return fail(MUSE_ERR_INVALID_ARG, "params is NULL");
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(MUSE_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", p->head_dim);
+  if (p->num_q_heads <= 0 || p->num_kv_heads <= 0)
+    return fail(MUSE_ERR_INVALID_ARG, "head counts must be positive");
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(MUSE_ERR_UNSUPPORTED, "num_q_heads %d not a multiple of num_kv_heads %d", p->num_q_heads,
+                p->num_kv_heads);
+  if (!pow2_group(p->num_q_heads / p->num_kv_heads))
+    return fail(MUSE_ERR_UNSUPPORTED, "group size %d not in {1,2,4,8,16}", p->num_q_heads / p->num_kv_heads);
+  if (p->sliding_window < 0) return fail(MUSE_ERR_INVALID_ARG, "sliding_window must be >= 0");
+  if (!(p->rope_theta >= 0.f) || !std::isfinite(p->rope_theta) || (p->rope_theta > 0.f && p->rope_theta <= 1.f))
+    return fail(MUSE_ERR_INVALID_ARG, "rope_theta must be 0 (NoPE) or > 1");
+  if (!std::isfinite(p->qk_scale) || p->qk_scale <= 0.f) return fail(MUSE_ERR_INVALID_ARG, "qk_scale must be > 0");
+  if (!(p->qk_norm_eps > 0.f) || !std::isfinite(p->qk_norm_eps))
+    return fail(MUSE_ERR_INVALID_ARG, "qk_norm_eps must be > 0");
+  if (p->out_norm != 0 && p->out_norm != 1) return fail(MUSE_ERR_INVALID_ARG, "out_norm must be 0 or 1");
+  if (p->out_norm && (!(p->out_norm_eps > 0.f) || !std::isfinite(p->out_norm_eps)))
+    return fail(MUSE_ERR_INVALID_ARG, "out_norm_eps must be > 0");
+  return MUSE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+double log2_theta(const muse_attn_params* p) {
+  return p->rope_theta > 0.f ? std::log2(static_cast<double>(p->rope_theta)) : 0.0;
+}
+
+// s * log2(e) / sqrt(D): q_hat pre-multiplied so logits come out in log2 units.
+float q_logit_scale(const muse_attn_params* p) {
+  return static_cast<float>(static_cast<double>(p->qk_scale) * 1.4426950408889634 /
+                            std::sqrt(static_cast<double>(p->head_dim)));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int64_t prefill_tiles(int32_t T) { return (static_cast<int64_t>(T) + kKeyTile - 1) / kKeyTile; }
+
+size_t prefill_ws(const muse_attn_params* p, int32_t B, int32_t T) {
+  const size_t per = static_cast<size_t>(B) * p->num_kv_heads * prefill_tiles(T) * kKeyTile * p->head_dim * 2;
+  return align256(per) * 2;
+}
+
+struct DecodePlan {
+  int chunk_tokens;
+  int max_chunks;
+};
+
+DecodePlan decode_plan(int32_t max_kv_len, const muse_kv_cache* c) {
+  DecodePlan d;
+  if (c->kind == MUSE_KV_RING) {
+    d.chunk_tokens = c->capacity >= 256 ? 256 : ((c->capacity + 31) / 32) * 32;
+    d.max_chunks = (c->capacity + d.chunk_tokens - 1) / d.chunk_tokens;
+  } else {
+    d.chunk_tokens = 2048;
+    d.max_chunks = (max_kv_len + d.chunk_tokens - 1) / d.chunk_tokens + 1;
+  }
+  return d;
+}
+
+size_t decode_ws(const muse_attn_params* p, int32_t B, int32_t max_kv_len, const muse_kv_cache* c) {
+  const DecodePlan d = decode_plan(max_kv_len, c);
+  const int G = p->num_q_heads / p->num_kv_heads;
+  size_t s = align256(static_cast<size_t>(B) * p->num_q_heads * p->head_dim * 4);
+  s += align256(static_cast<size_t>(B) * p->num_kv_heads * p->head_dim * 4);
+  s += align256(static_cast<size_t>(B) * p->num_kv_heads * d.max_chunks * G * (p->head_dim + 2) * 4);
+  return s;
+}
+
+int32_t check_cache(const muse_attn_params* p, int32_t B, int32_t max_kv_len, const muse_kv_cache* c) {
+  if (!c) return fail(MUSE_ERR_INVALID_ARG, "cache is NULL");
+  if (!c->k || !c->v) return fail(MUSE_ERR_INVALID_ARG, "cache k/v is NULL");
+  if (!aligned16(c->k) || !aligned16(c->v)) return fail(MUSE_ERR_INVALID_ARG, "cache k/v not 16-byte aligned");
+  if (c->kind == MUSE_KV_RING) {
+    if (p->sliding_window <= 0) return fail(MUSE_ERR_INVALID_ARG, "a ring cache needs a local layer (window > 0)");
+    if (c->capacity != p->sliding_window)
+      return fail(MUSE_ERR_INVALID_ARG, "ring capacity %d must equal the window %d", c->capacity, p->sliding_window);
+    if (c->capacity % 16 != 0) return fail(MUSE_ERR_UNSUPPORTED, "ring capacity must be a multiple of 16");
+  } else if (c->kind == MUSE_KV_PAGED) {
+    if (!c->block_table) return fail(MUSE_ERR_INVALID_ARG, "block_table is NULL");
+    if (c->page_tokens <= 0 || c->page_tokens % 16 != 0)
+      return fail(MUSE_ERR_UNSUPPORTED, "page_tokens must be a positive multiple of 16");
+    if (c->max_pages_per_seq <= 0 || c->num_pages <= 0)
+      return fail(MUSE_ERR_INVALID_ARG, "max_pages_per_seq and num_pages must be positive");
+    if (static_cast<int64_t>(max_kv_len) > static_cast<int64_t>(c->max_pages_per_seq) * c->page_tokens)
+      return fail(MUSE_ERR_INVALID_ARG, "max_kv_len %d exceeds block-table capacity %lld", max_kv_len,
+                  static_cast<long long>(c->max_pages_per_seq) * c->page_tokens);
+  } else {
+    return fail(MUSE_ERR_INVALID_ARG, "unknown cache kind %d", c->kind);
+  }
+  (void)B;
+  return MUSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t muse_version(void) { return 100; }
+
+const char* muse_last_error(void) { return g_err; }
+
+int32_t muse_layer_is_global(int32_t i, int32_t n_layers) {
+  if (n_layers <= 0 || i < 0 || i >= n_layers) return -1;
+  return ((n_layers - 1 - i) % 4) == 0 ? 1 : 0;
+}
+
+int32_t muse_rope_qknorm(const muse_attn_params* params, int32_t n_tokens, const void* q, int64_t q_stride_tok,
+                         const void* k, int64_t k_stride_tok, const int32_t* positions, void* q_out, void* k_out,
+                         int32_t out_dtype, void* stream) {
+  int32_t rc = check_params(params);
+  if (rc) return rc;
+  if (n_tokens < 0) return fail(MUSE_ERR_INVALID_ARG, "n_tokens must be >= 0");
+  if (out_dtype != MUSE_DTYPE_BF16 && out_dtype != MUSE_DTYPE_F16 && out_dtype != MUSE_DTYPE_F32)
+    return fail(MUSE_ERR_INVALID_ARG, "out_dtype %d unknown", out_dtype);
+  if (!q && !k) return fail(MUSE_ERR_INVALID_ARG, "q and k are both NULL");
+  if ((q && !q_out) || (k && !k_out)) return fail(MUSE_ERR_INVALID_ARG, "output pointer missing");
+  const int D = params->head_dim;
+  if (q && q_stride_tok < static_cast<int64_t>(params->num_q_heads) * D)
+    return fail(MUSE_ERR_INVALID_ARG, "q_stride_tok smaller than Hq * D");
+  if (k && k_stride_tok < static_cast<int64_t>(params->num_kv_heads) * D)
+    return fail(MUSE_ERR_INVALID_ARG, "k_stride_tok smaller than Hkv * D");
+  if (n_tokens == 0) return ok();
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  RopeQkArgs a{};
+  a.positions = positions;
+  a.eps = params->qk_norm_eps;
+  a.log2_theta = log2_theta(params);
+  a.use_rope = params->rope_theta > 0.f ? 1 : 0;
+  if (q) {
+    a.x = static_cast<const uint16_t*>(q);
+    a.stride_tok = q_stride_tok;
+    a.heads = params->num_q_heads;
+    a.n_rows = static_cast<int64_t>(n_tokens) * params->num_q_heads;
+    a.scale = params->qk_scale;
+    a.out = q_out;
+    hipError_t e = launch_rope_qknorm(D, out_dtype, a, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "rope_qknorm launch: %s", hipGetErrorString(e));
+  }
+  if (k) {
+    a.x = static_cast<const uint16_t*>(k);
+    a.stride_tok = k_stride_tok;
+    a.heads = params->num_kv_heads;
+    a.n_rows = static_cast<int64_t>(n_tokens) * params->num_kv_heads;
+    a.scale = 1.0f;
+    a.out = k_out;
+    hipError_t e = launch_rope_qknorm(D, out_dtype, a, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "rope_qknorm launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+size_t muse_attn_prefill_workspace_size(const muse_attn_params* params, int32_t B, int32_t T) {
+  if (check_params(params) || B < 0 || T < 0) return 0;
+  return prefill_ws(params, B, T);
+}
+
+int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, const void* q, const void* k,
+                          const void* v, const void* gate, const int64_t* strides, const int32_t* positions,
+                          void* out, void* workspace, size_t ws_bytes, void* stream) {
+  int32_t rc = check_params(params);
+  if (rc) return rc;
+  if (B < 0 || T < 0) return fail(MUSE_ERR_INVALID_ARG, "B and T must be >= 0");
+  if (B == 0 || T == 0) return ok();
+  if (!q || !k || !v || !gate || !out) return fail(MUSE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(out))
+    return fail(MUSE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const int D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
+  int64_t s[10];
+  if (strides) {
+    memcpy(s, strides, sizeof(s));
+  } else {
+    const int64_t hs[5] = {static_cast<int64_t>(Hq) * D, static_cast<int64_t>(Hkv) * D,
+                           static_cast<int64_t>(Hkv) * D, static_cast<int64_t>(Hq) * D,
+                           static_cast<int64_t>(Hq) * D};
+    for (int i = 0; i < 5; ++i) {
+      s[2 * i + 1] = hs[i];
+      s[2 * i] = hs[i] * T;
+    }
+  }
+  const int heads_of[5] = {Hq, Hkv, Hkv, Hq, Hq};
+  for (int i = 0; i < 5; ++i) {
+    if (s[2 * i] % 8 || s[2 * i + 1] % 8 || s[2 * i] < 0 || s[2 * i + 1] < 0)
+      return fail(MUSE_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements");
+    if (s[2 * i + 1] < static_cast<int64_t>(heads_of[i]) * D)
+      return fail(MUSE_ERR_INVALID_ARG, "token stride of tensor %d smaller than H * D", i);
+  }
+  if (!workspace || !aligned16(workspace)) return fail(MUSE_ERR_WORKSPACE, "workspace missing or misaligned");
+  const size_t need = prefill_ws(params, B, T);
+  if (ws_bytes < need)
+    return fail(MUSE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t n_tiles = prefill_tiles(T);
+  const size_t half_ws = need / 2;
+  half_t* khat = static_cast<half_t*>(workspace);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + half_ws);
+
+  KvPrepArgs kp{};
+  kp.k = static_cast<const uint16_t*>(k);
+  kp.v = static_cast<const uint16_t*>(v);
+  kp.k_sb = s[2];
+  kp.k_st = s[3];
+  kp.v_sb = s[4];
+  kp.v_st = s[5];
+  kp.positions = positions;
+  kp.T = T;
+  kp.Hkv = Hkv;
+  kp.n_tiles = static_cast<int>(n_tiles);
+  kp.eps = params->qk_norm_eps;
+  kp.log2_theta = log2_theta(params);
+  kp.use_rope = params->rope_theta > 0.f ? 1 : 0;
+  kp.khat = khat;
+  kp.vt = vt;
+  hipError_t e = launch_kv_prep(D, B, kp, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "kv_prep launch: %s", hipGetErrorString(e));
+
+  const int G = Hq / Hkv;
+  const int rows = prefill_rows_per_block(D, G);
+  const int bq = rows / G;
+  const int qgroup = prefill_qblock_group();
+  PrefillArgs pa{};
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.gate = static_cast<const uint16_t*>(gate);
+  pa.out = static_cast<uint16_t*>(out);
+  pa.khat = khat;
+  pa.vt = vt;
+  pa.q_sb = s[0];
+  pa.q_st = s[1];
+  pa.g_sb = s[6];
+  pa.g_st = s[7];
+  pa.o_sb = s[8];
+  pa.o_st = s[9];
+  pa.positions = positions;
+  pa.T = T;
+  pa.Hkv = Hkv;
+  pa.W = params->sliding_window;
+  pa.n_tiles = static_cast<int>(n_tiles);
+  pa.n_qblocks = (T + bq - 1) / bq;
+  pa.n_qblocks_pad = ((pa.n_qblocks + qgroup - 1) / qgroup) * qgroup;
+  pa.batch_heads = B * Hkv;
+  pa.qscale = q_logit_scale(params);
+  pa.qk_eps = params->qk_norm_eps;
+  pa.log2_theta = log2_theta(params);
+  pa.use_rope = params->rope_theta > 0.f ? 1 : 0;
+  pa.out_norm = params->out_norm;
+  pa.out_eps = params->out_norm_eps;
+  if (static_cast<int64_t>(pa.n_qblocks_pad) * pa.batch_heads > 0x7fffffffLL)
+    return fail(MUSE_ERR_UNSUPPORTED, "problem too large for one launch");
+  e = launch_prefill(D, G, pa, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t muse_attn_decode_workspace_size(const muse_attn_params* params, int32_t B, int32_t max_kv_len,
+                                       const muse_kv_cache* cache) {
+  if (check_params(params) || B < 0 || max_kv_len < 1 || !cache) return 0;
+  if (cache->kind == MUSE_KV_RING && cache->capacity <= 0) return 0;
+  return decode_ws(params, B, max_kv_len, cache);
+}
+
+int32_t muse_attn_decode(const muse_attn_params* params, int32_t B, const void* q_new, const void* k_new,
+                         const void* v_new, const void* gate, const int32_t* kv_len, int32_t max_kv_len,
+                         const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  int32_t rc = check_params(params);
+  if (rc) return rc;
+  if (B < 0) return fail(MUSE_ERR_INVALID_ARG, "B must be >= 0");
+  if (max_kv_len < 1) return fail(MUSE_ERR_INVALID_ARG, "max_kv_len must be >= 1");
+  rc = check_cache(params, B, max_kv_len, cache);
+  if (rc) return rc;
+  if (B == 0) return ok();
+  if (!q_new || !k_new || !v_new || !gate || !kv_len || !out)
+    return fail(MUSE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(q_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(gate) || !aligned16(out))
+    return fail(MUSE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (!workspace || !aligned16(workspace)) return fail(MUSE_ERR_WORKSPACE, "workspace missing or misaligned");
+  const size_t need = decode_ws(params, B, max_kv_len, cache);
+  if (ws_bytes < need) return fail(MUSE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  rc = check_device();
+  if (rc) return rc;
+  const DecodePlan plan = decode_plan(max_kv_len, cache);
+  const int D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
+  if (static_cast<int64_t>(B) * Hkv * plan.max_chunks > 0x7fffffffLL)
+    return fail(MUSE_ERR_UNSUPPORTED, "problem too large for one launch");
+  DecodeArgs a{};
+  a.q_new = static_cast<const uint16_t*>(q_new);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.kv_len = kv_len;
+  a.out = static_cast<uint16_t*>(out);
+  a.kc = static_cast<uint16_t*>(cache->k);
+  a.vc = static_cast<uint16_t*>(cache->v);
+  a.block_table = cache->block_table;
+  a.kind = cache->kind;
+  a.capacity = cache->capacity;
+  a.max_pages = cache->max_pages_per_seq;
+  a.page_tokens = cache->page_tokens;
+  a.num_pages = cache->num_pages;
+  a.B = B;
+  a.Hkv = Hkv;
+  a.W = params->sliding_window;
+  a.max_kv_len = max_kv_len;
+  a.chunk_tokens = plan.chunk_tokens;
+  a.max_chunks = plan.max_chunks;
+  a.qscale = q_logit_scale(params);
+  a.qk_eps = params->qk_norm_eps;
+  a.out_eps = params->out_norm_eps;
+  a.log2_theta = log2_theta(params);
+  a.use_rope = params->rope_theta > 0.f ? 1 : 0;
+  a.out_norm = params->out_norm;
+  char* ws = static_cast<char*>(workspace);
+  a.qhat = reinterpret_cast<float*>(ws);
+  ws += align256(static_cast<size_t>(B) * Hq * D * 4);
+  a.khat = reinterpret_cast<float*>(ws);
+  ws += align256(static_cast<size_t>(B) * Hkv * D * 4);
+  a.part = reinterpret_cast<float*>(ws);
+  hipError_t e = launch_decode(D, Hq / Hkv, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

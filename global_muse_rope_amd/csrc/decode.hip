@@ -1,0 +1,427 @@
+// Decode: one new token per sequence against a ring (local layer) or paged
+// (global layer) KV cache.
+//
+// What it computes (Muse Spark Open deep dive): the new token's q and k get
+// the weightless QK-norm, the query multiplier and (local layers) RoPE at
+// position p = kv_len - 1 (section 3.2 steps 2-4, section 3.4); the cache is
+// updated after those steps (section 3.2 notes), a local layer keeps the W
+// most recent entries (section 3.4 mask and cache notes, section 7.2), and
+// the query attends to every visible entry (GQA, section 3.1), followed by
+// Spark's per-head output norm and the sigmoid gate (section 3.3).
+//
+// Three kernels on the caller's stream:
+//   1. append: prologue of the new token; q_hat (fp32, in log2 units) and
+//      k_hat (fp32) to the workspace, k_hat and v (bf16) into the cache slot;
+//   2. split: a grid of (sequence, KV head, chunk of cached entries) items;
+//      each streams its chunk's K and V with 16-byte loads straight into MFMA
+//      operands and keeps a running maximum (the cache is caller data, so no
+//      bound on its logits is assumed); partial (max, sum, O) per item;
+//   3. combine: merges the partials with the new token's own term (computed
+//      in fp32 from the workspace copies), then output norm and gate.
+// Both contractions run on v_mfma_f32_16x16x32_bf16.  To keep fp32 accuracy
+// with bf16 operands, q_hat and p are split into hi + lo bf16 parts whose two
+// products accumulate into the same fp32 registers (the MFMA work this
+// doubles is far below the HBM roofline that bounds decode).
+#include "kernels.h"
+
+namespace muse {
+
+__device__ __forceinline__ bool decode_len_ok(int L, int max_len) { return L >= 1 && L <= max_len; }
+
+// ---------------------------------------------------------------------------
+// 1. append
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void decode_append_kernel(DecodeArgs a, int hq_total) {
+  constexpr int LPR = D / 2;
+  const int b = blockIdx.y;
+  const int L = a.kv_len[b];
+  const bool len_ok = decode_len_ok(L, a.max_kv_len);
+  const int gt = blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = gt / LPR;              // 0 .. Hq-1: queries; Hq .. Hq+Hkv-1: keys
+  const int j = gt % LPR;
+  const int rows = hq_total + a.Hkv;
+  const bool valid = row < rows;
+  const bool is_q = row < hq_total;
+  const int h = is_q ? row : row - hq_total;
+  float x0 = 0.f, x1 = 0.f;
+  if (valid) {
+    const uint16_t* p = is_q ? a.q_new + (static_cast<int64_t>(b) * hq_total + h) * D
+                             : a.k_new + (static_cast<int64_t>(b) * a.Hkv + h) * D;
+    x0 = bf16_bits_to_f32(p[j]);
+    x1 = bf16_bits_to_f32(p[j + D / 2]);
+  }
+  const float ss = group_sum<LPR>(x0 * x0 + x1 * x1);
+  const float r = (is_q ? a.qscale : 1.0f) / sqrtf(ss * (1.0f / D) + a.qk_eps);
+  x0 *= r;
+  x1 *= r;
+  const int pos = len_ok ? L - 1 : 0;
+  if (a.use_rope) {
+    float s, c;
+    rope_sincos(pos, j, D, a.log2_theta, &s, &c);
+    const float y0 = x0 * c - x1 * s;
+    const float y1 = x1 * c + x0 * s;
+    x0 = y0;
+    x1 = y1;
+  }
+  if (!valid) return;
+  if (is_q) {
+    float* qo = a.qhat + (static_cast<int64_t>(b) * hq_total + h) * D;
+    qo[j] = x0;
+    qo[j + D / 2] = x1;
+    return;
+  }
+  float* ko = a.khat + (static_cast<int64_t>(b) * a.Hkv + h) * D;
+  ko[j] = x0;
+  ko[j + D / 2] = x1;
+  if (!len_ok) return;
+  // cache write: k_hat row (token-major) and v column (head-dim-major)
+  const uint16_t* vp = a.v_new + (static_cast<int64_t>(b) * a.Hkv + h) * D;
+  int64_t kbase, vbase, vstride;
+  if (a.kind == MUSE_KV_RING) {
+    const int slot = pos % a.capacity;
+    kbase = ((static_cast<int64_t>(b) * a.Hkv + h) * a.capacity + slot) * D;
+    vbase = (static_cast<int64_t>(b) * a.Hkv + h) * D * a.capacity + slot;
+    vstride = a.capacity;
+  } else {
+    const int pi = pos / a.page_tokens;
+    const int rr = pos % a.page_tokens;
+    const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + pi];
+    if (page < 0 || page >= a.num_pages) return;
+    kbase = ((page * a.Hkv + h) * a.page_tokens + rr) * D;
+    vbase = (page * a.Hkv + h) * D * a.page_tokens + rr;
+    vstride = a.page_tokens;
+  }
+  a.kc[kbase + j] = f32_to_bf16_bits(x0);
+  a.kc[kbase + j + D / 2] = f32_to_bf16_bits(x1);
+  a.vc[vbase + static_cast<int64_t>(j) * vstride] = vp[j];
+  a.vc[vbase + static_cast<int64_t>(j + D / 2) * vstride] = vp[j + D / 2];
+}
+
+// Visible cached entries of sequence b, as an index range with a validity test.
+struct HistRange {
+  int base;   // first index of chunk 0
+  int end;    // indices < end may be valid
+  int lo;     // paged: first visible position
+  int skip;   // ring: slot holding the new token (excluded), or -1
+};
+
+__device__ __forceinline__ HistRange hist_range(const DecodeArgs& a, int L) {
+  HistRange r;
+  if (a.kind == MUSE_KV_RING) {
+    r.base = 0;
+    r.lo = 0;
+    if (L >= a.capacity) {
+      r.end = a.capacity;
+      r.skip = (L - 1) % a.capacity;
+    } else {
+      r.end = L - 1;
+      r.skip = -1;
+    }
+  } else {
+    r.lo = a.W > 0 ? max(0, L - a.W) : 0;
+    r.base = (r.lo / a.chunk_tokens) * a.chunk_tokens;
+    r.end = L - 1;
+    r.skip = -1;
+  }
+  return r;
+}
+
+__device__ __forceinline__ int hist_chunks(const HistRange& r, int chunk_tokens) {
+  return r.end > r.base ? (r.end - r.base + chunk_tokens - 1) / chunk_tokens : 0;
+}
+
+__device__ __forceinline__ bool hist_valid(const HistRange& r, int idx) {
+  return idx < r.end && idx >= r.lo && idx != r.skip;
+}
+
+// ---------------------------------------------------------------------------
+// 2. split
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+  constexpr int NW = 4;
+  constexpr int DS = D / 32;  // dim steps of QK^T
+  constexpr int DB = D / 16;  // dim blocks of O^T
+  constexpr float NEG = -1.0e30f;
+  __shared__ float sm_m[NW][16];
+  __shared__ float sm_l[NW][16];
+  __shared__ float sm_o[NW][16][D + 1];
+
+  const int item = blockIdx.x;
+  const int c = item % a.max_chunks;
+  const int bh = item / a.max_chunks;
+  const int b = bh / a.Hkv;
+  const int hk = bh - b * a.Hkv;
+  const int L = a.kv_len[b];
+  if (!decode_len_ok(L, a.max_kv_len)) return;
+  const HistRange hr = hist_range(a, L);
+  if (c >= hist_chunks(hr, a.chunk_tokens)) return;
+  const int c0 = hr.base + c * a.chunk_tokens;
+  const int c1 = min(c0 + a.chunk_tokens, hr.end);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;  // query head within the group (columns >= G are padding)
+  const int g4 = lane >> 4;   // 0..3
+
+  // q_hat hi/lo operands (B of S^T = K Q^T): head col, dims 8*g4 + 32*ds + [0, 8)
+  bf16x8 qhi[DS], qlo[DS];
+  {
+    const float* qp = a.qhat + (static_cast<int64_t>(b) * (a.Hkv * G) + hk * G + (col < G ? col : 0)) * D;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = col < G ? qp[32 * ds + 8 * g4 + e] : 0.f;
+        const bf16_t hi = static_cast<bf16_t>(x);
+        qhi[ds][e] = hi;
+        qlo[ds][e] = static_cast<bf16_t>(x - static_cast<float>(hi));
+      }
+  }
+
+  const uint16_t* kc = a.kc;
+  const uint16_t* vc = a.vc;
+  // address of (cached index idx) for this (b, hk): K row and V^T column
+  auto kaddr = [&](int idx) -> int64_t {
+    if (a.kind == MUSE_KV_RING) return ((static_cast<int64_t>(bh)) * a.capacity + idx) * D;
+    const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + idx / a.page_tokens];
+    return ((page * a.Hkv + hk) * a.page_tokens + idx % a.page_tokens) * D;
+  };
+  auto vaddr = [&](int idx) -> int64_t {  // element (dim 0, idx); dim stride = vstride
+    if (a.kind == MUSE_KV_RING) return static_cast<int64_t>(bh) * D * a.capacity + idx;
+    const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + idx / a.page_tokens];
+    return (page * a.Hkv + hk) * D * a.page_tokens + idx % a.page_tokens;
+  };
+  auto tile_ok = [&](int idx0) -> bool {  // 16-key tile starting at idx0 may be loaded
+    if (idx0 >= hr.end) return false;
+    if (a.kind == MUSE_KV_RING) return true;
+    const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + idx0 / a.page_tokens];
+    return page >= 0 && page < a.num_pages;
+  };
+  const int vstride = a.kind == MUSE_KV_RING ? a.capacity : a.page_tokens;
+
+  float m = NEG, lsum = 0.f;
+  f32x4 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // register prefetch of one 32-key sub-chunk
+  u32x4 kr[2][DS];
+  u32x2 vr[DB][2];
+  auto load = [&](int s0) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int idx0 = s0 + 16 * kt;
+      const bool ok = tile_ok(idx0);
+      const int64_t ka = ok ? kaddr(idx0 + col) : 0;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        kr[kt][ds] = ok ? *reinterpret_cast<const u32x4*>(kc + ka + 32 * ds + 8 * g4) : u32x4{0, 0, 0, 0};
+      const int64_t va = ok ? vaddr(idx0 + 4 * g4) : 0;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        vr[db][kt] = ok ? *reinterpret_cast<const u32x2*>(vc + va + static_cast<int64_t>(16 * db + col) * vstride)
+                        : u32x2{0, 0};
+    }
+  };
+
+  const int nsub = (c1 - c0 + 31) / 32;
+  if (w < nsub) load(c0 + 32 * w);
+  for (int sc = w; sc < nsub; sc += NW) {
+    const int s0 = c0 + 32 * sc;
+    u32x4 kcur[2][DS];
+    u32x2 vcur[DB][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) kcur[kt][ds] = kr[kt][ds];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      vcur[db][0] = vr[db][0];
+      vcur[db][1] = vr[db][1];
+    }
+    if (sc + NW < nsub) load(c0 + 32 * (sc + NW));
+
+    // S^T tiles: keys s0 + 16*kt + 4*g4 + i, head col
+    float s[2][4];
+    float tmax = NEG;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, kcur[kt][ds]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qhi[ds], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[ds], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int idx = s0 + 16 * kt + 4 * g4 + i;
+        s[kt][i] = hist_valid(hr, idx) ? acc[i] : NEG;
+        tmax = fmaxf(tmax, s[kt][i]);
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float mnew = fmaxf(m, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    bf16x8 phi, plo;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = s[kt][i] > NEG ? __builtin_amdgcn_exp2f(s[kt][i] - mnew) : 0.f;
+        psum += p;
+        const bf16_t hi = static_cast<bf16_t>(p);
+        phi[4 * kt + i] = hi;
+        plo[4 * kt + i] = static_cast<bf16_t>(p - static_cast<float>(hi));
+      }
+    lsum = lsum * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      o[db] *= alpha;
+      u32x4 vw = {vcur[db][0][0], vcur[db][0][1], vcur[db][1][0], vcur[db][1][1]};
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, vw);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[db], 0, 0, 0);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[db], 0, 0, 0);
+    }
+  }
+  lsum += __shfl_xor(lsum, 16, kWave);
+  lsum += __shfl_xor(lsum, 32, kWave);
+
+  // merge the waves' partials
+  if (g4 == 0) {
+    sm_m[w][col] = m;
+    sm_l[w][col] = lsum;
+  }
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm_o[w][col][16 * db + 4 * g4 + i] = o[db][i];
+  __syncthreads();
+  float* part = a.part + (static_cast<int64_t>(bh) * a.max_chunks + c) * (G * (D + 2));
+  for (int e = tid; e < G * D; e += 256) {
+    const int h = e / D, d = e % D;
+    float mm = NEG;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) mm = fmaxf(mm, sm_m[ww][h]);
+    float acc = 0.f, ls = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = sm_m[ww][h] > NEG ? __builtin_amdgcn_exp2f(sm_m[ww][h] - mm) : 0.f;
+      acc += f * sm_o[ww][h][d];
+      ls += f * sm_l[ww][h];
+    }
+    part[h * (D + 2) + d] = acc;
+    if (d == 0) {
+      part[h * (D + 2) + D] = mm;
+      part[h * (D + 2) + D + 1] = ls;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. combine + epilogue: one workgroup per (sequence, KV head); wave w takes
+// heads w, w + 4, ...; lane = dim (two dims per lane when D = 128).
+// ---------------------------------------------------------------------------
+template <int D, int G>
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int PER = D / 64;
+  constexpr float NEG = -1.0e30f;
+  const int bh = blockIdx.x;
+  const int b = bh / a.Hkv;
+  const int hk = bh - b * a.Hkv;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int L = a.kv_len[b];
+  const bool len_ok = decode_len_ok(L, a.max_kv_len);
+  const int nch = len_ok ? hist_chunks(hist_range(a, L), a.chunk_tokens) : 0;
+  const float* kn = a.khat + static_cast<int64_t>(bh) * D;
+  const uint16_t* vn = a.v_new + static_cast<int64_t>(bh) * D;
+  for (int hh = w; hh < G; hh += 4) {
+    const int hq = hk * G + hh;
+    const float* qp = a.qhat + (static_cast<int64_t>(b) * a.Hkv * G + hq) * D;
+    // the new token's own logit (log2 units) and value
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dot += qp[lane + 64 * e] * kn[lane + 64 * e];
+    const float snew = wave_sum(dot);
+    float mm = snew;
+    const float* part = a.part + static_cast<int64_t>(bh) * a.max_chunks * (G * (D + 2)) + hh * (D + 2);
+    for (int ci = 0; ci < nch; ++ci) mm = fmaxf(mm, part[static_cast<int64_t>(ci) * G * (D + 2) + D]);
+    const float fnew = __builtin_amdgcn_exp2f(snew - mm);
+    float ls = fnew;
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = fnew * bf16_bits_to_f32(vn[lane + 64 * e]);
+    for (int ci = 0; ci < nch; ++ci) {
+      const float* pc = part + static_cast<int64_t>(ci) * G * (D + 2);
+      const float mc = pc[D];
+      const float f = mc > NEG ? __builtin_amdgcn_exp2f(mc - mm) : 0.f;
+      ls += f * pc[D + 1];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += f * pc[lane + 64 * e];
+    }
+    const float inv = 1.0f / ls;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      acc[e] *= inv;
+      ss += acc[e] * acc[e];
+    }
+    float rsn = 1.0f;
+    if (a.out_norm) rsn = 1.0f / sqrtf(wave_sum(ss) * (1.0f / D) + a.out_eps);
+    const uint16_t* gp = a.gate + (static_cast<int64_t>(b) * a.Hkv * G + hq) * D;
+    uint16_t* op = a.out + (static_cast<int64_t>(b) * a.Hkv * G + hq) * D;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float g = bf16_bits_to_f32(gp[lane + 64 * e]);
+      const float y = len_ok ? acc[e] * rsn / (1.0f + __expf(-g)) : 0.f;
+      op[lane + 64 * e] = f32_to_bf16_bits(y);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+namespace {
+template <int D, int G>
+hipError_t launch_dg(const DecodeArgs& a, hipStream_t st) {
+  const int hq = a.Hkv * G;
+  const int rows = hq + a.Hkv;
+  const int threads = rows * (D / 2);
+  dim3 g1((threads + 255) / 256, a.B);
+  hipLaunchKernelGGL((decode_append_kernel<D>), g1, dim3(256), 0, st, a, hq);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned items = static_cast<unsigned>(a.B) * a.Hkv * a.max_chunks;
+  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(items), dim3(256), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_combine_kernel<D, G>), dim3(a.B * a.Hkv), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(int g, const DecodeArgs& a, hipStream_t st) {
+  switch (g) {
+    case 1: return launch_dg<D, 1>(a, st);
+    case 2: return launch_dg<D, 2>(a, st);
+    case 4: return launch_dg<D, 4>(a, st);
+    case 8: return launch_dg<D, 8>(a, st);
+    case 16: return launch_dg<D, 16>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+}  // namespace
+
+hipError_t launch_decode(int d, int g, const DecodeArgs& a, hipStream_t st) {
+  return d == 64 ? launch_d<64>(g, a, st) : launch_d<128>(g, a, st);
+}
+
+}  // namespace muse

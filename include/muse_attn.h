@@ -1,0 +1,173 @@
+/*
+ * muse_attn.h - C ABI of the MI355X (gfx950) attention library for the
+ * Muse Glimmer / Muse Spark Open attention layer.
+ *
+ * The layer (Muse Spark Open deep dive, gangliao.me, section 3 and its
+ * subsections 3.1-3.4; the normalization-and-gates audit on flozi.net):
+ *   - grouped-query attention, query head h reads KV head floor(h / G),
+ *     G = num_q_heads / num_kv_heads (section 3.1);
+ *   - weightless per-head RMS norm of q and k, x / sqrt(mean(x^2) + eps),
+ *     then q multiplied by the fixed qk_scale_factor, logits keep the usual
+ *     1/sqrt(D) (section 3.2, the five-step forward order);
+ *   - RoPE only on local layers: dimension j paired with j + D/2, angle
+ *     position * theta^(-2j/D); global layers are NoPE (section 3.4);
+ *   - causal mask: key j visible to query i iff j <= i and, on a local layer
+ *     with window W, j > i - W (section 3.4, mask note);
+ *   - Spark only: weightless RMS norm of each head's D outputs, then for both
+ *     models the elementwise gate y = o * sigmoid(g) (section 3.3).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (HIP device memory) unless a
+ *     parameter says "host".  Tensors are bf16 unless stated.  Within one
+ *     head a vector of D elements is contiguous; heads of one token are
+ *     contiguous (head stride D).  Pointers must be 16-byte aligned and
+ *     token/batch strides multiples of 8 elements.
+ *   - The caller owns and allocates every buffer, including the workspace;
+ *     the library allocates and frees nothing and keeps no device state
+ *     between calls.  `stream` is a hipStream_t (0 = the null stream).
+ *   - Every argument check runs on the host before any launch; on failure
+ *     nothing is enqueued and the call returns a status code, with a message
+ *     available from muse_last_error() (thread-local).  Calls are
+ *     asynchronous: success means the work was enqueued on `stream`.
+ *   - Supported shapes: head_dim 64 or 128; num_q_heads a multiple of
+ *     num_kv_heads with G = num_q_heads / num_kv_heads in {1, 2, 4, 8, 16};
+ *     the device must be gfx950.
+ */
+#ifndef MUSE_ATTN_H
+#define MUSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum muse_status {
+  MUSE_OK = 0,
+  MUSE_ERR_INVALID_ARG = 1,   /* null pointer, bad size, stride or alignment */
+  MUSE_ERR_UNSUPPORTED = 2,   /* head_dim, group size or device arch not supported */
+  MUSE_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the size query */
+  MUSE_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
+} muse_status;
+
+enum { MUSE_DTYPE_BF16 = 0, MUSE_DTYPE_F16 = 1, MUSE_DTYPE_F32 = 2 };
+enum { MUSE_KV_RING = 0, MUSE_KV_PAGED = 1 };
+
+/* One attention layer's settings, named after the models' config keys
+ * (deep dive, section 1.2 table): num_attention_heads, num_key_value_heads,
+ * head_dim, sliding_window, layer_rope_theta, qk_scale_factor, rms_norm_eps. */
+typedef struct muse_attn_params {
+  int32_t num_q_heads;    /* Hq: 32 (Glimmer) or 128 (Spark) */
+  int32_t num_kv_heads;   /* Hkv: 2 (Glimmer) or 16 (Spark) */
+  int32_t head_dim;       /* D: 128 (Glimmer) or 64 (Spark) */
+  int32_t sliding_window; /* W > 0: local layer; 0: global layer (full causal) */
+  float rope_theta;       /* RoPE base; 0 = NoPE (no rotation), as layer_rope_theta */
+  float qk_scale;         /* query multiplier s: 3.87 or 5.4730064863875 */
+  float qk_norm_eps;      /* eps of the weightless QK-norm, 1e-5 */
+  int32_t out_norm;       /* 1: per-head weightless output RMS norm (Spark); 0: none */
+  float out_norm_eps;     /* eps of the output norm */
+} muse_attn_params;
+
+/* Caller-owned KV cache of one layer, holding keys AFTER norm and RoPE (the
+ * cache is updated after those steps: deep dive, section 3.2 notes), bf16.
+ *
+ * MUSE_KV_RING (local layers): k is [B, Hkv, capacity, D]; v is stored
+ *   transposed per head, [B, Hkv, D, capacity].  Position p lives in slot
+ *   p mod capacity; capacity must equal the layer's window W, so once the
+ *   new token is written the ring holds exactly the W visible entries.
+ * MUSE_KV_PAGED (global layers): a pool of pages, each page holding
+ *   page_tokens consecutive positions of every KV head.  k is
+ *   [num_pages, Hkv, page_tokens, D]; v is [num_pages, Hkv, D, page_tokens].
+ *   Position p of sequence b lives in page block_table[b * max_pages_per_seq
+ *   + p / page_tokens], row p mod page_tokens.  With D = 64 and
+ *   page_tokens = 32 each (page, head) slice of K (or V) is 4 KiB.
+ * V is head-dim-major inside a page (and inside a ring head) so that both
+ * contractions read contiguous runs along their reduction axis. */
+typedef struct muse_kv_cache {
+  int32_t kind;                /* MUSE_KV_RING or MUSE_KV_PAGED */
+  int32_t capacity;            /* RING: entries per (sequence, head); must equal W */
+  void* k;                     /* device, bf16 */
+  void* v;                     /* device, bf16 */
+  const int32_t* block_table;  /* PAGED: device int32 [B, max_pages_per_seq] */
+  int32_t max_pages_per_seq;   /* PAGED: row length of block_table */
+  int32_t page_tokens;         /* PAGED: positions per page, a multiple of 16 */
+  int64_t num_pages;           /* PAGED: pages in the pool (block_table entries must be < this) */
+} muse_kv_cache;
+
+/* muse_rope_qknorm: the layer's prologue on its own (deep dive, section 3.2
+ * steps 2-4 and section 3.4).
+ *   q_hat = s * q / sqrt(mean(q^2) + eps), k_hat = k / sqrt(mean(k^2) + eps),
+ *   then, if rope_theta != 0, both rotated by their token's position.
+ * q: [n_tokens, Hq, D] bf16 with token stride q_stride_tok (elements);
+ * k: [n_tokens, Hkv, D] bf16 with token stride k_stride_tok;
+ * positions: device int32 [n_tokens], or NULL for 0 .. n_tokens-1;
+ * q_out: [n_tokens, Hq, D], k_out: [n_tokens, Hkv, D], contiguous, in
+ *   out_dtype (MUSE_DTYPE_BF16, _F16 or _F32), rounded to nearest even.
+ * Either q (with q_out) or k (with k_out) may be NULL to process only the
+ * other.  n_tokens == 0 is a no-op. */
+int32_t muse_rope_qknorm(const muse_attn_params* params, int32_t n_tokens,
+                         const void* q, int64_t q_stride_tok,
+                         const void* k, int64_t k_stride_tok,
+                         const int32_t* positions,
+                         void* q_out, void* k_out, int32_t out_dtype,
+                         void* stream);
+
+/* muse_attn_prefill: the whole layer over B causal sequences of T tokens
+ * (section 3.2 forward order, the mask of section 3.4 and the gate and
+ * output norm of section 3.3), after the q/k/v/gate projections and before
+ * o_proj.
+ * q, gate: [B, T, Hq, D]; k, v: [B, T, Hkv, D]; out: [B, T, Hq, D]; bf16.
+ * strides: host int64[10] = {batch, token} strides in elements of q, k, v,
+ *   gate, out in that order, or NULL for contiguous tensors.
+ * positions: device int32 [B, T] RoPE positions, or NULL for 0 .. T-1.  The
+ *   mask always uses the token index inside the sequence.
+ * workspace: device scratch of at least muse_attn_prefill_workspace_size()
+ *   bytes (16-byte aligned), clobbered by the call.
+ * T == 0 or B == 0 is a no-op. */
+int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T,
+                          const void* q, const void* k, const void* v, const void* gate,
+                          const int64_t* strides, const int32_t* positions,
+                          void* out, void* workspace, size_t ws_bytes, void* stream);
+
+size_t muse_attn_prefill_workspace_size(const muse_attn_params* params, int32_t B, int32_t T);
+
+/* muse_attn_decode: one new token per sequence against a KV cache.
+ * q_new, gate, out: [B, Hq, D]; k_new, v_new: [B, Hkv, D]; contiguous bf16.
+ * kv_len: device int32 [B], the sequence length INCLUDING the new token;
+ *   the new token's position is kv_len[b] - 1.  Every kv_len[b] must lie in
+ *   [1, max_kv_len]; a sequence outside that range gets zero output and no
+ *   cache write.
+ * max_kv_len: host upper bound on kv_len (sizes the launch); for a PAGED
+ *   cache it must not exceed max_pages_per_seq * page_tokens.
+ * The call writes the new token's normalized (and, on local layers, rotated)
+ * key and its value into the cache in place, then attends the query to the
+ * visible cached entries plus the new token (global: positions 0 .. p;
+ * local: p - W < j <= p).  The new token's own key and value enter the
+ * softmax at full fp32 precision; cached entries as stored (bf16).
+ * workspace: at least muse_attn_decode_workspace_size() bytes. */
+int32_t muse_attn_decode(const muse_attn_params* params, int32_t B,
+                         const void* q_new, const void* k_new, const void* v_new,
+                         const void* gate, const int32_t* kv_len, int32_t max_kv_len,
+                         const muse_kv_cache* cache, void* out,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+size_t muse_attn_decode_workspace_size(const muse_attn_params* params, int32_t B,
+                                       int32_t max_kv_len, const muse_kv_cache* cache);
+
+/* Layer schedule: layer i of n_layers is global (full attention, NoPE) iff
+ * (n_layers - 1 - i) mod 4 == 0 (deep dive, section 2.2 equation).
+ * Returns 1 (global), 0 (local) or -1 for i outside [0, n_layers). */
+int32_t muse_layer_is_global(int32_t layer_index, int32_t n_layers);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* muse_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t muse_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUSE_ATTN_H */

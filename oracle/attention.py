@@ -75,6 +75,8 @@ def rope_rotate(x, positions, theta: float) -> np.ndarray:
     d = x.shape[-1]
     half = d // 2
     pos = np.asarray(positions, dtype=np.float64)
+    if pos.ndim != 1 or pos.shape[0] != x.shape[0]:
+        raise ValueError("positions must hold one entry per token (leading axis of x)")
     ang = pos[:, None] * rope_inv_freq(d, theta)[None, :]      # [T, D/2]
     c = np.cos(ang)[:, None, :]
     s = np.sin(ang)[:, None, :]

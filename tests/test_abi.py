@@ -1,0 +1,162 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a device (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muse_attn.h")
+
+
+def _lib():
+    from global_muse_rope_amd import _capi
+    if not os.path.exists(_capi.LIB_PATH):
+        from global_muse_rope_amd import build_lib
+        build_lib.build()
+    return _capi, _capi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(muse_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ["muse_rope_qknorm", "muse_attn_prefill", "muse_attn_decode",
+                     "muse_attn_prefill_workspace_size", "muse_attn_decode_workspace_size",
+                     "muse_layer_is_global", "muse_last_error", "muse_version"]:
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    capi, lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in capi.SIGNATURES, name
+
+
+def test_struct_layouts_match_header():
+    capi, _ = _lib()
+    assert ctypes.sizeof(capi.MuseAttnParams) == 36
+    assert capi.MuseKvCache.k.offset == 8
+    assert capi.MuseKvCache.num_pages.offset == 40
+    assert ctypes.sizeof(capi.MuseKvCache) == 48
+
+
+def test_layer_schedule():
+    _, lib = _lib()
+    assert [i for i in range(52) if lib.muse_layer_is_global(i, 52) == 1] == list(range(3, 52, 4))
+    assert [i for i in range(62) if lib.muse_layer_is_global(i, 62) == 1] == list(range(1, 62, 4))
+    assert lib.muse_layer_is_global(-1, 52) == -1
+    assert lib.muse_layer_is_global(52, 52) == -1
+    assert lib.muse_version() >= 100
+
+
+def params(capi, **kw):
+    base = dict(num_q_heads=32, num_kv_heads=2, head_dim=128, sliding_window=2048, rope_theta=10000.0,
+                qk_scale=3.87, qk_norm_eps=1e-5, out_norm=0, out_norm_eps=1e-6)
+    base.update(kw)
+    return capi.MuseAttnParams(**base)
+
+
+FAKE = 0x1000  # 16-byte-aligned stand-in pointer; never dereferenced by a failing call
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), 2),
+    (dict(num_q_heads=30), 2),
+    (dict(num_q_heads=96, num_kv_heads=2), 2),
+    (dict(num_kv_heads=0), 1),
+    (dict(sliding_window=-1), 1),
+    (dict(rope_theta=-5.0), 1),
+    (dict(qk_scale=0.0), 1),
+    (dict(qk_norm_eps=0.0), 1),
+    (dict(out_norm=1, out_norm_eps=0.0), 1),
+    (dict(out_norm=2), 1),
+])
+def test_prefill_rejects_bad_params(kw, code):
+    capi, lib = _lib()
+    p = params(capi, **kw)
+    rc = lib.muse_attn_prefill(ctypes.byref(p), 1, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE,
+                               1 << 30, None)
+    assert rc == code
+    assert lib.muse_last_error()
+
+
+def test_prefill_argument_checks():
+    capi, lib = _lib()
+    p = params(capi)
+    assert lib.muse_attn_prefill(None, 1, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 30, None) == 1
+    # empty problem is a no-op
+    assert lib.muse_attn_prefill(ctypes.byref(p), 0, 64, None, None, None, None, None, None, None, None, 0, None) == 0
+    assert lib.muse_attn_prefill(ctypes.byref(p), 1, 0, None, None, None, None, None, None, None, None, 0, None) == 0
+    # null tensor, misalignment
+    assert lib.muse_attn_prefill(ctypes.byref(p), 1, 64, None, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 30, None) == 1
+    assert lib.muse_attn_prefill(ctypes.byref(p), 1, 64, FAKE + 2, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 30, None) == 1
+    # workspace too small
+    need = lib.muse_attn_prefill_workspace_size(ctypes.byref(p), 1, 64)
+    assert need > 0
+    assert lib.muse_attn_prefill(ctypes.byref(p), 1, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, need - 1, None) == 3
+    assert lib.muse_attn_prefill(ctypes.byref(p), 1, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, None, need, None) == 3
+    # strides: not a multiple of 8, token stride below H * D
+    bad = (ctypes.c_int64 * 10)(*([4096 * 64, 4100] + [256 * 64, 256] * 2 + [4096 * 64, 4096] * 2))
+    assert lib.muse_attn_prefill(ctypes.byref(p), 1, 64, FAKE, FAKE, FAKE, FAKE, bad, None, FAKE, FAKE, need, None) == 1
+    bad2 = (ctypes.c_int64 * 10)(*([4096 * 64, 2048] + [256 * 64, 256] * 2 + [4096 * 64, 4096] * 2))
+    assert lib.muse_attn_prefill(ctypes.byref(p), 1, 64, FAKE, FAKE, FAKE, FAKE, bad2, None, FAKE, FAKE, need, None) == 1
+
+
+def test_workspace_sizes():
+    capi, lib = _lib()
+    p = params(capi)
+    a = lib.muse_attn_prefill_workspace_size(ctypes.byref(p), 1, 1000)
+    b = lib.muse_attn_prefill_workspace_size(ctypes.byref(p), 1, 2000)
+    assert 0 < a < b
+    # k_hat fp16 + v bf16 over 64-key tiles: 2 * B * Hkv * ceil(T/64) * 64 * D * 2
+    assert a >= 2 * 2 * 16 * 64 * 128 * 2
+    bad = params(capi, head_dim=80)
+    assert lib.muse_attn_prefill_workspace_size(ctypes.byref(bad), 1, 1000) == 0
+
+
+def test_decode_argument_checks():
+    capi, lib = _lib()
+    p = params(capi, num_q_heads=128, num_kv_heads=16, head_dim=64, qk_scale=5.473, out_norm=1)
+    ring = capi.MuseKvCache(capi.MUSE_KV_RING, 2048, FAKE, FAKE, None, 0, 0, 0)
+    need = lib.muse_attn_decode_workspace_size(ctypes.byref(p), 16, 1 << 20, ctypes.byref(ring))
+    assert need > 0
+
+    def call(cache, max_len=1 << 20, ws=need, **kw):
+        pp = params(capi, **{**dict(num_q_heads=128, num_kv_heads=16, head_dim=64, qk_scale=5.473, out_norm=1), **kw})
+        return lib.muse_attn_decode(ctypes.byref(pp), 16, FAKE, FAKE, FAKE, FAKE, FAKE, max_len,
+                                    ctypes.byref(cache) if cache is not None else None, FAKE, FAKE, ws, None)
+
+    assert call(None) == 1
+    assert call(ring, ws=need - 1) == 3
+    assert call(ring, max_len=0) == 1
+    # ring capacity must equal the window
+    assert call(capi.MuseKvCache(capi.MUSE_KV_RING, 1024, FAKE, FAKE, None, 0, 0, 0)) == 1
+    # ring on a global layer
+    assert call(ring, sliding_window=0) == 1
+    # paged: block-table capacity, page size
+    paged = capi.MuseKvCache(capi.MUSE_KV_PAGED, 0, FAKE, FAKE, FAKE, 100, 32, 10000)
+    assert call(paged, max_len=100 * 32 + 1, sliding_window=0) == 1
+    assert call(capi.MuseKvCache(capi.MUSE_KV_PAGED, 0, FAKE, FAKE, FAKE, 100, 24, 10000), max_len=64,
+                sliding_window=0) == 2
+    assert call(capi.MuseKvCache(capi.MUSE_KV_PAGED, 0, FAKE, FAKE, None, 100, 32, 10000), max_len=64,
+                sliding_window=0) == 1
+    assert call(capi.MuseKvCache(7, 0, FAKE, FAKE, None, 0, 0, 0)) == 1
+
+
+def test_rope_qknorm_argument_checks():
+    capi, lib = _lib()
+    p = params(capi)
+    f = lib.muse_rope_qknorm
+    assert f(ctypes.byref(p), 4, None, 0, None, 0, None, None, None, 0, None) == 1        # no q, no k
+    assert f(ctypes.byref(p), 4, FAKE, 4096, None, 0, None, None, None, 0, None) == 1     # q without q_out
+    assert f(ctypes.byref(p), 4, FAKE, 4096, None, 0, None, FAKE, None, 9, None) == 1     # bad dtype
+    assert f(ctypes.byref(p), 4, FAKE, 100, None, 0, None, FAKE, None, 0, None) == 1      # stride < Hq * D
+    assert f(ctypes.byref(p), 0, FAKE, 4096, None, 0, None, FAKE, None, 0, None) == 0     # empty: no-op
+    assert f(ctypes.byref(p), -1, FAKE, 4096, None, 0, None, FAKE, None, 0, None) == 1
