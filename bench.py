@@ -1,0 +1,322 @@
+"""Benchmark of the attention layer on one MI355X.
+
+One step = the whole prefill path of the layer (key/value preparation,
+attention with the fused query prologue, output norm and gate) over the
+Glimmer local-layer workload: batch 1, 32768 tokens, 32 query / 2 KV heads,
+head width 128, causal window 2048, RoPE base 10000, multiplier 3.87.
+`value` is that step's algorithmic throughput (4 * Hq * D FLOPs per visible
+(query, key) pair) in TFLOP/s.  The same JSON line carries:
+  roofline      - the attention kernel's duration from HIP events recorded
+                  around it on the launch stream, against the bf16/f16 MFMA peak;
+  cpu_baseline  - the fp64 oracle on a bounded sample of the same workload;
+  decode        - the Spark decode step over a paged global-layer cache
+                  (16 sequences, lengths uniform in [131072, 1048576]) and a
+                  2048-entry ring, in GB/s of cached K/V read, against HBM peak;
+  prefill_other - the other prefill workloads (one or two timed reps each).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn prefill TFLOP/s & decode KV GB/s on 1 MI355X (% of MFMA/HBM peak)"
+MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent pairs through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e
+
+    def elapsed_ms(self, a, b):
+        f = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(f), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return f.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "global_muse_rope_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+PREFILL_SOURCES = ["prefill.hip", "kernels.h", "common.h"]
+DECODE_SOURCES = ["decode.hip", "kernels.h", "common.h"]
+
+
+def committed_traffic(name, digest, per_launch_alg):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel source."""
+    path = os.path.join(PROFILES, f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_digest") != digest:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def timed_steps(fn, steps, warmup, events, torch):
+    """Run warmup + steps; returns (wall ms per step, mean attention-kernel ms)."""
+    import global_muse_rope_amd._capi as capi
+    lib = capi.load()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    pairs = [(events.create(), events.create()) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in pairs:
+        capi.check(lib.muse_profile_events(a, b))
+        fn()
+    capi.check(lib.muse_profile_events(None, None))
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    kern = sum(events.elapsed_ms(a, b) for a, b in pairs) / steps
+    for a, b in pairs:
+        events.destroy(a)
+        events.destroy(b)
+    return wall, kern
+
+
+def prefill_case(cfg, steps, warmup, events, torch, ma, keep=False):
+    from synth.device import prefill_device_inputs
+    from global_muse_rope_amd import accounting as acc
+    L = cfg.layer
+    lp = ma.LayerParams.from_layer(L)
+    x = prefill_device_inputs(cfg)
+    out = torch.empty((cfg.batch, cfg.seq, L.hq, L.d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ma.prefill_workspace_size(lp, cfg.batch, cfg.seq), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ma.prefill(lp, x["q"], x["k"], x["v"], x["g"], out=out, workspace=ws)
+
+    wall, kern = timed_steps(step, steps, warmup, events, torch)
+    flops = acc.prefill_flops(L.hq, L.d, cfg.batch, cfg.seq, L.window)
+    res = {"ms_per_step": wall, "tflops": flops / (wall * 1e-3) / 1e12, "kernel_ms": kern,
+           "kernel_tflops": flops / (kern * 1e-3) / 1e12, "flops": flops}
+    if keep:
+        res["_tensors"] = (x, out)
+    else:
+        del x, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
+def decode_case(cfg, steps, warmup, events, torch, ma, flush=False):
+    from synth.device import decode_device_setup
+    from global_muse_rope_amd import accounting as acc
+    L = cfg.layer
+    s = decode_device_setup(cfg)
+    if s["kind"] == "ring":
+        s["cache"] = ma.KvCache.ring(s["kc"], s["vc"])
+    else:
+        s["cache"] = ma.KvCache.paged(s["kc"], s["vc"], s["block_table"], s["page_tokens"])
+    lp = ma.LayerParams.from_layer(L)
+    ws = torch.empty(ma.decode_workspace_size(lp, cfg.batch, s["max_len"], s["cache"]), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((cfg.batch, L.hq, L.d), dtype=torch.bfloat16, device="cuda")
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if flush else None
+
+    def step():
+        if scrub is not None:
+            scrub.fill_(1)     # evict the 256 MB last-level cache between steps
+        ma.decode(lp, s["q"], s["k"], s["v"], s["g"], s["kv_len"], s["max_len"], s["cache"], out=out, workspace=ws)
+
+    wall, kern = timed_steps(step, steps, warmup, events, torch)
+    kv_bytes = acc.decode_kv_bytes(L.hkv, L.d, s["lengths"], L.window)
+    io = acc.decode_io_bytes(L.hq, L.hkv, L.d, cfg.batch)
+    res = {"kernel_ms": kern, "kv_bytes": kv_bytes, "gbs": (kv_bytes + io) / (kern * 1e-3) / 1e9,
+           "ms_per_step": wall, "lengths_sum": int(sum(s["lengths"]))}
+    del s, ws, out, scrub
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, gpu_out, budget_s=15.0):
+    """The fp64 oracle, as it stands, on a bounded sample of rows of the same
+    workload; returns its throughput in TFLOP/s and the GPU/oracle max-abs
+    difference on those rows."""
+    import numpy as np
+    import oracle
+    from global_muse_rope_amd import accounting as acc
+    from synth.device import host_tokens, host_rows
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    L = cfg.layer
+    T = cfg.seq
+    k = host_tokens(cfg, "k", 0, 0, T)   # [T, Hkv, D] float64
+    v = host_tokens(cfg, "v", 0, 0, T)
+    rng = np.random.default_rng(1)
+    order = np.concatenate([[0, 1, L.window - 2, L.window - 1, L.window, T - 1],
+                            rng.permutation(T)]).astype(np.int64)
+    gpu = gpu_out.float().cpu().numpy()[0] if gpu_out is not None else None
+    t_start = time.perf_counter()
+    done, flops, worst = 0, 0, 0.0
+    elapsed = 0.0
+    while done < len(order) and elapsed < budget_s:
+        rows = order[done:done + 128]
+        q = host_rows(cfg, "q", 0, rows)
+        g = host_rows(cfg, "g", 0, rows)
+        t0 = time.perf_counter()
+        y = oracle.prefill(q, k[:rows.max() + 1], v[:rows.max() + 1], g, L, rows=rows)
+        elapsed += time.perf_counter() - t0
+        for r in rows:
+            lo, hi = oracle.visible_range(int(r), L.window)
+            flops += acc.flops_per_pair(L.hq, L.d) * (hi - lo + 1)
+        if gpu is not None:
+            worst = max(worst, float(np.max(np.abs(gpu[rows] - y))))
+        done += len(rows)
+    wall = time.perf_counter() - t_start
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} query rows (all {L.hq} heads) of {cfg.name}, chosen by a seeded permutation "
+                      f"plus window-edge rows; {flops / 1e9:.1f} GFLOP in {elapsed:.1f} s of oracle time "
+                      f"({wall:.1f} s with input regeneration)",
+            "gpu_max_abs_err_on_sample": worst}
+
+
+def pmc_pass(torch, ma):
+    """A short run for rocprofv3 counter passes: two prefill steps of the
+    benchmark workload and one plain 1 GiB device copy as the calibration."""
+    from synth.workloads import GLIMMER_LOCAL
+    prefill_case(GLIMMER_LOCAL, 1, 1, HipEvents(), torch, ma)
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log("pmc pass done: 2 prefill steps + 1 GiB copy")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--quick", action="store_true", help="only the benchmark workload and the CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import global_muse_rope_amd as ma
+    from synth import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ma._capi.load()   # fails loudly if the library is missing
+    if args.pmc_pass:
+        pmc_pass(torch, ma)
+        return
+    events = HipEvents()
+    props = torch.cuda.get_device_properties(0)
+
+    cfg = wl.GLIMMER_LOCAL
+    log(f"prefill {cfg.name}: warmup {args.warmup}, steps {args.steps}")
+    main_res = prefill_case(cfg, args.steps, args.warmup, events, torch, ma, keep=True)
+    x, gpu_out = main_res.pop("_tensors")
+    log(f"  {main_res['tflops']:.1f} TFLOP/s step, attention kernel {main_res['kernel_ms']:.3f} ms "
+        f"({main_res['kernel_tflops']:.1f} TFLOP/s)")
+    digest = source_digest(PREFILL_SOURCES)
+    traffic = committed_traffic("prefill_glimmer_local_32k", digest, main_res["flops"])
+    result = {
+        "metric": METRIC,
+        "value": round(main_res["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq, "q_heads": cfg.layer.hq,
+                   "kv_heads": cfg.layer.hkv, "head_dim": cfg.layer.d, "window": cfg.layer.window,
+                   "rope_theta": cfg.layer.theta, "qk_scale": cfg.layer.scale, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(main_res["kernel_tflops"], 2), "peak": MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(main_res["kernel_tflops"] / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "prefill_kernel", "kernel_ms": round(main_res["kernel_ms"], 4),
+                     "flops_per_launch": main_res["flops"], "source_digest": digest},
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu:
+        log("cpu baseline (oracle, bounded sample)")
+        result["cpu_baseline"] = cpu_baseline(cfg, gpu_out)
+        log(f"  {result['cpu_baseline']['sample']}")
+    del x, gpu_out
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        dec = {}
+        for dcfg, steps, flush in [(wl.SPARK_DECODE_GLOBAL, 10, False), (wl.SPARK_DECODE_LOCAL, 20, True)]:
+            log(f"decode {dcfg.name}")
+            r = decode_case(dcfg, steps, 2, events, torch, ma, flush=flush)
+            log(f"  {r['gbs']:.0f} GB/s, split kernel {r['kernel_ms']:.3f} ms")
+            dec[dcfg.name] = {"value": round(r["gbs"], 1), "unit": "GB/s", "kernel": "decode_split_kernel",
+                              "kernel_ms": round(r["kernel_ms"], 4), "ms_per_step": round(r["ms_per_step"], 4),
+                              "kv_bytes_per_step": r["kv_bytes"], "cache_flushed": flush,
+                              "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS,
+                                           "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4)}}
+        result["decode"] = dec
+
+    if not args.quick:
+        other = {}
+        for pcfg in [wl.GLIMMER_GLOBAL, wl.SPARK_LOCAL, wl.SPARK_GLOBAL]:
+            log(f"prefill {pcfg.name}")
+            r = prefill_case(pcfg, 2, 1, events, torch, ma)
+            log(f"  {r['tflops']:.1f} TFLOP/s step, kernel {r['kernel_tflops']:.1f} TFLOP/s")
+            other[pcfg.name] = {"tflops_step": round(r["tflops"], 2), "ms_per_step": round(r["ms_per_step"], 3),
+                                "kernel_tflops": round(r["kernel_tflops"], 2),
+                                "frac_of_mfma_peak": round(r["kernel_tflops"] / MFMA_PEAK_TFLOPS, 4)}
+        result["prefill_other"] = other
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

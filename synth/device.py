@@ -1,0 +1,156 @@
+"""Workload inputs generated directly in device memory (same bits as the host
+forms in ``synth``), and host regeneration of any slice for the oracle.
+
+Prefill tensors are indexed in the canonical layout [B, T, H, D].  Decode:
+the new token's q, k, v, gate are [B, H, D]; cached entries of (sequence b,
+KV head h) at position p are element p * D + d of stream
+S_CACHE_BASE + 2 * (b * Hkv + h) (+1 for values).  Cached keys are drawn
+like raw projections (mean square 1 per head, as the layer's normalized keys
+have on average) and stored as given; the layer treats cache contents as
+data.  Paged caches place each sequence's pages at positions drawn from a
+seeded permutation of the pool.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import normal_bf16_torch, normal_bf16_torch_tensor, bf16_bits_to_f64, f32_to_bf16_bits, normal_f32
+from .workloads import S_Q, S_K, S_V, S_G, S_CACHE_BASE, decode_lengths
+
+STREAM = {"q": S_Q, "k": S_K, "v": S_V, "g": S_G}
+
+
+def prefill_shapes(cfg):
+    L = cfg.layer
+    return {"q": (cfg.batch, cfg.seq, L.hq, L.d), "k": (cfg.batch, cfg.seq, L.hkv, L.d),
+            "v": (cfg.batch, cfg.seq, L.hkv, L.d), "g": (cfg.batch, cfg.seq, L.hq, L.d)}
+
+
+def prefill_device_inputs(cfg, device="cuda"):
+    return {n: normal_bf16_torch_tensor(cfg.seed, STREAM[n], shp, device)
+            for n, shp in prefill_shapes(cfg).items()}
+
+
+def host_rows(cfg, name, b, rows, heads=None):
+    """float64 values of tensor `name` at batch b, token rows, given heads."""
+    B, T, H, D = prefill_shapes(cfg)[name]
+    rows = np.asarray(rows, dtype=np.int64)
+    heads = np.arange(H) if heads is None else np.asarray(heads, dtype=np.int64)
+    idx = ((b * T + rows[:, None, None]) * H + heads[None, :, None]) * D + np.arange(D)[None, None, :]
+    return bf16_bits_to_f64(f32_to_bf16_bits(normal_f32(cfg.seed, STREAM[name], idx)))
+
+
+def host_tokens(cfg, name, b, t0, t1, heads=None):
+    """float64 values of tokens t0 .. t1-1 (all of `heads`) via the torch CPU form."""
+    import torch
+    B, T, H, D = prefill_shapes(cfg)[name]
+    heads = np.arange(H) if heads is None else np.asarray(heads, dtype=np.int64)
+    out = np.empty((t1 - t0, len(heads), D), dtype=np.float64)
+    step = 1 << 15
+    hh = torch.from_numpy(heads)[None, :, None]
+    dd = torch.arange(D, dtype=torch.int64)[None, None, :]
+    for s in range(t0, t1, step):
+        e = min(t1, s + step)
+        tok = torch.arange(s, e, dtype=torch.int64)[:, None, None]
+        idx = ((b * T + tok) * H + hh) * D + dd
+        out[s - t0:e - t0] = normal_bf16_torch(cfg.seed, STREAM[name], idx.reshape(-1)).float().numpy().reshape(
+            e - s, len(heads), D)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def cache_stream(b, h, hkv, which):
+    return S_CACHE_BASE + 2 * (b * hkv + h) + (1 if which == "v" else 0)
+
+
+def cache_values_torch(seed, b, h, hkv, which, p0, p1, d, device):
+    """bf16 tensor [p1 - p0, d] of cached entries at positions p0 .. p1-1."""
+    import torch
+    idx = torch.arange(p0 * d, p1 * d, dtype=torch.int64, device=device)
+    return normal_bf16_torch(seed, cache_stream(b, h, hkv, which), idx).view(p1 - p0, d)
+
+
+def cache_values_host(seed, b, h, hkv, which, p0, p1, d):
+    """float64 [p1 - p0, d], the same values on the host."""
+    vals = np.empty((p1 - p0, d), dtype=np.float64)
+    step = 1 << 16
+    for s in range(p0, p1, step):
+        e = min(p1, s + step)
+        vals[s - p0:e - p0] = cache_values_torch(seed, b, h, hkv, which, s, e, d, "cpu").float().numpy()
+    return vals
+
+
+def new_token_shapes(cfg):
+    L = cfg.layer
+    return {"q": (cfg.batch, L.hq, L.d), "k": (cfg.batch, L.hkv, L.d), "v": (cfg.batch, L.hkv, L.d),
+            "g": (cfg.batch, L.hq, L.d)}
+
+
+def new_token_host(cfg):
+    out = {}
+    for n, shp in new_token_shapes(cfg).items():
+        idx = np.arange(int(np.prod(shp)), dtype=np.int64)
+        out[n] = bf16_bits_to_f64(f32_to_bf16_bits(normal_f32(cfg.seed + 1, STREAM[n], idx))).reshape(shp)
+    return out
+
+
+def decode_device_setup(cfg, device="cuda", lengths=None):
+    """Ring (window > 0) or paged (global) cache filled for every sequence's
+    history, the new-token tensors and kv_len.  Returns a dict of tensors:
+    q, k, v, g, kv_len (int32), lengths (numpy), max_len, and the cache
+    pieces kind, kc, vc, block_table, page_tokens."""
+    import torch
+    L = cfg.layer
+    d, hkv, B = L.d, L.hkv, cfg.batch
+    lengths = decode_lengths(cfg.seed, B, cfg.len_lo, cfg.len_hi) if lengths is None else np.asarray(lengths)
+    max_len = int(cfg.len_hi)
+    res = {n: normal_bf16_torch_tensor(cfg.seed + 1, STREAM[n], shp, device)
+           for n, shp in new_token_shapes(cfg).items()}
+    res["kv_len"] = torch.from_numpy(lengths.astype(np.int32)).to(device)
+    res["lengths"] = lengths
+    res["max_len"] = max_len
+    if L.window > 0:
+        W = L.window
+        kc = torch.zeros((B, hkv, W, d), dtype=torch.bfloat16, device=device)
+        vc = torch.zeros((B, hkv, d, W), dtype=torch.bfloat16, device=device)
+        for b in range(B):
+            n = int(lengths[b])
+            p0, p1 = max(0, n - 1 - W), n - 1
+            if p1 <= p0:
+                continue
+            slots = torch.arange(p0, p1, device=device) % W
+            for h in range(hkv):
+                kc[b, h, slots, :] = cache_values_torch(cfg.seed, b, h, hkv, "k", p0, p1, d, device)
+                vc[b, h, :, slots] = cache_values_torch(cfg.seed, b, h, hkv, "v", p0, p1, d, device).t()
+        res.update(kind="ring", kc=kc, vc=vc, block_table=None, page_tokens=0)
+        return res
+    pt = cfg.page_tokens
+    pages = [(int(n) + pt - 1) // pt for n in lengths]
+    max_pages = (max_len + pt - 1) // pt
+    n_pool = sum(pages) + 1
+    perm = np.random.default_rng(cfg.seed + 2).permutation(n_pool).astype(np.int32)
+    table = np.full((B, max_pages), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :pages[b]] = perm[off:off + pages[b]]
+        off += pages[b]
+    kc = torch.empty((n_pool, hkv, pt, d), dtype=torch.bfloat16, device=device)
+    vc = torch.empty((n_pool, hkv, d, pt), dtype=torch.bfloat16, device=device)
+    tdev = torch.from_numpy(table).to(device)
+    for b in range(B):
+        n = int(lengths[b])
+        idxp = tdev[b, :pages[b]].long()
+        for h in range(hkv):
+            for which, dst in (("k", kc), ("v", vc)):
+                vals = torch.zeros((pages[b] * pt, d), dtype=torch.bfloat16, device=device)
+                vals[:n] = cache_values_torch(cfg.seed, b, h, hkv, which, 0, n, d, device)
+                vals = vals.view(pages[b], pt, d)
+                if which == "k":
+                    dst[idxp, h] = vals
+                else:
+                    dst[idxp, h] = vals.transpose(1, 2)
+    res.update(kind="paged", kc=kc, vc=vc, block_table=tdev, page_tokens=pt)
+    return res
