@@ -65,6 +65,7 @@ SIGNATURES = {
     "muse_layer_is_global": (_i32, [_i32, _i32]),
     "muse_last_error": (ctypes.c_char_p, []),
     "muse_version": (_i32, []),
+    "muse_profile_events": (_i32, [_vp, _vp]),
 }
 
 _lib = None

@@ -13,6 +13,8 @@ using namespace muse;
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_prof_start = nullptr;
+thread_local hipEvent_t g_prof_stop = nullptr;
 
 int32_t fail(int32_t code, const char* fmt, ...) {
   va_list ap;
@@ -88,10 +90,22 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 int64_t prefill_tiles(int32_t T) { return (static_cast<int64_t>(T) + kKeyTile - 1) / kKeyTile; }
 
-size_t prefill_ws(const muse_attn_params* p, int32_t B, int32_t T) {
-  const size_t per = static_cast<size_t>(B) * p->num_kv_heads * prefill_tiles(T) * kKeyTile * p->head_dim * 2;
-  return align256(per) * 2;
+// Prefill workspace: k_hat tiles (fp16), V^T tiles (bf16), and on RoPE
+// layers the (cos, sin) table for B * T positions.
+struct PrefillWs {
+  size_t k_bytes, v_bytes, rope_bytes, total;
+};
+
+PrefillWs prefill_ws_layout(const muse_attn_params* p, int32_t B, int32_t T) {
+  PrefillWs w;
+  w.k_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * prefill_tiles(T) * kKeyTile * p->head_dim * 2);
+  w.v_bytes = w.k_bytes;
+  w.rope_bytes = p->rope_theta > 0.f ? align256(static_cast<size_t>(B) * T * (p->head_dim / 2) * 8) : 0;
+  w.total = w.k_bytes + w.v_bytes + w.rope_bytes;
+  return w;
 }
+
+size_t prefill_ws(const muse_attn_params* p, int32_t B, int32_t T) { return prefill_ws_layout(p, B, T).total; }
 
 struct DecodePlan {
   int chunk_tokens;
@@ -151,6 +165,13 @@ extern "C" {
 int32_t muse_version(void) { return 100; }
 
 const char* muse_last_error(void) { return g_err; }
+
+int32_t muse_profile_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return fail(MUSE_ERR_INVALID_ARG, "pass both events or neither");
+  g_prof_start = static_cast<hipEvent_t>(start);
+  g_prof_stop = static_cast<hipEvent_t>(stop);
+  return ok();
+}
 
 int32_t muse_layer_is_global(int32_t i, int32_t n_layers) {
   if (n_layers <= 0 || i < 0 || i >= n_layers) return -1;
@@ -247,9 +268,22 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t n_tiles = prefill_tiles(T);
-  const size_t half_ws = need / 2;
+  const PrefillWs wl = prefill_ws_layout(params, B, T);
   half_t* khat = static_cast<half_t*>(workspace);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + half_ws);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + wl.k_bytes);
+  float2* rope = wl.rope_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + wl.k_bytes + wl.v_bytes)
+                               : nullptr;
+  hipError_t e;
+  if (rope) {
+    RopeTableArgs ra{};
+    ra.positions = positions;
+    ra.T = T;
+    ra.n_rows = positions ? static_cast<int64_t>(B) * T : T;
+    ra.log2_theta = log2_theta(params);
+    ra.table = rope;
+    e = launch_rope_table(D, ra, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "rope table launch: %s", hipGetErrorString(e));
+  }
 
   KvPrepArgs kp{};
   kp.k = static_cast<const uint16_t*>(k);
@@ -258,16 +292,15 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   kp.k_st = s[3];
   kp.v_sb = s[4];
   kp.v_st = s[5];
-  kp.positions = positions;
+  kp.rope = rope;
+  kp.rope_batched = positions ? 1 : 0;
   kp.T = T;
   kp.Hkv = Hkv;
   kp.n_tiles = static_cast<int>(n_tiles);
   kp.eps = params->qk_norm_eps;
-  kp.log2_theta = log2_theta(params);
-  kp.use_rope = params->rope_theta > 0.f ? 1 : 0;
   kp.khat = khat;
   kp.vt = vt;
-  hipError_t e = launch_kv_prep(D, B, kp, st);
+  e = launch_kv_prep(D, B, kp, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "kv_prep launch: %s", hipGetErrorString(e));
 
   const int G = Hq / Hkv;
@@ -286,7 +319,8 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   pa.g_st = s[7];
   pa.o_sb = s[8];
   pa.o_st = s[9];
-  pa.positions = positions;
+  pa.rope = rope;
+  pa.rope_batched = positions ? 1 : 0;
   pa.T = T;
   pa.Hkv = Hkv;
   pa.W = params->sliding_window;
@@ -296,14 +330,20 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   pa.batch_heads = B * Hkv;
   pa.qscale = q_logit_scale(params);
   pa.qk_eps = params->qk_norm_eps;
-  pa.log2_theta = log2_theta(params);
-  pa.use_rope = params->rope_theta > 0.f ? 1 : 0;
   pa.out_norm = params->out_norm;
   pa.out_eps = params->out_norm_eps;
   if (static_cast<int64_t>(pa.n_qblocks_pad) * pa.batch_heads > 0x7fffffffLL)
     return fail(MUSE_ERR_UNSUPPORTED, "problem too large for one launch");
+  if (g_prof_start) {
+    e = hipEventRecord(g_prof_start, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  }
   e = launch_prefill(D, G, pa, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  if (g_prof_stop) {
+    e = hipEventRecord(g_prof_stop, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 
@@ -370,7 +410,7 @@ int32_t muse_attn_decode(const muse_attn_params* params, int32_t B, const void* 
   a.khat = reinterpret_cast<float*>(ws);
   ws += align256(static_cast<size_t>(B) * Hkv * D * 4);
   a.part = reinterpret_cast<float*>(ws);
-  hipError_t e = launch_decode(D, Hq / Hkv, a, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_decode(D, Hq / Hkv, a, static_cast<hipStream_t>(stream), g_prof_start, g_prof_stop);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }

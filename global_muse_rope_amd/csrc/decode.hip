@@ -391,7 +391,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 namespace {
 template <int D, int G>
-hipError_t launch_dg(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_dg(const DecodeArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
   const int hq = a.Hkv * G;
   const int rows = hq + a.Hkv;
   const int threads = rows * (D / 2);
@@ -400,28 +400,30 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned items = static_cast<unsigned>(a.B) * a.Hkv * a.max_chunks;
+  if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(items), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D, G>), dim3(a.B * a.Hkv), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(int g, const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_d(int g, const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
   switch (g) {
-    case 1: return launch_dg<D, 1>(a, st);
-    case 2: return launch_dg<D, 2>(a, st);
-    case 4: return launch_dg<D, 4>(a, st);
-    case 8: return launch_dg<D, 8>(a, st);
-    case 16: return launch_dg<D, 16>(a, st);
+    case 1: return launch_dg<D, 1>(a, st, e0, e1);
+    case 2: return launch_dg<D, 2>(a, st, e0, e1);
+    case 4: return launch_dg<D, 4>(a, st, e0, e1);
+    case 8: return launch_dg<D, 8>(a, st, e0, e1);
+    case 16: return launch_dg<D, 16>(a, st, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 }  // namespace
 
-hipError_t launch_decode(int d, int g, const DecodeArgs& a, hipStream_t st) {
-  return d == 64 ? launch_d<64>(g, a, st) : launch_d<128>(g, a, st);
+hipError_t launch_decode(int d, int g, const DecodeArgs& a, hipStream_t st, hipEvent_t e0, hipEvent_t e1) {
+  return d == 64 ? launch_d<64>(g, a, st, e0, e1) : launch_d<128>(g, a, st, e0, e1);
 }
 
 }  // namespace muse

@@ -57,6 +57,21 @@ __global__ __launch_bounds__(256) void rope_qknorm_kernel(RopeQkArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// RoPE table for a prefill call: one (cos, sin) pair per (position row, j).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
+  const int64_t gt = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gt >= a.n_rows * (D / 2)) return;
+  const int64_t row = gt / (D / 2);
+  const int j = static_cast<int>(gt % (D / 2));
+  const int pos = a.positions ? a.positions[row] : static_cast<int>(row % a.T);
+  float s, c;
+  rope_sincos(pos, j, D, a.log2_theta, &s, &c);
+  a.table[gt] = make_float2(c, s);
+}
+
+// ---------------------------------------------------------------------------
 // Prefill key/value preparation: one 64-key tile of one (sequence, KV head)
 // per workgroup.  Writes k_hat as fp16 [tile][key][D] and V transposed as
 // bf16 [tile][D][key], both in the chunk-swizzled order the attention kernel
@@ -95,15 +110,16 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
   for (int e = 0; e < RUN; ++e) ss += lo[e] * lo[e] + hi[e] * hi[e];
   ss = group_sum<4>(ss);
   const float rs = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
-  const int pos = valid ? (a.positions ? a.positions[static_cast<int64_t>(b) * a.T + tok] : tok) : 0;
+  const float2* rt = nullptr;
+  if (a.rope && valid)
+    rt = a.rope + ((a.rope_batched ? static_cast<int64_t>(b) * a.T : 0) + tok) * (D / 2) + qq * RUN;
 #pragma unroll
   for (int e = 0; e < RUN; ++e) {
     float x0 = lo[e] * rs, x1 = hi[e] * rs;
-    if (a.use_rope) {
-      float s, c;
-      rope_sincos(pos, qq * RUN + e, D, a.log2_theta, &s, &c);
-      const float y0 = x0 * c - x1 * s;
-      const float y1 = x1 * c + x0 * s;
+    if (rt) {
+      const float2 cs = rt[e];
+      const float y0 = x0 * cs.x - x1 * cs.y;
+      const float y1 = x1 * cs.x + x0 * cs.y;
       x0 = y0;
       x1 = y1;
     }
@@ -178,6 +194,14 @@ hipError_t launch_rope_qknorm(int d, int out_dtype, const RopeQkArgs& a, hipStre
     else MUSE_RQ(128, MUSE_DTYPE_BF16);
   }
 #undef MUSE_RQ
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(int d, const RopeTableArgs& a, hipStream_t st) {
+  const int64_t n = a.n_rows * (d / 2);
+  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+  if (d == 64) hipLaunchKernelGGL((rope_table_kernel<64>), dim3(blocks), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((rope_table_kernel<128>), dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

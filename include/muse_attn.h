@@ -163,6 +163,15 @@ int32_t muse_layer_is_global(int32_t layer_index, int32_t n_layers);
 /* Message of the last failed call on this thread ("" if none). */
 const char* muse_last_error(void);
 
+/* Profiling aid: on the calling thread, make the next muse_attn_prefill /
+ * muse_attn_decode calls record `start` (a hipEvent_t) on their stream just
+ * before their main attention kernel (the prefill attention kernel; the decode
+ * split kernel) and `stop` just after it, so a caller can time that kernel
+ * with hipEventElapsedTime.  Pass NULL, NULL to turn it off.  Nothing is
+ * recorded by muse_rope_qknorm.  Returns MUSE_OK, or MUSE_ERR_INVALID_ARG if
+ * exactly one of the two is NULL. */
+int32_t muse_profile_events(void* start, void* stop);
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t muse_version(void);
 
