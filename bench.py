@@ -212,11 +212,13 @@ def cpu_baseline(cfg, gpu_out, budget_s=15.0):
             "gpu_max_abs_err_on_sample": worst}
 
 
-def pmc_pass(torch, ma):
-    """A short run for rocprofv3 counter passes: two prefill steps of the
-    benchmark workload and one plain 1 GiB device copy as the calibration."""
-    from synth.workloads import GLIMMER_LOCAL
-    prefill_case(GLIMMER_LOCAL, 1, 1, HipEvents(), torch, ma)
+def pmc_pass(torch, ma, workload):
+    """A short run for rocprofv3 counter passes: two prefill steps of one
+    workload (default: the benchmark workload) and one plain 1 GiB device copy
+    as the calibration of the byte counters."""
+    from synth import workloads as wl
+    cfg = {c.name: c for c in wl.PREFILL}[workload]
+    prefill_case(cfg, 1, 1, HipEvents(), torch, ma)
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
     b = torch.empty_like(a)
     torch.cuda.synchronize()
@@ -234,6 +236,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")
+    ap.add_argument("--pmc-workload", default="glimmer_local_prefill_32k")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -249,7 +252,7 @@ def main():
         sys.exit(1)
     ma._capi.load()   # fails loudly if the library is missing
     if args.pmc_pass:
-        pmc_pass(torch, ma)
+        pmc_pass(torch, ma, args.pmc_workload)
         return
     events = HipEvents()
     props = torch.cuda.get_device_properties(0)

@@ -5,7 +5,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmuse_attn.so")
+# MUSE_ATTN_LIB may name another build of the same library (A/B timing of
+# kernel variants); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("MUSE_ATTN_LIB") or os.path.join(_PKG, "libmuse_attn.so")
 
 MUSE_OK = 0
 MUSE_ERR_INVALID_ARG = 1

@@ -32,29 +32,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libmuse_attn.so")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", os.path.join(SRC, src), "-o", obj]
+def _compile(src: str, defines=(), tag="") -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *["-D" + d for d in defines], "-c", os.path.join(SRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link the shared library."""
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile every HIP source for gfx950 and link the shared library.
+    `defines` (macro definitions) and `out` select a variant build."""
     os.makedirs(BUILD, exist_ok=True)
+    tag = "" if not defines else "_" + "_".join(d.replace("=", "") for d in defines)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, defines, tag), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 if __name__ == "__main__":

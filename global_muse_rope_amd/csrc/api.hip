@@ -90,18 +90,17 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 int64_t prefill_tiles(int32_t T) { return (static_cast<int64_t>(T) + kKeyTile - 1) / kKeyTile; }
 
-// Prefill workspace: k_hat tiles (fp16), V^T tiles (bf16), and on RoPE
-// layers the (cos, sin) table for B * T positions.
+// Prefill workspace: the K/V tile images (k_hat fp16 + V^T bf16, padded rows)
+// and, on RoPE layers, the (cos, sin) table for B * T positions.
 struct PrefillWs {
-  size_t k_bytes, v_bytes, rope_bytes, total;
+  size_t tile_bytes, rope_bytes, total;
 };
 
 PrefillWs prefill_ws_layout(const muse_attn_params* p, int32_t B, int32_t T) {
   PrefillWs w;
-  w.k_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * prefill_tiles(T) * kKeyTile * p->head_dim * 2);
-  w.v_bytes = w.k_bytes;
+  w.tile_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * prefill_tiles(T) * tile_chunks(p->head_dim) * 16);
   w.rope_bytes = p->rope_theta > 0.f ? align256(static_cast<size_t>(B) * T * (p->head_dim / 2) * 8) : 0;
-  w.total = w.k_bytes + w.v_bytes + w.rope_bytes;
+  w.total = w.tile_bytes + w.rope_bytes;
   return w;
 }
 
@@ -269,10 +268,8 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t n_tiles = prefill_tiles(T);
   const PrefillWs wl = prefill_ws_layout(params, B, T);
-  half_t* khat = static_cast<half_t*>(workspace);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + wl.k_bytes);
-  float2* rope = wl.rope_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + wl.k_bytes + wl.v_bytes)
-                               : nullptr;
+  u32x4* tiles = static_cast<u32x4*>(workspace);
+  float2* rope = wl.rope_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + wl.tile_bytes) : nullptr;
   hipError_t e;
   if (rope) {
     RopeTableArgs ra{};
@@ -298,8 +295,7 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   kp.Hkv = Hkv;
   kp.n_tiles = static_cast<int>(n_tiles);
   kp.eps = params->qk_norm_eps;
-  kp.khat = khat;
-  kp.vt = vt;
+  kp.tiles = tiles;
   e = launch_kv_prep(D, B, kp, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "kv_prep launch: %s", hipGetErrorString(e));
 
@@ -311,8 +307,7 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   pa.q = static_cast<const uint16_t*>(q);
   pa.gate = static_cast<const uint16_t*>(gate);
   pa.out = static_cast<uint16_t*>(out);
-  pa.khat = khat;
-  pa.vt = vt;
+  pa.tiles = tiles;
   pa.q_sb = s[0];
   pa.q_st = s[1];
   pa.g_sb = s[6];

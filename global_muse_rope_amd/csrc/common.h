@@ -21,6 +21,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds_wave_base + 16 * i; the base must be
+// wave-uniform.  Completion is tracked by the vector-memory counter.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

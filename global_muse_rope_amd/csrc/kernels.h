@@ -10,30 +10,29 @@ namespace muse {
 constexpr int kKeyTile = 64;
 
 // ---------------------------------------------------------------------------
-// Prefill workspace layouts (written by kv_prep_kernel, copied verbatim into
-// LDS by the attention kernel, 16-byte chunks XOR-swizzled so that the MFMA
-// operand reads of 32 consecutive rows spread over all LDS banks):
-//   khat: fp16 [B * Hkv][n_tiles][64 keys][D], chunk c of key row r stored at
-//         chunk k_chunk_swizzle(c, r);
-//   vt:   bf16 [B * Hkv][n_tiles][D][64 keys], head-dim-major; inside each
-//         16-key group keys are stored in the order 0-3, 8-11, 4-7, 12-15 so
-//         that one 16-byte read gives the eight keys an MFMA lane consumes;
-//         chunk c of dim row d stored at chunk v_chunk_swizzle(c, d).
+// Prefill tile image: one 64-key tile of one (sequence, KV head), written by
+// kv_prep_kernel and copied verbatim into LDS by the attention kernel, in
+// 16-byte chunks:
+//   K part: 64 key rows of k_hat (fp16), D/8 data chunks + 1 pad chunk each;
+//   V part: D head-dim rows of V (bf16) over the 64 keys, 8 data chunks + 1 pad
+//           chunk each; inside each 16-key group the keys are stored in the
+//           order 0-3, 8-11, 4-7, 12-15 so that one 16-byte read gives the
+//           eight keys an MFMA lane consumes.
+// A row stride of 2^n + 1 chunks puts any 16 consecutive rows, read at the
+// same chunk, on 16 distinct 16-byte bank groups, and keeps every MFMA
+// fragment address an immediate offset from one per-lane base.
 // ---------------------------------------------------------------------------
-
-// Rows of 128 bytes (8 chunks): XOR with ((d >> 1) & 7) ^ ((d & 1) << 2) gives
-// distinct chunks to any 8 consecutive rows and, within the even and within
-// the odd rows of any 16 consecutive rows, so 16-byte reads of 16 rows at one
-// logical chunk hit distinct banks whether the LDS serves 8 or 16 lanes per
-// cycle.
-__host__ __device__ __forceinline__ int row128_swizzle(int d) { return ((d >> 1) & 7) ^ ((d & 1) << 2); }
-
 template <int D>
-__host__ __device__ __forceinline__ int k_chunk_swizzle(int c, int r) {
-  return D == 128 ? (c ^ (r & 15)) : (c ^ row128_swizzle(r));
-}
+struct TileLayout {
+  static constexpr int KROW = D / 8 + 1;
+  static constexpr int VROW = kKeyTile / 8 + 1;
+  static constexpr int KCHUNKS = kKeyTile * KROW;
+  static constexpr int VCHUNKS = D * VROW;
+  static constexpr int CHUNKS = KCHUNKS + VCHUNKS;
+  static_assert(CHUNKS % 64 == 0, "a tile is copied in whole 64-lane wave instructions");
+};
 
-__host__ __device__ __forceinline__ int v_chunk_swizzle(int c, int d) { return c ^ row128_swizzle(d); }
+inline int tile_chunks(int d) { return d == 128 ? TileLayout<128>::CHUNKS : TileLayout<64>::CHUNKS; }
 
 struct RopeQkArgs {
   const uint16_t* x;
@@ -66,16 +65,14 @@ struct KvPrepArgs {
   int rope_batched;    // table rows indexed by b * T + t (else t)
   int T, Hkv, n_tiles;
   float eps;
-  half_t* khat;
-  uint16_t* vt;
+  u32x4* tiles;        // [B * Hkv][n_tiles][TileLayout<D>::CHUNKS]
 };
 
 struct PrefillArgs {
   const uint16_t* q;
   const uint16_t* gate;
   uint16_t* out;
-  const half_t* khat;
-  const uint16_t* vt;
+  const u32x4* tiles;  // [B * Hkv][n_tiles][TileLayout<D>::CHUNKS]
   int64_t q_sb, q_st, g_sb, g_st, o_sb, o_st;
   const float2* rope;  // null on NoPE layers
   int rope_batched;

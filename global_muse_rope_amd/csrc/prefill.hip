@@ -31,6 +31,8 @@
 //   * Launch order: heaviest query blocks first (causal work grows with the
 //     block index), and groups of 8 consecutive query blocks of one KV head
 //     land on one XCD so they share K/V tiles in that XCD's L2.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace muse {
@@ -44,17 +46,15 @@ struct PrefillCfg {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int THREADS = NW * 64;
-  static constexpr int KCH = 8 * D;  // 16-byte chunks of one K (or V) tile
-  static constexpr int CPT = KCH / THREADS;
   static_assert(32 % G == 0 || G == 32, "a 32-row block must hold whole tokens");
-  static_assert(KCH % THREADS == 0, "tile copy must divide evenly");
 };
 
 template <int D, int G, int NW, int MB>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D, G, NW, MB>;
-  constexpr int NBUF = 3;
-  __shared__ u32x4 smem[NBUF][2 * C::KCH];
+  using TL = TileLayout<D>;
+  constexpr int NBUF = 4;
+  __shared__ u32x4 smem[NBUF][TL::CHUNKS];
 
   // ---- workgroup -> (sequence, KV head, query block) ----
   const int nblk = gridDim.x;
@@ -144,8 +144,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int mid_hi = min((t0 + 1) / kKeyTile, tile_hi + 1);  // need k0 + 63 <= t0
   const int m_lo = min(mid_lo, mid_hi);
   const int m_hi = max(mid_hi, m_lo);
-  const int tw0 = t0 + (w * MB * 32) / G;
-  const int tw1 = t0 + ((w + 1) * MB * 32 - 1) / G;
 
   // per-lane visible range of each row block: key in [lo_t, lo_t + span]
   int lo_t[MB], span[MB];
@@ -155,8 +153,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     span[mb] = tq[mb] - lo_t[mb];
   }
 
-  const u32x4* ksrc = reinterpret_cast<const u32x4*>(a.khat) + static_cast<int64_t>(bh) * a.n_tiles * C::KCH;
-  const u32x4* vsrc = reinterpret_cast<const u32x4*>(a.vt) + static_cast<int64_t>(bh) * a.n_tiles * C::KCH;
+  const u32x4* tsrc = a.tiles + static_cast<int64_t>(bh) * a.n_tiles * TL::CHUNKS;
 
   f32x16 o[MB][C::DB];
   float lsum[MB];
@@ -169,143 +166,173 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       for (int i = 0; i < 16; ++i) o[mb][db][i] = 0.f;
   }
 
-  // ---- tile staging: three LDS buffers, tiles i and i+1 resident while
-  // tile i+2 is in flight in registers ----
-  u32x4 pre[2 * C::CPT];
-  auto gload = [&](int tile) {
-    const int64_t base = static_cast<int64_t>(tile) * C::KCH;
+  // ---- tile staging: four LDS buffers; tiles i-1 (its V still feeds the
+  // pipelined PV), i and i+1 resident while the copy of tile i+2 streams
+  // straight from global memory into LDS (global_load_lds_dwordx4: no register
+  // staging, no LDS store instructions).  Each wave instruction copies 64
+  // consecutive 16-byte chunks, so the LDS image of a tile equals its
+  // workspace image. ----
+  auto gload = [&](int tile, int buf) {
+    const u32x4* src = tsrc + static_cast<int64_t>(tile) * TL::CHUNKS;
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      pre[i] = ksrc[base + tid + i * C::THREADS];
-      pre[C::CPT + i] = vsrc[base + tid + i * C::THREADS];
-    }
+    for (int c = 0; c < TL::CHUNKS; c += C::THREADS)
+      if (c + w * 64 < TL::CHUNKS) copy16_to_lds(src + c + w * 64 + lane, &smem[buf][c + w * 64]);
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      smem[buf][tid + i * C::THREADS] = pre[i];
-      smem[buf][C::KCH + tid + i * C::THREADS] = pre[C::CPT + i];
-    }
-  };
-  // after computing tile `tile`: stage tile+2, fetch tile+3, barrier
+  // after computing tile `tile`: publish tile+2 (its copy was issued one step
+  // earlier; the barrier waits for it), then start tile+3 into the buffer of
+  // tile-1, which no wave reads any more
   auto advance = [&](int tile) {
     const int rel = tile - tile_lo;
-    if (tile + 2 <= tile_hi) sstore((rel + 2) % NBUF);
-    if (tile + 3 <= tile_hi) gload(tile + 3);
     __syncthreads();
+    if (tile + 3 <= tile_hi) gload(tile + 3, (rel + 3) % NBUF);
   };
 
   bf16x2 ones;
   ones[0] = static_cast<bf16_t>(1.0f);
   ones[1] = static_cast<bf16_t>(1.0f);
 
-  auto qk = [&](int tile, int kb, f32x16* s) {
-    const half_t* Ks = reinterpret_cast<const half_t*>(&smem[(tile - tile_lo) % NBUF][0]);
-    const int krow = 32 * kb + l32;
+  // Edge tiles (a wave-uniform flag) overwrite the logits of invisible keys
+  // with -inf, in a branch taken only on those tiles.
+  auto mask_logits = [&](f32x16* sl, bool masked, int k0) {
+    if (masked) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int kbase = k0 + 4 * h2 - lo_t[mb];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int off = 8 * (i >> 2) + (i & 3);
+          sl[mb][i] = static_cast<unsigned>(kbase + off) <= static_cast<unsigned>(span[mb]) ? sl[mb][i] : -INFINITY;
+        }
+      }
+    }
+  };
+
+  // One half-step, written in issue order.  Matrix-core items of
+  //   S_out = QK(tile_q, half kb_q)   and   O += PV(tile_v, half kb_v; P_in)
+  // alternate (a dependent MFMA chain on one accumulator runs at half rate,
+  // so the QK chain is interleaved with the independent PV accumulators);
+  // each LDS fragment read is issued QDEPTH items before its MFMA; between
+  // the MFMAs the vector ALUs turn S_in into P_out = exp2(S_in) (logits are
+  // bounded by 63.2 in log2 units, so no running maximum is needed) and
+  // accumulate the row sums.  sched_barrier(0) walls keep this order.
+  // Every fragment address is a compile-time offset from one per-lane base.
+  const int k_lane = (l32 * TL::KROW + h2) * 16;              // bytes
+  const int v_lane = (TL::KCHUNKS + l32 * TL::VROW + h2) * 16;  // bytes
+  auto half_step = [&](int tile_q, int kb_q, f32x16* s_out, int tile_v, int kb_v, bf16x8 (*p_in)[2],
+                       const f32x16* s_in, bf16x8 (*p_out)[2]) {
+    constexpr int NK = C::KS;
+    constexpr int NV = 2 * C::DB;
+    constexpr int N = NK + NV;
+    constexpr int M = NK < NV ? NK : NV;
+    constexpr int QDEPTH = 3;
+    constexpr int NE = 16;  // logits per lane per row block
+    const char* kbase = reinterpret_cast<const char*>(&smem[(tile_q - tile_lo) % NBUF][0]) + k_lane +
+                        32 * kb_q * TL::KROW * 16;
+    const char* vbase = reinterpret_cast<const char*>(&smem[(tile_v - tile_lo) % NBUF][0]) + v_lane +
+                        4 * kb_v * 16;
+    auto is_k = [](int j) { return j < 2 * M ? (j % 2 == 0) : (NK > NV); };
+    auto idx = [](int j) { return j < 2 * M ? j / 2 : j - M; };
+    auto load = [&](int j) -> u32x4 {
+      const int i = idx(j);
+      if (is_k(j)) return *reinterpret_cast<const u32x4*>(kbase + 2 * i * 16);
+      const int st = i / C::DB, db = i % C::DB;
+      return *reinterpret_cast<const u32x4*>(vbase + (32 * db * TL::VROW + 2 * st) * 16);
+    };
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[mb][i] = 0.f;
+      for (int e = 0; e < 16; ++e) s_out[mb][e] = 0.f;
+    u32x4 q[QDEPTH];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const half8 kf = *reinterpret_cast<const half8*>(Ks + krow * D + k_chunk_swizzle<D>(2 * ks + h2, krow) * 8);
+    for (int j = 0; j < QDEPTH; ++j) q[j] = load(j);
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[mb][ks], s[mb], 0, 0, 0);
-    }
-  };
-  // p = exp2(logit): logits are bounded by 63.2 in log2 units (no max needed)
-  auto softmax = [&](const f32x16* s, bf16x8 (*p)[2], bool masked, int k0) {
+    for (int j = 0; j < N; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4 f = q[j % QDEPTH];
+      const int i = idx(j);
+      if (is_k(j)) {
+        const half8 kf = __builtin_bit_cast(half8, f);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int kbase = k0 + 4 * h2 - lo_t[mb];
+        for (int mb = 0; mb < MB; ++mb)
+          s_out[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[mb][i], s_out[mb], 0, 0, 0);
+      } else {
+        const int st = i / C::DB, db = i % C::DB;
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, f);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = s[mb][i];
-        if (masked) {
-          const int off = 8 * (i >> 2) + (i & 3);
-          x = static_cast<unsigned>(kbase + off) <= static_cast<unsigned>(span[mb]) ? x : -INFINITY;
-        }
-        p[mb][i >> 3][i & 7] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(x));
+        for (int mb = 0; mb < MB; ++mb)
+          o[mb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_in[mb][st], o[mb][db], 0, 0, 0);
       }
+      if (j + QDEPTH < N) q[j % QDEPTH] = load(j + QDEPTH);
+      // this item's slice of the exponentials (pairs, so each pair's row sum
+      // is one packed dot product)
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
+      for (int e = (j * NE / N) & ~1; e < (((j + 1) * NE / N) & ~1); e += 2) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int mb = 0; mb < MB; ++mb) {
           bf16x2 pr;
-          pr[0] = p[mb][st][2 * j];
-          pr[1] = p[mb][st][2 * j + 1];
+          pr[0] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(s_in[mb][e]));
+          pr[1] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(s_in[mb][e + 1]));
+          p_out[mb][e >> 3][e & 7] = pr[0];
+          p_out[mb][e >> 3][(e & 7) + 1] = pr[1];
           lsum[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[mb], false);
         }
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
-  auto pv = [&](int tile, int kb, bf16x8 (*p)[2]) {
-    const uint16_t* Vs = reinterpret_cast<const uint16_t*>(&smem[(tile - tile_lo) % NBUF][C::KCH]);
+
+  // Software pipeline over half-tiles (32 keys): while the vector ALUs turn
+  // the logits of half h into probabilities, the matrix cores compute the
+  // logits of half h+1 and accumulate P V of half h-1.  Per tile the two
+  // halves swap the roles of the S and P registers, so no copies are needed.
+  // One loop body serves every tile (a single copy keeps register pressure
+  // low): the first tile's "previous half" has P = 0 over valid V data, and
+  // the last tile's "next half" recomputes logits that are never used.
+  f32x16 sc[MB], sn[MB];          // logits: current half, next half
+  bf16x8 pc[MB][2], pp[MB][2];    // probabilities: current half, previous half
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        const int dim = 32 * db + l32;
-        const bf16x8 vf =
-            *reinterpret_cast<const bf16x8*>(Vs + dim * kKeyTile + v_chunk_swizzle(4 * kb + 2 * st + h2, dim) * 8);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          o[mb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p[mb][st], o[mb][db], 0, 0, 0);
-      }
-  };
-  // one edge tile, masked per element, skipped by waves that see none of it
-  auto edge_tile = [&](int tile) {
-    const int k0 = tile * kKeyTile;
-    const bool any = (k0 <= tw1) && (a.W == 0 || k0 + kKeyTile - 1 > tw0 - a.W);
-    if (any) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s[MB];
-        bf16x8 p[MB][2];
-        qk(tile, kb, s);
-        softmax(s, p, true, k0 + 32 * kb);
-        pv(tile, kb, p);
-      }
-    }
-    advance(tile);
-  };
+      for (int e = 0; e < 8; ++e) pp[mb][st][e] = static_cast<bf16_t>(0.0f);
 
   // prologue: tiles 0 and 1 of the range into LDS, tile 2 in flight
-  gload(tile_lo);
-  sstore(0);
-  if (tile_lo + 1 <= tile_hi) {
-    gload(tile_lo + 1);
-    sstore(1);
-  }
-  if (tile_lo + 2 <= tile_hi) gload(tile_lo + 2);
+  gload(tile_lo, 0);
+  if (tile_lo + 1 <= tile_hi) gload(tile_lo + 1, 1);
   __syncthreads();
+  if (tile_lo + 2 <= tile_hi) gload(tile_lo + 2, 2);
 
-  int tile = tile_lo;
-  for (; tile < m_lo; ++tile) edge_tile(tile);
-  if (tile < m_hi) {
-    // software-pipelined middle: the logits of the next half-tile are
-    // computed on the matrix cores while the exponentials of the current one
-    // run on the vector ALUs.
-    f32x16 s0[MB], s1[MB];
-    bf16x8 p[MB][2];
-    qk(tile, 0, s0);
-    for (; tile < m_hi - 1; ++tile) {
-      qk(tile, 1, s1);
-      softmax(s0, p, false, 0);
-      pv(tile, 0, p);
-      qk(tile + 1, 0, s0);
-      softmax(s1, p, false, 0);
-      pv(tile, 1, p);
-      advance(tile);
-    }
-    qk(tile, 1, s1);
-    softmax(s0, p, false, 0);
-    pv(tile, 0, p);
-    softmax(s1, p, false, 0);
-    pv(tile, 1, p);
-    advance(tile);
-    ++tile;
+  // S(first tile, 0..31); the "previous" P is zero, so this PV adds nothing
+  // (its exponentials of zero logits are discarded with the row sums)
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sn[mb][e] = 0.f;
+  half_step(tile_lo, 0, sc, tile_lo, 0, pp, sn, pc);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) lsum[mb] = 0.f;
+  for (int t = tile_lo; t <= tile_hi; ++t) {
+    const bool masked = t < m_lo || t >= m_hi;
+    const int k0 = t * kKeyTile;
+    const int tprev = t > tile_lo ? t - 1 : t;
+    const int tnext = t < tile_hi ? t + 1 : t;
+    mask_logits(sc, masked, k0);
+    // S(t, 32..63) and O += P(t-1, 32..63) V  ||  P(t, 0..31)
+    half_step(t, 1, sn, tprev, 1, pp, sc, pc);
+    mask_logits(sn, masked, k0 + 32);
+    // S(t+1, 0..31) and O += P(t, 0..31) V  ||  P(t, 32..63)
+    half_step(tnext, 0, sc, t, 0, pc, sn, pp);
+    advance(t);
   }
-  for (; tile <= tile_hi; ++tile) edge_tile(tile);
+  // drain: O += P(last, 32..63) V; the logits and exponentials computed
+  // alongside are unused, and the row sums are restored
+  float lkeep[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) lkeep[mb] = lsum[mb];
+  half_step(tile_hi, 0, sn, tile_hi, 1, pp, sc, pc);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) lsum[mb] = lkeep[mb];
 
   // ---- epilogue: 1/sum, per-head output norm, sigmoid gate, bf16 store ----
 #pragma unroll
@@ -355,14 +382,34 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 // Host side
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kWaves = 8;
-constexpr int kRowBlocks = 1;
+// Launch shape per head width: waves per workgroup and 32-row MFMA blocks per
+// wave.  Head width 128: 8 waves x 32 rows (two waves per SIMD, so one wave's
+// exponentials overlap the other's matrix-core work).  Head width 64: the
+// same shape needs half the registers, so two workgroups share a CU.
+#ifndef MUSE_PREFILL_WAVES_D128
+#define MUSE_PREFILL_WAVES_D128 8
+#endif
+#ifndef MUSE_PREFILL_MB_D128
+#define MUSE_PREFILL_MB_D128 1
+#endif
+#ifndef MUSE_PREFILL_WAVES_D64
+#define MUSE_PREFILL_WAVES_D64 8
+#endif
+#ifndef MUSE_PREFILL_MB_D64
+#define MUSE_PREFILL_MB_D64 1
+#endif
+template <int D>
+struct LaunchShape {
+  static constexpr int NW = D == 128 ? MUSE_PREFILL_WAVES_D128 : MUSE_PREFILL_WAVES_D64;
+  static constexpr int MB = D == 128 ? MUSE_PREFILL_MB_D128 : MUSE_PREFILL_MB_D64;
+};
 
 template <int D, int G>
 hipError_t launch_dg(const PrefillArgs& a, hipStream_t st) {
-  using C = PrefillCfg<D, G, kWaves, kRowBlocks>;
+  constexpr int NW = LaunchShape<D>::NW, MB = LaunchShape<D>::MB;
+  using C = PrefillCfg<D, G, NW, MB>;
   const unsigned grid = static_cast<unsigned>(a.n_qblocks_pad) * static_cast<unsigned>(a.batch_heads);
-  hipLaunchKernelGGL((prefill_kernel<D, G, kWaves, kRowBlocks>), dim3(grid), dim3(C::THREADS), 0, st, a);
+  hipLaunchKernelGGL((prefill_kernel<D, G, NW, MB>), dim3(grid), dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
 }
 
@@ -379,7 +426,9 @@ hipError_t launch_d(int g, const PrefillArgs& a, hipStream_t st) {
 }
 }  // namespace
 
-int prefill_rows_per_block(int, int) { return kWaves * kRowBlocks * 32; }
+int prefill_rows_per_block(int d, int) {
+  return d == 128 ? LaunchShape<128>::NW * LaunchShape<128>::MB * 32 : LaunchShape<64>::NW * LaunchShape<64>::MB * 32;
+}
 
 int prefill_qblock_group() { return kQBlockGroup; }
 

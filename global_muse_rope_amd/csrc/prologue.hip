@@ -73,9 +73,9 @@ __global__ __launch_bounds__(256) void rope_table_kernel(RopeTableArgs a) {
 
 // ---------------------------------------------------------------------------
 // Prefill key/value preparation: one 64-key tile of one (sequence, KV head)
-// per workgroup.  Writes k_hat as fp16 [tile][key][D] and V transposed as
-// bf16 [tile][D][key], both in the chunk-swizzled order the attention kernel
-// copies straight into LDS (see kernels.h for the layouts).
+// per workgroup.  Writes the tile image the attention kernel copies straight
+// into LDS: k_hat as fp16 key rows and V transposed to head-dim rows (bf16),
+// both with one pad chunk per row (layout in TileLayout).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
@@ -126,7 +126,9 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     lo[e] = x0;
     hi[e] = x1;
   }
-  half_t* kdst = a.khat + (bh * a.n_tiles + tile) * (BK * D) + r * D;
+  using TL = TileLayout<D>;
+  u32x4* tdst = a.tiles + (bh * a.n_tiles + tile) * TL::CHUNKS;
+  u32x4* kdst = tdst + r * TL::KROW;
 #pragma unroll
   for (int c = 0; c < RUN / 8; ++c) {
     u32x4 w0, w1;
@@ -137,8 +139,8 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     }
     const int c0 = (qq * RUN) / 8 + c;             // logical chunk, first half
     const int c1 = (D / 2 + qq * RUN) / 8 + c;     // logical chunk, second half
-    *reinterpret_cast<u32x4*>(kdst + k_chunk_swizzle<D>(c0, r) * 8) = w0;
-    *reinterpret_cast<u32x4*>(kdst + k_chunk_swizzle<D>(c1, r) * 8) = w1;
+    kdst[c0] = w0;
+    kdst[c1] = w1;
   }
 
   // ---- values: stage the tile, write it transposed ----
@@ -156,7 +158,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     *reinterpret_cast<u32x2*>(&vs[r][D / 2 + qq * RUN + c * 8 + 4]) = u32x2{w1[2], w1[3]};
   }
   __syncthreads();
-  uint16_t* vdst = a.vt + (bh * a.n_tiles + tile) * (BK * D);
+  u32x4* vdst = tdst + TL::KCHUNKS;
   constexpr int CHUNKS = D * BK / 8;  // 16-byte chunks of the transposed tile
   for (int ci = tid; ci < CHUNKS; ci += 256) {
     const int d = ci / (BK / 8);
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = static_cast<uint32_t>(e[2 * i]) | (static_cast<uint32_t>(e[2 * i + 1]) << 16);
-    *reinterpret_cast<u32x4*>(vdst + d * BK + v_chunk_swizzle(pc, d) * 8) = w;
+    vdst[d * TL::VROW + pc] = w;
   }
 }
 
