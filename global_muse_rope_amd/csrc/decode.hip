@@ -207,23 +207,35 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // register prefetch of one 32-key sub-chunk
+  // register prefetch of one 32-key sub-chunk.  Row r = 4g + i of key tile kt
+  // holds entry 8g + 4kt + i, so the eight entries a lane needs for P V are
+  // contiguous in the head-dim-major V rows (one 16-byte load per fragment).
   u32x4 kr[2][DS];
-  u32x2 vr[DB][2];
+  u32x4 vr[DB];
   auto load = [&](int s0) {
+    const bool kok = tile_ok(s0 + 8 * (col >> 2));
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int idx0 = s0 + 16 * kt;
-      const bool ok = tile_ok(idx0);
-      const int64_t ka = ok ? kaddr(idx0 + col) : 0;
+      const int64_t ka = kok ? kaddr(s0 + 8 * (col >> 2) + 4 * kt + (col & 3)) : 0;
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
-        kr[kt][ds] = ok ? *reinterpret_cast<const u32x4*>(kc + ka + 32 * ds + 8 * g4) : u32x4{0, 0, 0, 0};
-      const int64_t va = ok ? vaddr(idx0 + 4 * g4) : 0;
+        kr[kt][ds] = kok ? *reinterpret_cast<const u32x4*>(kc + ka + 32 * ds + 8 * g4) : u32x4{0, 0, 0, 0};
+    }
+    const bool vok = tile_ok(s0 + 8 * g4);
+    const int64_t va = vok ? vaddr(s0 + 8 * g4) : 0;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+      vr[db] = vok ? *reinterpret_cast<const u32x4*>(vc + va + static_cast<int64_t>(16 * db + col) * vstride)
+                   : u32x4{0, 0, 0, 0};
+    // entries at or past the end may never have been written: zero them so
+    // that p = 0 cannot meet a non-finite value
+    const int nv = hr.end - (s0 + 8 * g4);
+    if (vok && nv < 8) {
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        vr[db][kt] = ok ? *reinterpret_cast<const u32x2*>(vc + va + static_cast<int64_t>(16 * db + col) * vstride)
-                        : u32x2{0, 0};
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd)
+          vr[db][wd] = 2 * wd >= nv ? 0u : (2 * wd + 1 >= nv ? (vr[db][wd] & 0xffffu) : vr[db][wd]);
     }
   };
 
@@ -232,19 +244,16 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   for (int sc = w; sc < nsub; sc += NW) {
     const int s0 = c0 + 32 * sc;
     u32x4 kcur[2][DS];
-    u32x2 vcur[DB][2];
+    u32x4 vcur[DB];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) kcur[kt][ds] = kr[kt][ds];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      vcur[db][0] = vr[db][0];
-      vcur[db][1] = vr[db][1];
-    }
+    for (int db = 0; db < DB; ++db) vcur[db] = vr[db];
     if (sc + NW < nsub) load(c0 + 32 * (sc + NW));
 
-    // S^T tiles: keys s0 + 16*kt + 4*g4 + i, head col
+    // S^T tiles: entries s0 + 8*g4 + 4*kt + i, head col
     float s[2][4];
     float tmax = NEG;
 #pragma unroll
@@ -258,7 +267,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int idx = s0 + 16 * kt + 4 * g4 + i;
+        const int idx = s0 + 8 * g4 + 4 * kt + i;
         s[kt][i] = hist_valid(hr, idx) ? acc[i] : NEG;
         tmax = fmaxf(tmax, s[kt][i]);
       }
@@ -284,8 +293,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       o[db] *= alpha;
-      u32x4 vw = {vcur[db][0][0], vcur[db][0][1], vcur[db][1][0], vcur[db][1][1]};
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, vw);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, vcur[db]);
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[db], 0, 0, 0);
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[db], 0, 0, 0);
     }

@@ -310,3 +310,53 @@ def test_decode_visibility_exact(kind, w):
             expect = (markers >= lo) & (markers <= hi - 1)      # cached positions only (new v is zero)
             for h in range(hq):
                 assert np.array_equal(seen[b, h], expect), (b, L, start)
+
+
+@pytest.mark.parametrize("kind,w,d,lens", [
+    ("paged", 0, 64, [300, 77, 1, 2, 33, 64, 17]),
+    ("ring", 256, 64, [1, 2, 9, 100, 255]),
+    ("paged", 0, 128, [5000, 17, 40]),
+])
+def test_decode_unwritten_entries_ignored(kind, w, d, lens):
+    """Cache entries never written (ring slots and page rows at or past the
+    sequence's last position, and unused pages) may hold any bits: poisoned
+    with NaN they must leave the output bit-identical to zero-filled ones."""
+    hq, hkv = (16, 2) if d == 64 else (32, 2)
+    layer = Layer(hq=hq, hkv=hkv, d=d, window=w, theta=10000.0 if w else 0.0,
+                  scale=SPARK_SCALE, out_norm=(d == 64), out_eps=1e-6)
+    B = len(lens)
+    lens = np.array(lens, dtype=np.int32)
+    new = {n: to_dev(synth.normal_bf16_bits(3, sid, shp)) for n, sid, shp in
+           [("q", 12, (B, hq, d)), ("k", 13, (B, hkv, d)), ("v", 14, (B, hkv, d)), ("g", 15, (B, hq, d))]}
+    kv = torch.from_numpy(lens).to(DEV)
+    outs = []
+    for poison in (False, True):
+        cache, _, _ = make_cache(kind, layer, B, lens, page_tokens=16)
+        if poison:
+            k, v = cache.k, cache.v
+            if kind == "ring":
+                for b in range(B):
+                    L = int(lens[b])
+                    if L - 1 < w:
+                        k[b, :, L - 1:, :] = float("nan")
+                        v[b, :, :, L - 1:] = float("nan")
+            else:
+                table = cache.block_table.cpu().numpy()
+                used = set()
+                for b in range(B):
+                    L = int(lens[b])
+                    for p in range(table.shape[1] * 16):
+                        pg, r = int(table[b, p // 16]), p % 16
+                        if p < L - 1:
+                            used.add((pg, r))
+                for pg in range(k.shape[0]):
+                    for r in range(16):
+                        if (pg, r) not in used:
+                            k[pg, :, r, :] = float("nan")
+                            v[pg, :, :, r] = float("nan")
+        y = ma.decode(ma.LayerParams.from_layer(layer), new["q"], new["k"], new["v"], new["g"], kv,
+                      int(lens.max()), cache)
+        torch.cuda.synchronize()
+        outs.append(y.float().cpu())
+    assert torch.isfinite(outs[1]).all()
+    assert torch.equal(outs[0], outs[1])
