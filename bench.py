@@ -78,7 +78,7 @@ PREFILL_SOURCES = ["prefill.hip", "kernels.h", "common.h"]
 DECODE_SOURCES = ["decode.hip", "kernels.h", "common.h"]
 
 
-def committed_traffic(name, digest, per_launch_alg):
+def committed_traffic(name, digest):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they
     were taken on the current kernel source."""
     path = os.path.join(PROFILES, f"{name}_traffic.json")
@@ -213,18 +213,79 @@ def cpu_baseline(cfg, gpu_out, budget_s=15.0):
 
 
 def pmc_pass(torch, ma, workload):
-    """A short run for rocprofv3 counter passes: two prefill steps of one
-    workload (default: the benchmark workload) and one plain 1 GiB device copy
-    as the calibration of the byte counters."""
+    """A short run for rocprofv3 counter passes: two steps of one workload
+    (prefill or decode; default: the benchmark workload) and one plain 1 GiB
+    device copy as the calibration of the byte counters."""
     from synth import workloads as wl
-    cfg = {c.name: c for c in wl.PREFILL}[workload]
-    prefill_case(cfg, 1, 1, HipEvents(), torch, ma)
+    cfgs = {c.name: c for c in wl.PREFILL + wl.DECODE}
+    cfg = cfgs[workload]
+    if cfg in wl.DECODE:
+        decode_case(cfg, 1, 1, HipEvents(), torch, ma)
+    else:
+        prefill_case(cfg, 1, 1, HipEvents(), torch, ma)
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     b.copy_(a)
     torch.cuda.synchronize()
-    log("pmc pass done: 2 prefill steps + 1 GiB copy")
+    log(f"pmc pass done: 2 steps of {workload} + 1 GiB copy")
+
+
+def _counter_rows(path):
+    """(kernel name, counter value) per dispatch from a rocprofv3 counter CSV."""
+    import csv
+    out = []
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def traffic_summary(workload, kernel, fetch_csv, write_csv, commands):
+    """HBM bytes per launch of `kernel` from one FETCH_SIZE and one WRITE_SIZE
+    rocprofv3 pass over `bench.py --pmc-pass`, each scaled by what the same
+    counter reads for the pass's plain 1 GiB copy; written next to the other
+    profile summaries with the digest of the kernel sources it was taken on."""
+    copy_bytes = float(1 << 30)
+    res = {"workload": workload, "kernel": kernel, "commands": commands}
+    total = 0.0
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path)
+        kern = [v for n, v in rows if kernel in n]
+        copy = [v for n, v in rows if "copyBuffer" in n]   # the runtime's blit kernel doing the 1 GiB copy
+        if not kern or not copy:
+            raise SystemExit(f"{path}: no {kernel} or copy dispatch found")
+        kib = sum(kern) / len(kern)
+        copy_kib = max(copy)
+        factor = (copy_bytes / 1024) / copy_kib
+        res[name] = {"kib_per_dispatch": kib, "dispatches": len(kern), "copy_kib": copy_kib,
+                     "scale": round(factor, 4), "bytes_per_launch": kib * 1024 * factor}
+        total += kib * 1024 * factor
+    res["hbm_bytes_per_launch"] = total
+    srcs = PREFILL_SOURCES if "prefill" in kernel else DECODE_SOURCES
+    res["source_digest"] = source_digest(srcs)
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
+def only_case(name, steps, warmup, torch, ma):
+    """Time one workload by itself (for a per-workload kernel trace)."""
+    from synth import workloads as wl
+    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE}[name]
+    events = HipEvents()
+    if cfg in wl.DECODE:
+        r = decode_case(cfg, steps, warmup, events, torch, ma, flush=cfg.layer.window > 0)
+        print(json.dumps({"workload": name, "kernel": "decode_split_kernel", "kernel_ms": round(r["kernel_ms"], 4),
+                          "GB/s": round(r["gbs"], 1), "ms_per_step": round(r["ms_per_step"], 4),
+                          "steps": steps, "warmup": warmup}), flush=True)
+    else:
+        r = prefill_case(cfg, steps, warmup, events, torch, ma)
+        print(json.dumps({"workload": name, "kernel": "prefill_kernel", "kernel_ms": round(r["kernel_ms"], 4),
+                          "kernel_TFLOP/s": round(r["kernel_tflops"], 2), "step_TFLOP/s": round(r["tflops"], 2),
+                          "ms_per_step": round(r["ms_per_step"], 4), "steps": steps, "warmup": warmup}),
+              flush=True)
 
 
 def main():
@@ -237,7 +298,14 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true")
     ap.add_argument("--pmc-workload", default="glimmer_local_prefill_32k")
+    ap.add_argument("--only", metavar="WORKLOAD", help="time one workload by itself and print its line")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM-traffic summary of two counter passes (no GPU needed)")
+    ap.add_argument("--commands", default="", help="the rocprofv3 commands, recorded in the summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, args.commands)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
@@ -254,6 +322,9 @@ def main():
     if args.pmc_pass:
         pmc_pass(torch, ma, args.pmc_workload)
         return
+    if args.only:
+        only_case(args.only, args.steps, args.warmup, torch, ma)
+        return
     events = HipEvents()
     props = torch.cuda.get_device_properties(0)
 
@@ -264,7 +335,7 @@ def main():
     log(f"  {main_res['tflops']:.1f} TFLOP/s step, attention kernel {main_res['kernel_ms']:.3f} ms "
         f"({main_res['kernel_tflops']:.1f} TFLOP/s)")
     digest = source_digest(PREFILL_SOURCES)
-    traffic = committed_traffic("prefill_glimmer_local_32k", digest, main_res["flops"])
+    traffic = committed_traffic(f"prefill_kernel_{cfg.name}", digest)
     result = {
         "metric": METRIC,
         "value": round(main_res["tflops"], 2),
