@@ -47,6 +47,7 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
         e = ctypes.c_void_p()
@@ -165,6 +166,30 @@ def decode_case(cfg, steps, warmup, events, torch, ma, flush=False):
     del s, ws, out, scrub
     torch.cuda.empty_cache()
     return res
+
+
+def copy_bandwidth(torch, events, nbytes=2 << 30, reps=5):
+    """A plain device-to-device copy (the runtime's blit kernel) of `nbytes`:
+    bytes read + written per second, the practical HBM ceiling the decode
+    figures are also compared with."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = events.create(), events.create()
+    stream = torch.cuda.current_stream().cuda_stream
+    hip = events.hip
+    hip.hipEventRecord(e0, stream)
+    for _ in range(reps):
+        b.copy_(a)
+    hip.hipEventRecord(e1, stream)
+    torch.cuda.synchronize()
+    ms = events.elapsed_ms(e0, e1) / reps
+    events.destroy(e0)
+    events.destroy(e1)
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(cfg, gpu_out, budget_s=15.0):
@@ -366,6 +391,9 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_decode:
+        copy_gbs = copy_bandwidth(torch, events)
+        log(f"device copy {copy_gbs:.0f} GB/s (read + write)")
+        result["hbm_copy_gbs"] = round(copy_gbs, 1)
         dec = {}
         for dcfg, steps, flush in [(wl.SPARK_DECODE_GLOBAL, 10, False), (wl.SPARK_DECODE_LOCAL, 20, True)]:
             log(f"decode {dcfg.name}")
@@ -375,7 +403,8 @@ def main():
                               "kernel_ms": round(r["kernel_ms"], 4), "ms_per_step": round(r["ms_per_step"], 4),
                               "kv_bytes_per_step": r["kv_bytes"], "cache_flushed": flush,
                               "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS,
-                                           "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4)}}
+                                           "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                                           "frac_of_copy": round(r["gbs"] / copy_gbs, 4)}}
         result["decode"] = dec
 
     if not args.quick:

@@ -460,8 +460,24 @@ def _sign_flip_rope(x, positions, theta):
     return oracle.attention.__dict__["_orig_rope"](x, -np.asarray(positions), theta)
 
 
+def _interleaved_gqa_attend(qh_rows, row_index, kh, v, layer):
+    """attend_rows with query head h mapped to KV head h mod Hkv (a plausible
+    mix-up of the contiguous grouping)."""
+    kh = np.asarray(kh, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty(np.shape(qh_rows), dtype=np.float64)
+    for r, i in enumerate(row_index):
+        lo, hi = oracle.visible_range(int(i), layer.window)
+        for h in range(layer.hq):
+            kv = h % layer.hkv
+            lg = kh[lo:hi + 1, kv, :] @ qh_rows[r, h] / np.sqrt(layer.d)
+            w = oracle.softmax(lg)
+            out[r, h] = w @ v[lo:hi + 1, kv, :]
+    return out
+
+
 @pytest.mark.parametrize("mistake", ["adjacent_pairs", "rope_sign", "eps_outside", "window_off_by_one",
-                                     "whole_vector_onorm", "no_query_scale"])
+                                     "whole_vector_onorm", "no_query_scale", "interleaved_gqa"])
 def test_planted_mistakes_fail_the_library_pin(monkeypatch, mistake):
     import oracle.attention as A
     layer = LIB_CASES[0]
@@ -483,6 +499,8 @@ def test_planted_mistakes_fail_the_library_pin(monkeypatch, mistake):
                 o = o / np.sqrt(np.mean(flat * flat, -1) + lyr.out_eps)[:, None, None]
             return o * A.sigmoid(gate)
         monkeypatch.setattr(A, "output_epilogue", whole)
+    elif mistake == "interleaved_gqa":
+        monkeypatch.setattr(A, "attend_rows", _interleaved_gqa_attend)
     elif mistake == "no_query_scale":
         from dataclasses import replace
         orig = A.query_prologue
