@@ -23,7 +23,7 @@
 //     The S^T accumulator layout is exactly the P^T operand layout of the
 //     second MFMA, so P never leaves registers.
 //   * Tiles are copied verbatim from the pre-swizzled workspace into a
-//     three-buffer LDS ring (two tiles resident, the next in flight); only
+//     four-buffer LDS ring (three tiles resident, the next in flight); only
 //     tiles crossing the causal diagonal or the window start are masked, and
 //     a wave skips edge tiles it cannot see.  Between the edges the loop is
 //     software-pipelined: the logits of the next half-tile go to the matrix
@@ -269,9 +269,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       for (int e = (j * NE / N) & ~1; e < (((j + 1) * NE / N) & ~1); e += 2) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
+          // The empty asm statements pin the exponentials to this slot.  On
+          // the input side they stop the edge-tile mask from being folded into
+          // exp2 (exp2(-inf) = 0) and the exponentials from being hoisted; on
+          // the output side they stop machine sinking from moving them into
+          // the next block, past the matrix-core work they hide under.
+          float x0 = s_in[mb][e], x1 = s_in[mb][e + 1];
+          asm volatile("" : "+v"(x0), "+v"(x1));
           bf16x2 pr;
-          pr[0] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(s_in[mb][e]));
-          pr[1] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(s_in[mb][e + 1]));
+          pr[0] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(x0));
+          pr[1] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(x1));
+          uint32_t pw = __builtin_bit_cast(uint32_t, pr);
+          asm volatile("" : "+v"(pw));
+          pr = __builtin_bit_cast(bf16x2, pw);
           p_out[mb][e >> 3][e & 7] = pr[0];
           p_out[mb][e >> 3][(e & 7) + 1] = pr[1];
           lsum[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[mb], false);
