@@ -38,6 +38,19 @@
 namespace muse {
 
 constexpr int kQBlockGroup = 8;
+// LDS fragment queue depth (fragments in flight per wave) per head width.
+// Head width 64 keeps the register count low enough for two workgroups per CU.
+#ifndef MUSE_PREFILL_QD_D128
+#define MUSE_PREFILL_QD_D128 8
+#endif
+#ifndef MUSE_PREFILL_QD_D64
+#define MUSE_PREFILL_QD_D64 2
+#endif
+constexpr int kFragQueueD128 = MUSE_PREFILL_QD_D128;
+constexpr int kFragQueueD64 = MUSE_PREFILL_QD_D64;
+// s_waitcnt immediate that waits for vmcnt(0) only (expcnt and lgkmcnt at
+// their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 template <int D, int G, int NW, int MB>
 struct PrefillCfg {
@@ -83,52 +96,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
 
-  // ---- queries: load, weightless RMS norm, scale, RoPE, fp16 operands ----
-  half8 qf[MB][C::KS];
-  int tq[MB];
+  int tq[MB];  // token of this lane's query column in each row block
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int r = (w * MB + mb) * 32 + l32;
-    const int t = t0 + r / G;
-    const int hq = hk * G + (r % G);
-    tq[mb] = t;
-    float x[C::KS][8];
-    const bool valid = t < a.T;
-    const uint16_t* qp = a.q + b * a.q_sb + static_cast<int64_t>(t) * a.q_st + static_cast<int64_t>(hq) * D + 8 * h2;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 wv = {0, 0, 0, 0};
-      if (valid) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-      unpack_bf16x8(wv, x[ks]);
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
-    ss += __shfl_xor(ss, 32, kWave);
-    const float rs = a.qscale * __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.qk_eps);
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[ks][e] *= rs;
-    if (a.rope && valid) {
-      const float2* rt = a.rope + ((a.rope_batched ? static_cast<int64_t>(b) * a.T : 0) + t) * (D / 2) + 8 * h2;
-#pragma unroll
-      for (int ks = 0; ks < C::KS / 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float2 cs = rt[16 * ks + e];
-          const float x0 = x[ks][e], x1 = x[ks + C::KS / 2][e];
-          x[ks][e] = x0 * cs.x - x1 * cs.y;
-          x[ks + C::KS / 2][e] = x1 * cs.x + x0 * cs.y;
-        }
-    }
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[mb][ks][e] = static_cast<half_t>(x[ks][e]);
-  }
+  for (int mb = 0; mb < MB; ++mb) tq[mb] = t0 + ((w * MB + mb) * 32 + l32) / G;
 
   // ---- key range: masked edge tiles and the unmasked middle ----
   const int tlast = min(t0 + C::BQ, a.T) - 1;      // last real token of the block
@@ -178,12 +148,71 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     for (int c = 0; c < TL::CHUNKS; c += C::THREADS)
       if (c + w * 64 < TL::CHUNKS) copy16_to_lds(src + c + w * 64 + lane, &smem[buf][c + w * 64]);
   };
+  // The first three tiles of the range start streaming into LDS before the
+  // query prologue, so their latency overlaps the query loads.
+  gload(tile_lo, 0);
+  if (tile_lo + 1 <= tile_hi) gload(tile_lo + 1, 1);
+  if (tile_lo + 2 <= tile_hi) gload(tile_lo + 2, 2);
+
+  // ---- queries: load, weightless RMS norm, scale, RoPE, fp16 operands ----
+  half8 qf[MB][C::KS];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = (w * MB + mb) * 32 + l32;
+    const int t = tq[mb];
+    const int hq = hk * G + (r % G);
+    float x[C::KS][8];
+    const bool valid = t < a.T;
+    const uint16_t* qp = a.q + b * a.q_sb + static_cast<int64_t>(t) * a.q_st + static_cast<int64_t>(hq) * D + 8 * h2;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      u32x4 wv = {0, 0, 0, 0};
+      if (valid) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      unpack_bf16x8(wv, x[ks]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[ks][e] * x[ks][e];
+    ss += __shfl_xor(ss, 32, kWave);
+    const float rs = a.qscale * __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.qk_eps);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[ks][e] *= rs;
+    if (a.rope && valid) {
+      const float2* rt = a.rope + ((a.rope_batched ? static_cast<int64_t>(b) * a.T : 0) + t) * (D / 2) + 8 * h2;
+#pragma unroll
+      for (int ks = 0; ks < C::KS / 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 cs = rt[16 * ks + e];
+          const float x0 = x[ks][e], x1 = x[ks + C::KS / 2][e];
+          x[ks][e] = x0 * cs.x - x1 * cs.y;
+          x[ks + C::KS / 2][e] = x1 * cs.x + x0 * cs.y;
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[mb][ks][e] = static_cast<half_t>(x[ks][e]);
+  }
+
   // after computing tile `tile`: publish tile+2 (its copy was issued one step
-  // earlier; the barrier waits for it), then start tile+3 into the buffer of
-  // tile-1, which no wave reads any more
+  // earlier), then start tile+3 into the buffer of tile-1, which no wave reads
+  // any more.  The barrier waits only for this wave's own tile copies
+  // (vmcnt): LDS fragment reads of the next half-tile, which target tiles
+  // that stay resident, remain in flight across it.  The empty asm statements
+  // keep the compiler from moving memory accesses across the barrier.
   auto advance = [&](int tile) {
     const int rel = tile - tile_lo;
-    __syncthreads();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
     if (tile + 3 <= tile_hi) gload(tile + 3, (rel + 3) % NBUF);
   };
 
@@ -207,50 +236,62 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // One half-step, written in issue order.  Matrix-core items of
-  //   S_out = QK(tile_q, half kb_q)   and   O += PV(tile_v, half kb_v; P_in)
-  // alternate (a dependent MFMA chain on one accumulator runs at half rate,
-  // so the QK chain is interleaved with the independent PV accumulators);
-  // each LDS fragment read is issued QDEPTH items before its MFMA; between
-  // the MFMAs the vector ALUs turn S_in into P_out = exp2(S_in) (logits are
-  // bounded by 63.2 in log2 units, so no running maximum is needed) and
-  // accumulate the row sums.  sched_barrier(0) walls keep this order.
-  // Every fragment address is a compile-time offset from one per-lane base.
+  // A half-step works on 32 keys.  Its matrix-core items alternate
+  //   K item i:  S_out += K(tile_q, half kb_q) fragment i  x  q_hat fragment i
+  //   V item i:  O     += V^T(tile_v, half kb_v) fragment i  x  P_in
+  // (a dependent MFMA chain on one accumulator runs at half rate, so the QK
+  // chain is interleaved with the independent PV accumulators); between them
+  // the vector ALUs turn S_in into P_out = exp2(S_in) (logits are bounded by
+  // 63.2 in log2 units, so no running maximum is needed) and accumulate the
+  // row sums.  sched_barrier(0) walls keep this order.
+  //
+  // LDS fragments stream through a queue of QD registers that runs
+  // continuously across half-steps and tiles: the fragment of item j is read
+  // QD items before its MFMA, the last QD reads of a half-step fetch the first
+  // items of the next one, so the read latency stays hidden behind QD matrix
+  // items and the queue never drains.  Every fragment address is a
+  // compile-time offset from a per-half-step base.
+  constexpr int NK = C::KS;
+  constexpr int NI = NK + 2 * C::DB;  // items per half-step (NK == 2 * DB)
+  static_assert(NK == 2 * C::DB, "K and V items alternate one to one");
+  constexpr int QD = D == 128 ? kFragQueueD128 : kFragQueueD64;
+  static_assert(NI % QD == 0, "queue slots line up across half-steps");
   const int k_lane = (l32 * TL::KROW + h2) * 16;              // bytes
   const int v_lane = (TL::KCHUNKS + l32 * TL::VROW + h2) * 16;  // bytes
-  auto half_step = [&](int tile_q, int kb_q, f32x16* s_out, int tile_v, int kb_v, bf16x8 (*p_in)[2],
-                       const f32x16* s_in, bf16x8 (*p_out)[2]) {
-    constexpr int NK = C::KS;
-    constexpr int NV = 2 * C::DB;
-    constexpr int N = NK + NV;
-    constexpr int M = NK < NV ? NK : NV;
-    constexpr int QDEPTH = 3;
+  struct Half {
+    const char* k;
+    const char* v;
+  };
+  auto half_at = [&](int tile_q, int kb_q, int tile_v, int kb_v) -> Half {
+    Half hb;
+    hb.k = reinterpret_cast<const char*>(&smem[(tile_q - tile_lo) % NBUF][0]) + k_lane + 32 * kb_q * TL::KROW * 16;
+    hb.v = reinterpret_cast<const char*>(&smem[(tile_v - tile_lo) % NBUF][0]) + v_lane + 4 * kb_v * 16;
+    return hb;
+  };
+  auto frag = [&](const Half& hb, int j) -> u32x4 {
+    const int i = j >> 1;
+    if ((j & 1) == 0) return *reinterpret_cast<const u32x4*>(hb.k + 2 * i * 16);
+    const int st = i / C::DB, db = i % C::DB;
+    return *reinterpret_cast<const u32x4*>(hb.v + (32 * db * TL::VROW + 2 * st) * 16);
+  };
+  u32x4 fq[QD];
+  auto prime = [&](const Half& hb) {
+#pragma unroll
+    for (int j = 0; j < QD; ++j) fq[j] = frag(hb, j);
+  };
+  auto half_step = [&](const Half& cur, const Half& nxt, f32x16* s_out, bf16x8 (*p_in)[2], const f32x16* s_in,
+                       bf16x8 (*p_out)[2]) {
     constexpr int NE = 16;  // logits per lane per row block
-    const char* kbase = reinterpret_cast<const char*>(&smem[(tile_q - tile_lo) % NBUF][0]) + k_lane +
-                        32 * kb_q * TL::KROW * 16;
-    const char* vbase = reinterpret_cast<const char*>(&smem[(tile_v - tile_lo) % NBUF][0]) + v_lane +
-                        4 * kb_v * 16;
-    auto is_k = [](int j) { return j < 2 * M ? (j % 2 == 0) : (NK > NV); };
-    auto idx = [](int j) { return j < 2 * M ? j / 2 : j - M; };
-    auto load = [&](int j) -> u32x4 {
-      const int i = idx(j);
-      if (is_k(j)) return *reinterpret_cast<const u32x4*>(kbase + 2 * i * 16);
-      const int st = i / C::DB, db = i % C::DB;
-      return *reinterpret_cast<const u32x4*>(vbase + (32 * db * TL::VROW + 2 * st) * 16);
-    };
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s_out[mb][e] = 0.f;
-    u32x4 q[QDEPTH];
 #pragma unroll
-    for (int j = 0; j < QDEPTH; ++j) q[j] = load(j);
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
+    for (int j = 0; j < NI; ++j) {
       __builtin_amdgcn_sched_barrier(0);
-      const u32x4 f = q[j % QDEPTH];
-      const int i = idx(j);
-      if (is_k(j)) {
+      const u32x4 f = fq[j % QD];
+      const int i = j >> 1;
+      if ((j & 1) == 0) {
         const half8 kf = __builtin_bit_cast(half8, f);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -262,11 +303,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         for (int mb = 0; mb < MB; ++mb)
           o[mb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_in[mb][st], o[mb][db], 0, 0, 0);
       }
-      if (j + QDEPTH < N) q[j % QDEPTH] = load(j + QDEPTH);
+      fq[j % QD] = j + QD < NI ? frag(cur, j + QD) : frag(nxt, j + QD - NI);
       // this item's slice of the exponentials (pairs, so each pair's row sum
       // is one packed dot product)
 #pragma unroll
-      for (int e = (j * NE / N) & ~1; e < (((j + 1) * NE / N) & ~1); e += 2) {
+      for (int e = (j * NE / NI) & ~1; e < (((j + 1) * NE / NI) & ~1); e += 2) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           // The empty asm statements pin the exponentials to this slot.  On
@@ -291,13 +332,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Software pipeline over half-tiles (32 keys): while the vector ALUs turn
-  // the logits of half h into probabilities, the matrix cores compute the
-  // logits of half h+1 and accumulate P V of half h-1.  Per tile the two
-  // halves swap the roles of the S and P registers, so no copies are needed.
-  // One loop body serves every tile (a single copy keeps register pressure
-  // low): the first tile's "previous half" has P = 0 over valid V data, and
-  // the last tile's "next half" recomputes logits that are never used.
+  // Software pipeline over half-tiles (32 keys): half-step k computes the
+  // logits of half k on the matrix cores, turns the logits of half k-1 into
+  // probabilities on the vector ALUs, and accumulates P V of half k-2.  Per
+  // tile the two half-steps swap the roles of the S and P registers, so no
+  // copies are needed.  One loop body serves every tile (a single copy keeps
+  // register pressure low): before the first tile, the "previous" P is zero
+  // over valid V data; the final drain step recomputes logits of the last
+  // tile that are never used.
   f32x16 sc[MB], sn[MB];          // logits: current half, next half
   bf16x8 pc[MB][2], pp[MB][2];    // probabilities: current half, previous half
 #pragma unroll
@@ -307,11 +349,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pp[mb][st][e] = static_cast<bf16_t>(0.0f);
 
-  // prologue: tiles 0 and 1 of the range into LDS, tile 2 in flight
-  gload(tile_lo, 0);
-  if (tile_lo + 1 <= tile_hi) gload(tile_lo + 1, 1);
+  // tiles 0, 1 and 2 of the range are resident after this barrier
   __syncthreads();
-  if (tile_lo + 2 <= tile_hi) gload(tile_lo + 2, 2);
 
   // S(first tile, 0..31); the "previous" P is zero, so this PV adds nothing
   // (its exponentials of zero logits are discarded with the row sums)
@@ -319,7 +358,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) sn[mb][e] = 0.f;
-  half_step(tile_lo, 0, sc, tile_lo, 0, pp, sn, pc);
+  {
+    const Half h0 = half_at(tile_lo, 0, tile_lo, 0);
+    prime(h0);
+    half_step(h0, half_at(tile_lo, 1, tile_lo, 1), sc, pp, sn, pc);
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) lsum[mb] = 0.f;
   for (int t = tile_lo; t <= tile_hi; ++t) {
@@ -327,12 +370,15 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     const int k0 = t * kKeyTile;
     const int tprev = t > tile_lo ? t - 1 : t;
     const int tnext = t < tile_hi ? t + 1 : t;
+    const Half ha = half_at(t, 1, tprev, 1);
+    const Half hb = half_at(tnext, 0, t, 0);
+    const Half hn = half_at(tnext, 1, t, 1);   // half A of the next tile (or the drain)
     mask_logits(sc, masked, k0);
     // S(t, 32..63) and O += P(t-1, 32..63) V  ||  P(t, 0..31)
-    half_step(t, 1, sn, tprev, 1, pp, sc, pc);
+    half_step(ha, hb, sn, pp, sc, pc);
     mask_logits(sn, masked, k0 + 32);
     // S(t+1, 0..31) and O += P(t, 0..31) V  ||  P(t, 32..63)
-    half_step(tnext, 0, sc, t, 0, pc, sn, pp);
+    half_step(hb, hn, sc, pc, sn, pp);
     advance(t);
   }
   // drain: O += P(last, 32..63) V; the logits and exponentials computed
@@ -340,11 +386,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   float lkeep[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) lkeep[mb] = lsum[mb];
-  half_step(tile_hi, 0, sn, tile_hi, 1, pp, sc, pc);
+  {
+    const Half hd = half_at(tile_hi, 1, tile_hi, 1);
+    half_step(hd, hd, sn, pp, sc, pc);
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) lsum[mb] = lkeep[mb];
 
-  // ---- epilogue: 1/sum, per-head output norm, sigmoid gate, bf16 store ----
+  // ---- epilogue: 1/sum, per-head output norm, then through LDS to row-major
+  // order for the sigmoid gate and coalesced bf16 stores.  In the MFMA layout
+  // a lane holds 4 consecutive dims of one (token, head) column, so direct
+  // stores would leave every 128-byte line written in 16-byte pieces by
+  // different instructions; staged, each lane loads 8 consecutive gate values
+  // and stores 8 consecutive outputs, and a wave covers whole lines. ----
+  constexpr int OROW = D + 4;                  // floats per staged column (padded)
+  static_assert(NW * MB * 32 * OROW * 4 <= NBUF * TL::CHUNKS * 16, "staging fits the tile buffers");
+  __syncthreads();                              // every wave is done with the tiles
+  float* ost = reinterpret_cast<float*>(&smem[0][0]) + w * (MB * 32 * OROW);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const float ltot = lsum[mb] + __shfl_xor(lsum[mb], 32, kWave);
@@ -362,28 +420,49 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       ss += __shfl_xor(ss, 32, kWave);
       rsn = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.out_eps);
     }
-    const int t = tq[mb];
+    float* col = ost + (mb * 32 + l32) * OROW;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = o[mb][db][4 * grp + e] * rsn;
+        *reinterpret_cast<f32x4*>(col + 32 * db + 8 * grp + 4 * h2) = v;
+      }
+  }
+  // LDS accesses of one wave execute in order; the fence keeps the compiler
+  // from reordering the reads below above the writes
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  constexpr int CPC = D / 8;                     // 8-value chunks per column
+  constexpr int NCH = MB * 32 * CPC;             // chunks per wave
+  static_assert(NCH % kWave == 0, "whole chunk rounds");
+#pragma unroll
+  for (int it = 0; it < NCH / kWave; ++it) {
+    const int k = it * kWave + lane;
+    const int cl = k / CPC;                      // wave-local column
+    const int d0 = (k % CPC) * 8;
+    const int r = w * MB * 32 + cl;              // block column
+    const int t = t0 + r / G;
     if (t < a.T) {
-      const int r = (w * MB + mb) * 32 + l32;
       const int hq = hk * G + (r % G);
-      const uint16_t* gp = a.gate + b * a.g_sb + static_cast<int64_t>(t) * a.g_st + static_cast<int64_t>(hq) * D;
-      uint16_t* op = a.out + b * a.o_sb + static_cast<int64_t>(t) * a.o_st + static_cast<int64_t>(hq) * D;
+      const u32x4 gw = *reinterpret_cast<const u32x4*>(a.gate + b * a.g_sb + static_cast<int64_t>(t) * a.g_st +
+                                                       static_cast<int64_t>(hq) * D + d0);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(ost + cl * OROW + d0);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(ost + cl * OROW + d0 + 4);
+      float g[8];
+      unpack_bf16x8(gw, g);
+      float y[8];
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+      for (int e = 0; e < 8; ++e) {
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g[e]));
+        y[e] = (e < 4 ? v0[e] : v1[e - 4]) * sg;
+      }
+      u32x4 ow;
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int d0 = 32 * db + 8 * grp + 4 * h2;
-          const u32x2 gw = *reinterpret_cast<const u32x2*>(gp + d0);
-          float g[4] = {__uint_as_float(gw[0] << 16), __uint_as_float(gw[0] & 0xffff0000u),
-                        __uint_as_float(gw[1] << 16), __uint_as_float(gw[1] & 0xffff0000u)};
-          float y[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g[e]));
-            y[e] = o[mb][db][4 * grp + e] * rsn * sg;
-          }
-          *reinterpret_cast<u32x2*>(op + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
-        }
+      for (int e = 0; e < 4; ++e) ow[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+      *reinterpret_cast<u32x4*>(a.out + b * a.o_sb + static_cast<int64_t>(t) * a.o_st + static_cast<int64_t>(hq) * D +
+                                d0) = ow;
     }
   }
 }
