@@ -117,7 +117,7 @@ DecodePlan decode_plan(int32_t max_kv_len, const muse_kv_cache* c) {
     d.chunk_tokens = c->capacity >= 256 ? 256 : ((c->capacity + 31) / 32) * 32;
     d.max_chunks = (c->capacity + d.chunk_tokens - 1) / d.chunk_tokens;
   } else {
-    d.chunk_tokens = 2048;
+    d.chunk_tokens = kPagedChunk;
     d.max_chunks = (max_kv_len + d.chunk_tokens - 1) / d.chunk_tokens + 1;
   }
   return d;

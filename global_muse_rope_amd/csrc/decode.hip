@@ -138,6 +138,16 @@ __device__ __forceinline__ bool hist_valid(const HistRange& r, int idx) {
 // ---------------------------------------------------------------------------
 // 2. split
 // ---------------------------------------------------------------------------
+// Block-table entries one paged chunk can touch: chunks of kPagedChunk
+// positions over pages of at least 16 positions, plus one for a chunk start
+// that is not page-aligned.
+constexpr int kMaxChunkPages = kPagedChunk / 16 + 2;
+// Register buffers of 32-entry sub-chunks per wave (PD - 1 in flight).
+#ifndef MUSE_DECODE_DEPTH
+#define MUSE_DECODE_DEPTH 2
+#endif
+constexpr int kDecodeDepth = MUSE_DECODE_DEPTH;
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int NW = 4;
@@ -147,6 +157,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   __shared__ float sm_o[NW][16][D + 1];
+  __shared__ int sm_page[kMaxChunkPages];
 
   const int item = blockIdx.x;
   const int c = item % a.max_chunks;
@@ -169,16 +180,38 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // q_hat hi/lo operands (B of S^T = K Q^T): head col, dims 8*g4 + 32*ds + [0, 8)
   bf16x8 qhi[DS], qlo[DS];
   {
-    const float* qp = a.qhat + (static_cast<int64_t>(b) * (a.Hkv * G) + hk * G + (col < G ? col : 0)) * D;
+    const float* qp = a.qhat + (static_cast<int64_t>(b) * (a.Hkv * G) + hk * G + (col < G ? col : 0)) * D + 8 * g4;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds)
+    for (int ds = 0; ds < DS; ++ds) {
+      f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+      if (col < G) {
+        x0 = *reinterpret_cast<const f32x4*>(qp + 32 * ds);
+        x1 = *reinterpret_cast<const f32x4*>(qp + 32 * ds + 4);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = col < G ? qp[32 * ds + 8 * g4 + e] : 0.f;
+        const float x = e < 4 ? x0[e] : x1[e - 4];
         const bf16_t hi = static_cast<bf16_t>(x);
         qhi[ds][e] = hi;
         qlo[ds][e] = static_cast<bf16_t>(x - static_cast<float>(hi));
       }
+    }
+  }
+
+  // Paged cache: the chunk's block-table entries go to LDS once, so the
+  // address of every prefetch is one LDS read away instead of a dependent
+  // global load (whose wait would also drain the loads already in flight).
+  // Absent or out-of-range pages are stored as -1.
+  const int pt = a.page_tokens;
+  const int pg0 = a.kind == MUSE_KV_RING ? 0 : c0 / pt;
+  if (a.kind != MUSE_KV_RING) {
+    const int npg = (c1 - 1) / pt - pg0 + 1;
+    for (int i = tid; i < npg; i += NW * kWave) {
+      const int pi = pg0 + i;
+      int page = pi < a.max_pages ? a.block_table[static_cast<int64_t>(b) * a.max_pages + pi] : -1;
+      sm_page[i] = (page >= 0 && page < a.num_pages) ? page : -1;
+    }
+    __syncthreads();
   }
 
   const uint16_t* kc = a.kc;
@@ -186,19 +219,18 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // address of (cached index idx) for this (b, hk): K row and V^T column
   auto kaddr = [&](int idx) -> int64_t {
     if (a.kind == MUSE_KV_RING) return ((static_cast<int64_t>(bh)) * a.capacity + idx) * D;
-    const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + idx / a.page_tokens];
-    return ((page * a.Hkv + hk) * a.page_tokens + idx % a.page_tokens) * D;
+    const int64_t page = sm_page[idx / pt - pg0];
+    return ((page * a.Hkv + hk) * pt + idx % pt) * D;
   };
   auto vaddr = [&](int idx) -> int64_t {  // element (dim 0, idx); dim stride = vstride
     if (a.kind == MUSE_KV_RING) return static_cast<int64_t>(bh) * D * a.capacity + idx;
-    const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + idx / a.page_tokens];
-    return (page * a.Hkv + hk) * D * a.page_tokens + idx % a.page_tokens;
+    const int64_t page = sm_page[idx / pt - pg0];
+    return (page * a.Hkv + hk) * D * pt + idx % pt;
   };
   auto tile_ok = [&](int idx0) -> bool {  // 16-key tile starting at idx0 may be loaded
     if (idx0 >= hr.end) return false;
     if (a.kind == MUSE_KV_RING) return true;
-    const int64_t page = a.block_table[static_cast<int64_t>(b) * a.max_pages + idx0 / a.page_tokens];
-    return page >= 0 && page < a.num_pages;
+    return sm_page[idx0 / pt - pg0] >= 0;
   };
   const int vstride = a.kind == MUSE_KV_RING ? a.capacity : a.page_tokens;
 
@@ -207,51 +239,56 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // register prefetch of one 32-key sub-chunk.  Row r = 4g + i of key tile kt
+  // Sub-chunks of 32 entries stream through PD register buffers: while one is
+  // processed, the next PD - 1 are in flight.  The loop is unrolled by PD so
+  // every buffer index is a compile-time constant (no register copies, whose
+  // waits would drain the loads in flight).  Row r = 4g + i of key tile kt
   // holds entry 8g + 4kt + i, so the eight entries a lane needs for P V are
   // contiguous in the head-dim-major V rows (one 16-byte load per fragment).
-  u32x4 kr[2][DS];
-  u32x4 vr[DB];
-  auto load = [&](int s0) {
-    const bool kok = tile_ok(s0 + 8 * (col >> 2));
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int64_t ka = kok ? kaddr(s0 + 8 * (col >> 2) + 4 * kt + (col & 3)) : 0;
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        kr[kt][ds] = kok ? *reinterpret_cast<const u32x4*>(kc + ka + 32 * ds + 8 * g4) : u32x4{0, 0, 0, 0};
-    }
-    const bool vok = tile_ok(s0 + 8 * g4);
-    const int64_t va = vok ? vaddr(s0 + 8 * g4) : 0;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-      vr[db] = vok ? *reinterpret_cast<const u32x4*>(vc + va + static_cast<int64_t>(16 * db + col) * vstride)
-                   : u32x4{0, 0, 0, 0};
-    // entries at or past the end may never have been written: zero them so
-    // that p = 0 cannot meet a non-finite value
-    const int nv = hr.end - (s0 + 8 * g4);
-    if (vok && nv < 8) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd)
-          vr[db][wd] = 2 * wd >= nv ? 0u : (2 * wd + 1 >= nv ? (vr[db][wd] & 0xffffu) : vr[db][wd]);
-    }
+  constexpr int PD = kDecodeDepth;
+  struct Buf {
+    u32x4 k[2][DS];
+    u32x4 v[DB];
+    bool kok, vok;
   };
-
-  const int nsub = (c1 - c0 + 31) / 32;
-  if (w < nsub) load(c0 + 32 * w);
-  for (int sc = w; sc < nsub; sc += NW) {
-    const int s0 = c0 + 32 * sc;
-    u32x4 kcur[2][DS];
-    u32x4 vcur[DB];
+  Buf bufs[PD];
+  // Loads are issued unconditionally (an absent tile reads the start of the
+  // cache instead) and zeroed at use: predicated loads would leave the
+  // number of loads in flight unknown and force full waits.
+  auto load = [&](Buf& B, int s0) {
+    const int ik = s0 + 8 * (col >> 2);
+    B.kok = tile_ok(ik);
+    // rows ik + (col & 3) and ik + 4 + (col & 3) share one page (pages hold
+    // a multiple of 16 positions and ik is a multiple of 8)
+    const int64_t ka = B.kok ? kaddr(ik + (col & 3)) : 0;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) kcur[kt][ds] = kr[kt][ds];
+      for (int ds = 0; ds < DS; ++ds)
+        B.k[kt][ds] = *reinterpret_cast<const u32x4*>(kc + ka + 4 * kt * D + 32 * ds + 8 * g4);
+    const int iv = s0 + 8 * g4;
+    B.vok = tile_ok(iv);
+    const int64_t va = B.vok ? vaddr(iv) : 0;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) vcur[db] = vr[db];
-    if (sc + NW < nsub) load(c0 + 32 * (sc + NW));
+    for (int db = 0; db < DB; ++db)
+      B.v[db] = *reinterpret_cast<const u32x4*>(vc + va + static_cast<int64_t>(16 * db + col) * vstride);
+  };
+
+  auto process = [&](Buf& B, int s0) {
+    // absent tiles read as zeros; V entries at or past the end may never have
+    // been written and are zeroed too, so p = 0 never meets a non-finite value
+    u32x4 kcur[2][DS];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) kcur[kt][ds] = B.kok ? B.k[kt][ds] : u32x4{0, 0, 0, 0};
+    u32x4 vcur[DB];
+    const int nv = B.vok ? hr.end - (s0 + 8 * g4) : 0;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd)
+        vcur[db][wd] = 2 * wd >= nv ? 0u : (2 * wd + 1 >= nv ? (B.v[db][wd] & 0xffffu) : B.v[db][wd]);
 
     // S^T tiles: entries s0 + 8*g4 + 4*kt + i, head col
     float s[2][4];
@@ -296,6 +333,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       const bf16x8 vf = __builtin_bit_cast(bf16x8, vcur[db]);
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[db], 0, 0, 0);
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[db], 0, 0, 0);
+    }
+  };
+
+  // this wave's sub-chunks: w, w + NW, w + 2 NW, ...
+  const int nsub = (c1 - c0 + 31) / 32;
+  const int nmine = nsub > w ? (nsub - w + NW - 1) / NW : 0;
+  auto sub_s0 = [&](int j) { return c0 + 32 * (w + j * NW); };
+#pragma unroll
+  for (int j = 0; j < PD - 1; ++j)
+    if (j < nmine) load(bufs[j], sub_s0(j));
+  for (int j0 = 0; j0 < nmine; j0 += PD) {
+#pragma unroll
+    for (int u = 0; u < PD; ++u) {
+      const int j = j0 + u;
+      if (j < nmine) {
+        if (j + PD - 1 < nmine) load(bufs[(u + PD - 1) % PD], sub_s0(j + PD - 1));
+        process(bufs[u], sub_s0(j));
+      }
     }
   }
   lsum += __shfl_xor(lsum, 16, kWave);

@@ -8,6 +8,8 @@ namespace muse {
 
 // Keys per LDS tile of the prefill kernel.
 constexpr int kKeyTile = 64;
+// Cached positions per split of a paged decode cache.
+constexpr int kPagedChunk = 2048;
 
 // ---------------------------------------------------------------------------
 // Prefill tile image: one 64-key tile of one (sequence, KV head), written by
