@@ -28,9 +28,11 @@
 //     a wave skips edge tiles it cannot see.  Between the edges the loop is
 //     software-pipelined: the logits of the next half-tile go to the matrix
 //     cores while the exponentials of the current one run on the vector ALUs.
-//   * Launch order: heaviest query blocks first (causal work grows with the
-//     block index), and groups of 8 consecutive query blocks of one KV head
-//     land on one XCD so they share K/V tiles in that XCD's L2.
+//   * Launch order.  Global layers: heaviest query blocks first (causal work
+//     grows with the block index), and groups of 8 consecutive query blocks
+//     of one KV head land on one XCD so they share K/V tiles in its L2.
+//     Local layers (uniform work): each XCD walks one contiguous range of
+//     query blocks, so the 2048-key window's tiles stay in that XCD's L2.
 #include <type_traits>
 
 #include "kernels.h"
@@ -70,21 +72,34 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   __shared__ u32x4 smem[NBUF][TL::CHUNKS];
 
   // ---- workgroup -> (sequence, KV head, query block) ----
-  const int nblk = gridDim.x;
+  // Workgroups are dealt to the 8 XCDs round-robin (blockIdx mod 8), and each
+  // XCD runs its share in increasing blockIdx order.
+  const int nblk = gridDim.x;  // n_qblocks_pad * batch_heads, a multiple of 8
   const int raw = blockIdx.x;
   constexpr int QC = kQBlockGroup;
-  int L = raw;
-  const int full_groups = (nblk / (8 * QC)) * (8 * QC);
-  if (raw < full_groups) {
-    const int slot = raw >> 3, xcd = raw & 7;
-    L = (slot / QC) * (8 * QC) + xcd * QC + (slot % QC);
+  int bh, qb;
+  if (a.W > 0) {
+    // local layer: uniform work per block; each XCD takes one contiguous
+    // range of query blocks in order, so the window's tiles stay in its L2
+    const int lx = (raw & 7) * (nblk >> 3) + (raw >> 3);
+    bh = lx / a.n_qblocks_pad;
+    qb = lx - bh * a.n_qblocks_pad;
+  } else {
+    // global layer: heaviest (latest) query blocks first; groups of QC
+    // consecutive blocks of one KV head land on one XCD
+    int L = raw;
+    const int full_groups = (nblk / (8 * QC)) * (8 * QC);
+    if (raw < full_groups) {
+      const int slot = raw >> 3, xcd = raw & 7;
+      L = (slot / QC) * (8 * QC) + xcd * QC + (slot % QC);
+    }
+    const int per = a.batch_heads * QC;
+    const int qbc = L / per;
+    const int rem = L - qbc * per;
+    bh = rem / QC;
+    const int qi = rem - bh * QC;
+    qb = a.n_qblocks_pad - 1 - (qbc * QC + qi);
   }
-  const int per = a.batch_heads * QC;
-  const int qbc = L / per;
-  const int rem = L - qbc * per;
-  const int bh = rem / QC;
-  const int qi = rem - bh * QC;
-  const int qb = a.n_qblocks_pad - 1 - (qbc * QC + qi);
   if (qb >= a.n_qblocks) return;  // padding block: exits before any barrier
   const int b = bh / a.Hkv;
   const int hk = bh - b * a.Hkv;
