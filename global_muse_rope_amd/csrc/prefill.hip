@@ -294,9 +294,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < QD; ++j) fq[j] = frag(hb, j);
   };
-  auto half_step = [&](const Half& cur, const Half& nxt, f32x16* s_out, bf16x8 (*p_in)[2], const f32x16* s_in,
+  auto half_step = [&](const Half& cur, const Half& nxt, f32x16* s_out, bf16x8 (*p_in)[2], f32x16* s_in,
                        bf16x8 (*p_out)[2]) {
     constexpr int NE = 16;  // logits per lane per row block
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(s_in[mb]));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -325,13 +327,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       for (int e = (j * NE / NI) & ~1; e < (((j + 1) * NE / NI) & ~1); e += 2) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          // The empty asm statements pin the exponentials to this slot.  On
-          // the input side they stop the edge-tile mask from being folded into
-          // exp2 (exp2(-inf) = 0) and the exponentials from being hoisted; on
-          // the output side they stop machine sinking from moving them into
-          // the next block, past the matrix-core work they hide under.
-          float x0 = s_in[mb][e], x1 = s_in[mb][e + 1];
-          asm volatile("" : "+v"(x0), "+v"(x1));
+          // The empty asm statements pin the exponentials to this slot: the
+          // one on the whole S_in at the top of the half-step stops the
+          // edge-tile mask from being folded into exp2 (exp2(-inf) = 0) and
+          // the exponentials from being hoisted; the one on each output stops
+          // machine sinking from moving them into the next block, past the
+          // matrix-core work they hide under.
+          const float x0 = s_in[mb][e], x1 = s_in[mb][e + 1];
           bf16x2 pr;
           pr[0] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(x0));
           pr[1] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(x1));
