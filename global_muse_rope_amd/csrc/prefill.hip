@@ -71,45 +71,67 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   constexpr int NBUF = 4;
   __shared__ u32x4 smem[NBUF][TL::CHUNKS];
 
-  // ---- workgroup -> (sequence, KV head, query block) ----
-  // Workgroups are dealt to the 8 XCDs round-robin (blockIdx mod 8), and each
-  // XCD runs its share in increasing blockIdx order.
-  const int nblk = gridDim.x;  // n_qblocks_pad * batch_heads, a multiple of 8
-  const int raw = blockIdx.x;
-  constexpr int QC = kQBlockGroup;
-  int bh, qb;
-  if (a.W > 0) {
-    // local layer: uniform work per block; each XCD takes one contiguous
-    // range of query blocks in order, so the window's tiles stay in its L2
-    const int lx = (raw & 7) * (nblk >> 3) + (raw >> 3);
-    bh = lx / a.n_qblocks_pad;
-    qb = lx - bh * a.n_qblocks_pad;
-  } else {
-    // global layer: heaviest (latest) query blocks first; groups of QC
-    // consecutive blocks of one KV head land on one XCD
-    int L = raw;
-    const int full_groups = (nblk / (8 * QC)) * (8 * QC);
-    if (raw < full_groups) {
-      const int slot = raw >> 3, xcd = raw & 7;
-      L = (slot / QC) * (8 * QC) + xcd * QC + (slot % QC);
-    }
-    const int per = a.batch_heads * QC;
-    const int qbc = L / per;
-    const int rem = L - qbc * per;
-    bh = rem / QC;
-    const int qi = rem - bh * QC;
-    qb = a.n_qblocks_pad - 1 - (qbc * QC + qi);
-  }
-  if (qb >= a.n_qblocks) return;  // padding block: exits before any barrier
-  const int b = bh / a.Hkv;
-  const int hk = bh - b * a.Hkv;
-  const int t0 = qb * C::BQ;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
+
+  // ---- workgroups -> (sequence, KV head, query block) ----
+  // Workgroups are dealt to the 8 XCDs round-robin (blockIdx mod 8), and each
+  // XCD runs its share in increasing blockIdx order.
+  //   Local layer (uniform work per block): a persistent grid; XCD x owns one
+  //   contiguous range of logical blocks and its K workgroups walk it with
+  //   stride K, so the XCD works on K consecutive query blocks at a time and
+  //   the window's tiles stay in its L2.  Each workgroup warms the L2 with the
+  //   next block's queries while it computes the current one.
+  //   Global layer: one block per workgroup, heaviest (latest) query blocks
+  //   first, groups of QC consecutive blocks of one KV head on one XCD.
+  const int nlog = a.n_qblocks_pad * a.batch_heads;  // a multiple of 8
+  constexpr int QC = kQBlockGroup;
+  // (head width 64 already fits two workgroups per CU, which overlap each
+  // other's block starts; the persistent loop's registers would cost that)
+  const bool persistent = D == 128 && a.W > 0;
+  int lx_first, lx_end, lx_step;
+  if (persistent) {
+    const int per = nlog >> 3;
+    const int xcd = blockIdx.x & 7;
+    lx_first = xcd * per + (blockIdx.x >> 3);
+    lx_end = (xcd + 1) * per;
+    lx_step = gridDim.x >> 3;
+  } else {
+    lx_first = blockIdx.x;
+    lx_end = blockIdx.x + 1;
+    lx_step = 1;
+  }
+  auto block_of = [&](int lx, int& bh, int& qb) {
+    if (persistent) {
+      bh = lx / a.n_qblocks_pad;
+      qb = lx - bh * a.n_qblocks_pad;
+    } else {
+      int L = lx;
+      const int full_groups = (nlog / (8 * QC)) * (8 * QC);
+      if (lx < full_groups) {
+        const int slot = lx >> 3, xcd = lx & 7;
+        L = (slot / QC) * (8 * QC) + xcd * QC + (slot % QC);
+      }
+      const int per = a.batch_heads * QC;
+      const int qbc = L / per;
+      const int rem = L - qbc * per;
+      bh = rem / QC;
+      const int qi = rem - bh * QC;
+      qb = a.n_qblocks_pad - 1 - (qbc * QC + qi);
+    }
+  };
+
+  for (int lx = lx_first; lx < lx_end; lx += lx_step) {
+  int bh, qb;
+  block_of(lx, bh, qb);
+  if (qb >= a.n_qblocks) continue;  // padding block (uniform over the workgroup)
+  const int b = bh / a.Hkv;
+  const int hk = bh - b * a.Hkv;
+  const int t0 = qb * C::BQ;
 
   int tq[MB];  // token of this lane's query column in each row block
 #pragma unroll
@@ -220,6 +242,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // (vmcnt): LDS fragment reads of the next half-tile, which target tiles
   // that stay resident, remain in flight across it.  The empty asm statements
   // keep the compiler from moving memory accesses across the barrier.
+
   auto advance = [&](int tile) {
     const int rel = tile - tile_lo;
     asm volatile("" ::: "memory");
@@ -482,6 +505,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
                                 d0) = ow;
     }
   }
+  // the staging area is the tile buffers: every wave is done reading it
+  // before the next block's tile copies land there
+  __syncthreads();
+  }  // query blocks of this workgroup
 }
 
 // ---------------------------------------------------------------------------
@@ -510,12 +537,36 @@ struct LaunchShape {
   static constexpr int MB = D == 128 ? MUSE_PREFILL_MB_D128 : MUSE_PREFILL_MB_D64;
 };
 
+// Resident workgroups of one kernel on the current device: CUs times the
+// occupancy the kernel's registers and LDS allow (cached per device).
+template <typename K>
+int resident_workgroups(K kernel, int threads) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  if (cache[dev] > 0) return cache[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+  cache[dev] = cus * per_cu;
+  return cache[dev];
+}
+
 template <int D, int G>
 hipError_t launch_dg(const PrefillArgs& a, hipStream_t st) {
   constexpr int NW = LaunchShape<D>::NW, MB = LaunchShape<D>::MB;
   using C = PrefillCfg<D, G, NW, MB>;
-  const unsigned grid = static_cast<unsigned>(a.n_qblocks_pad) * static_cast<unsigned>(a.batch_heads);
-  hipLaunchKernelGGL((prefill_kernel<D, G, NW, MB>), dim3(grid), dim3(C::THREADS), 0, st, a);
+  auto kernel = prefill_kernel<D, G, NW, MB>;
+  const int nlog = a.n_qblocks_pad * a.batch_heads;  // a multiple of 8
+  int grid = nlog;
+  if (D == 128 && a.W > 0) {
+    // local layers run a persistent grid of at most one wave of resident
+    // workgroups, a multiple of 8 so every XCD gets the same number
+    const int cap = resident_workgroups(kernel, C::THREADS) & ~7;
+    if (cap >= 8 && cap < nlog) grid = cap;
+  }
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
 }
 

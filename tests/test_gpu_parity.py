@@ -121,6 +121,29 @@ def test_prefill_batch_and_positions():
     check_prefill(layer, B, T, seed=3, positions=pos)
 
 
+def test_prefill_local_many_blocks_per_workgroup():
+    """A local layer with more query blocks than resident workgroups, so one
+    workgroup walks several blocks (and their padding) in turn; two
+    sequences, a ragged length and positions offset per sequence.  Rows are
+    sampled for the oracle (each row depends only on its own window)."""
+    layer = Layer(hq=32, hkv=2, d=128, window=512, theta=10000.0, scale=GLIMMER_SCALE)
+    B, T = 2, 6001
+    pos = np.stack([np.arange(T), np.arange(T) + 70000]).astype(np.int32)
+    bits = prefill_inputs_host(layer, B, T, seed=17)
+    y = run_prefill(layer, bits, positions=pos)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(0, 20), np.arange(500, 530), np.arange(T - 40, T),
+                                     rng.integers(0, T, 60)]))
+    worst = 0.0
+    for b in range(B):
+        ref = oracle.prefill(_f(bits["q"])[b][rows], _f(bits["k"])[b][: rows.max() + 1],
+                             _f(bits["v"])[b][: rows.max() + 1], _f(bits["g"])[b][rows], layer,
+                             positions=pos[b], rows=rows)
+        worst = max(worst, max_err(y[b][rows], ref))
+    print(f"local many-blocks B={B} T={T} max_abs_err={worst:.3e}", flush=True)
+    assert worst <= TOL
+
+
 def test_prefill_strided_views():
     """q, k, v, gate as views of one fused [B, T, (Hq + 2 Hkv + Hq) * D] tensor;
     output written into a strided view."""
