@@ -267,6 +267,15 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t n_tiles = prefill_tiles(T);
+  {
+    // launch-size limits, checked before any launch
+    const int bq = prefill_rows_per_block(D, Hq / Hkv) / (Hq / Hkv);
+    const int qgroup = prefill_qblock_group();
+    const int64_t nq = (static_cast<int64_t>(T) + bq - 1) / bq;
+    const int64_t nq_pad = ((nq + qgroup - 1) / qgroup) * qgroup;
+    if (nq_pad * B * Hkv > 0x7fffffffLL || n_tiles * Hkv > 0x7fffffffLL || B > 65535)
+      return fail(MUSE_ERR_UNSUPPORTED, "problem too large for one launch");
+  }
   const PrefillWs wl = prefill_ws_layout(params, B, T);
   u32x4* tiles = static_cast<u32x4*>(workspace);
   float2* rope = wl.rope_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + wl.tile_bytes) : nullptr;
@@ -327,8 +336,6 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   pa.qk_eps = params->qk_norm_eps;
   pa.out_norm = params->out_norm;
   pa.out_eps = params->out_norm_eps;
-  if (static_cast<int64_t>(pa.n_qblocks_pad) * pa.batch_heads > 0x7fffffffLL)
-    return fail(MUSE_ERR_UNSUPPORTED, "problem too large for one launch");
   if (g_prof_start) {
     e = hipEventRecord(g_prof_start, st);
     if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));

@@ -82,44 +82,68 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
   constexpr int BK = kKeyTile;
   constexpr int RUN = D / 8;  // elements per thread in each half of the head
   __shared__ uint16_t vs[BK][D + 8];
-  const int tile = blockIdx.x;
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
+  // KV heads vary fastest over the grid: the workgroups of one tile's heads
+  // run together and read each token's row of all heads in one pass
+  const int tile = blockIdx.x / a.Hkv;
+  const int hk = blockIdx.x - tile * a.Hkv;
+  const int b = blockIdx.y;
   const int tid = threadIdx.x;
   const int r = tid >> 2;          // key within the tile
   const int qq = tid & 3;          // quarter of each half of the head
   const int tok = tile * BK + r;
-  const bool valid = tok < a.T;
   const int64_t bh = static_cast<int64_t>(b) * a.Hkv + hk;
+
+  // All loads of the tile (raw keys, values and RoPE rows) are issued
+  // before the first use so their latencies overlap.  Rows past the end of
+  // the sequence repeat the last row: they are never visible to a query (the
+  // attention kernel masks them before the exponential), and finite values
+  // keep p = 0 from meeting a non-finite V.
+  const int tl = min(tok, a.T - 1);
+  const uint16_t* kp = a.k + b * a.k_sb + static_cast<int64_t>(tl) * a.k_st + static_cast<int64_t>(hk) * D;
+  const uint16_t* vp = a.v + b * a.v_sb + static_cast<int64_t>(tl) * a.v_st + static_cast<int64_t>(hk) * D;
+  u32x4 kw[2][RUN / 8], vw[2][RUN / 8];
+#pragma unroll
+  for (int c = 0; c < RUN / 8; ++c)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      kw[hf][c] = *reinterpret_cast<const u32x4*>(kp + hf * (D / 2) + qq * RUN + c * 8);
+      vw[hf][c] = *reinterpret_cast<const u32x4*>(vp + hf * (D / 2) + qq * RUN + c * 8);
+    }
+  float2 cs[RUN];
+  const bool use_rope = a.rope != nullptr;
+  if (use_rope) {
+    const float2* rt = a.rope + ((a.rope_batched ? static_cast<int64_t>(b) * a.T : 0) + tl) * (D / 2) + qq * RUN;
+#pragma unroll
+    for (int e = 0; e < RUN; ++e) cs[e] = rt[e];
+  }
+
+  // ---- values: stage the tile for the transposed write ----
+#pragma unroll
+  for (int c = 0; c < RUN / 8; ++c)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      *reinterpret_cast<u32x2*>(&vs[r][hf * (D / 2) + qq * RUN + c * 8]) = u32x2{vw[hf][c][0], vw[hf][c][1]};
+      *reinterpret_cast<u32x2*>(&vs[r][hf * (D / 2) + qq * RUN + c * 8 + 4]) = u32x2{vw[hf][c][2], vw[hf][c][3]};
+    }
 
   // ---- keys: norm + RoPE, fp16 out ----
   float lo[RUN], hi[RUN];
-  const uint16_t* kp = a.k + b * a.k_sb + static_cast<int64_t>(tok) * a.k_st + static_cast<int64_t>(hk) * D;
 #pragma unroll
   for (int c = 0; c < RUN / 8; ++c) {
-    u32x4 w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
-    if (valid) {
-      w0 = *reinterpret_cast<const u32x4*>(kp + qq * RUN + c * 8);
-      w1 = *reinterpret_cast<const u32x4*>(kp + D / 2 + qq * RUN + c * 8);
-    }
-    unpack_bf16x8(w0, lo + c * 8);
-    unpack_bf16x8(w1, hi + c * 8);
+    unpack_bf16x8(kw[0][c], lo + c * 8);
+    unpack_bf16x8(kw[1][c], hi + c * 8);
   }
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < RUN; ++e) ss += lo[e] * lo[e] + hi[e] * hi[e];
   ss = group_sum<4>(ss);
   const float rs = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
-  const float2* rt = nullptr;
-  if (a.rope && valid)
-    rt = a.rope + ((a.rope_batched ? static_cast<int64_t>(b) * a.T : 0) + tok) * (D / 2) + qq * RUN;
 #pragma unroll
   for (int e = 0; e < RUN; ++e) {
     float x0 = lo[e] * rs, x1 = hi[e] * rs;
-    if (rt) {
-      const float2 cs = rt[e];
-      const float y0 = x0 * cs.x - x1 * cs.y;
-      const float y1 = x1 * cs.x + x0 * cs.y;
+    if (use_rope) {
+      const float y0 = x0 * cs[e].x - x1 * cs[e].y;
+      const float y1 = x1 * cs[e].x + x0 * cs[e].y;
       x0 = y0;
       x1 = y1;
     }
@@ -143,20 +167,6 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     kdst[c1] = w1;
   }
 
-  // ---- values: stage the tile, write it transposed ----
-  const uint16_t* vp = a.v + b * a.v_sb + static_cast<int64_t>(tok) * a.v_st + static_cast<int64_t>(hk) * D;
-#pragma unroll
-  for (int c = 0; c < RUN / 8; ++c) {
-    u32x4 w0 = {0, 0, 0, 0}, w1 = {0, 0, 0, 0};
-    if (valid) {
-      w0 = *reinterpret_cast<const u32x4*>(vp + qq * RUN + c * 8);
-      w1 = *reinterpret_cast<const u32x4*>(vp + D / 2 + qq * RUN + c * 8);
-    }
-    *reinterpret_cast<u32x2*>(&vs[r][qq * RUN + c * 8]) = u32x2{w0[0], w0[1]};
-    *reinterpret_cast<u32x2*>(&vs[r][qq * RUN + c * 8 + 4]) = u32x2{w0[2], w0[3]};
-    *reinterpret_cast<u32x2*>(&vs[r][D / 2 + qq * RUN + c * 8]) = u32x2{w1[0], w1[1]};
-    *reinterpret_cast<u32x2*>(&vs[r][D / 2 + qq * RUN + c * 8 + 4]) = u32x2{w1[2], w1[3]};
-  }
   __syncthreads();
   u32x4* vdst = tdst + TL::KCHUNKS;
   constexpr int CHUNKS = D * BK / 8;  // 16-byte chunks of the transposed tile
@@ -208,7 +218,7 @@ hipError_t launch_rope_table(int d, const RopeTableArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_kv_prep(int d, int B, const KvPrepArgs& a, hipStream_t st) {
-  dim3 grid(a.n_tiles, a.Hkv, B);
+  dim3 grid(static_cast<unsigned>(a.n_tiles) * static_cast<unsigned>(a.Hkv), B);
   if (d == 64) hipLaunchKernelGGL((kv_prep_kernel<64>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((kv_prep_kernel<128>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
