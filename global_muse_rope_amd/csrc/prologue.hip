@@ -166,6 +166,9 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     kdst[c0] = w0;
     kdst[c1] = w1;
   }
+  // the pad chunks are written too (zeros), so every line of the tile image
+  // is written whole
+  if (qq == 0) kdst[D / 8] = u32x4{0, 0, 0, 0};
 
   __syncthreads();
   u32x4* vdst = tdst + TL::KCHUNKS;
@@ -184,6 +187,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = static_cast<uint32_t>(e[2 * i]) | (static_cast<uint32_t>(e[2 * i + 1]) << 16);
     vdst[d * TL::VROW + pc] = w;
+    if (pc == 0) vdst[d * TL::VROW + BK / 8] = u32x4{0, 0, 0, 0};
   }
 }
 
