@@ -53,3 +53,4 @@ from .attention import (  # noqa: F401
     prefill,
     decode_one,
 )
+from . import fp8  # noqa: F401  (E4M3 cache codes)
