@@ -56,28 +56,46 @@ class KvCache:
     ring:  k [B, Hkv, W, D], v [B, Hkv, D, W]
     paged: k [num_pages, Hkv, page_tokens, D], v [num_pages, Hkv, D, page_tokens],
            block_table int32 [B, max_pages_per_seq]
+    Entries are bf16, or E4M3 codes (uint8 or float8_e4m3fn tensors) with
+    fp32 scales k_scale, v_scale: [num_pages, Hkv] (paged) or [B, Hkv] (ring).
     """
     kind: int
     k: "object"
     v: "object"
     block_table: Optional["object"] = None
     page_tokens: int = 0
+    k_scale: Optional["object"] = None
+    v_scale: Optional["object"] = None
 
     @classmethod
-    def ring(cls, k, v):
-        return cls(MUSE_KV_RING, k, v)
+    def ring(cls, k, v, k_scale=None, v_scale=None):
+        return cls(MUSE_KV_RING, k, v, None, 0, k_scale, v_scale)
 
     @classmethod
-    def paged(cls, k, v, block_table, page_tokens):
-        return cls(MUSE_KV_PAGED, k, v, block_table, page_tokens)
+    def paged(cls, k, v, block_table, page_tokens, k_scale=None, v_scale=None):
+        return cls(MUSE_KV_PAGED, k, v, block_table, page_tokens, k_scale, v_scale)
+
+    @property
+    def dtype(self) -> int:
+        torch = _torch()
+        if self.k.dtype == torch.bfloat16:
+            return _capi.MUSE_DTYPE_BF16
+        if self.k.dtype in (torch.uint8, getattr(torch, "float8_e4m3fn", None)):
+            return _capi.MUSE_DTYPE_FP8_E4M3
+        raise TypeError(f"cache entries must be bfloat16 or E4M3 codes, got {self.k.dtype}")
 
     def c(self) -> _capi.MuseKvCache:
+        fp8 = self.dtype == _capi.MUSE_DTYPE_FP8_E4M3
+        if fp8 and (self.k_scale is None or self.v_scale is None):
+            raise ValueError("an E4M3 cache needs k_scale and v_scale")
+        ks = self.k_scale.data_ptr() if fp8 else None
+        vs = self.v_scale.data_ptr() if fp8 else None
         if self.kind == MUSE_KV_RING:
             return _capi.MuseKvCache(MUSE_KV_RING, int(self.k.shape[2]), self.k.data_ptr(), self.v.data_ptr(),
-                                     None, 0, 0, 0)
+                                     None, 0, 0, 0, self.dtype, ks, vs)
         return _capi.MuseKvCache(MUSE_KV_PAGED, 0, self.k.data_ptr(), self.v.data_ptr(),
                                  self.block_table.data_ptr(), int(self.block_table.shape[1]),
-                                 int(self.page_tokens), int(self.k.shape[0]))
+                                 int(self.page_tokens), int(self.k.shape[0]), self.dtype, ks, vs)
 
 
 def _torch():

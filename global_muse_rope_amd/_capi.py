@@ -20,6 +20,7 @@ STATUS_NAMES = {0: "MUSE_OK", 1: "MUSE_ERR_INVALID_ARG", 2: "MUSE_ERR_UNSUPPORTE
 MUSE_DTYPE_BF16 = 0
 MUSE_DTYPE_F16 = 1
 MUSE_DTYPE_F32 = 2
+MUSE_DTYPE_FP8_E4M3 = 3
 MUSE_KV_RING = 0
 MUSE_KV_PAGED = 1
 
@@ -48,6 +49,9 @@ class MuseKvCache(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("page_tokens", ctypes.c_int32),
         ("num_pages", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 

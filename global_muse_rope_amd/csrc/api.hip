@@ -153,6 +153,11 @@ int32_t check_cache(const muse_attn_params* p, int32_t B, int32_t max_kv_len, co
   } else {
     return fail(MUSE_ERR_INVALID_ARG, "unknown cache kind %d", c->kind);
   }
+  if (c->dtype == MUSE_DTYPE_FP8_E4M3) {
+    if (!c->k_scale || !c->v_scale) return fail(MUSE_ERR_INVALID_ARG, "an E4M3 cache needs k_scale and v_scale");
+  } else if (c->dtype != MUSE_DTYPE_BF16) {
+    return fail(MUSE_ERR_UNSUPPORTED, "cache dtype %d (bf16 or E4M3 codes only)", c->dtype);
+  }
   (void)B;
   return MUSE_OK;
 }
@@ -161,7 +166,7 @@ int32_t check_cache(const muse_attn_params* p, int32_t B, int32_t max_kv_len, co
 
 extern "C" {
 
-int32_t muse_version(void) { return 100; }
+int32_t muse_version(void) { return 101; }
 
 const char* muse_last_error(void) { return g_err; }
 
@@ -388,6 +393,9 @@ int32_t muse_attn_decode(const muse_attn_params* params, int32_t B, const void* 
   a.out = static_cast<uint16_t*>(out);
   a.kc = static_cast<uint16_t*>(cache->k);
   a.vc = static_cast<uint16_t*>(cache->v);
+  a.fp8 = cache->dtype == MUSE_DTYPE_FP8_E4M3 ? 1 : 0;
+  a.k_scale = cache->k_scale;
+  a.v_scale = cache->v_scale;
   a.block_table = cache->block_table;
   a.kind = cache->kind;
   a.capacity = cache->capacity;

@@ -62,6 +62,41 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4& w, float* f) {
   }
 }
 
+// OCP E4M3 code of x (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+// subnormals, no infinities; 0x7F is NaN): round to nearest, ties to an even
+// mantissa, finite magnitudes beyond 448 saturate to 448, NaN gives 0x7F.
+__device__ __forceinline__ uint8_t e4m3_encode(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float ax = fabsf(x);
+  if (ax != ax) return 0x7F;
+  if (ax >= 448.0f) return static_cast<uint8_t>(sign | 0x7Eu);
+  if (ax < 0.015625f) {                     // below 2^-6: multiples of 2^-9
+    const int m = static_cast<int>(rintf(ax * 512.0f));  // exact scaling, ties to even; 8 = 2^-6
+    return static_cast<uint8_t>(sign | static_cast<uint32_t>(m));
+  }
+  int e = static_cast<int>((u >> 23) & 0xFFu) - 127;  // -6 .. 8
+  uint32_t keep = (u >> 20) & 0x7u;
+  const uint32_t rem = u & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ++keep;
+  if (keep == 8u) {
+    keep = 0u;
+    ++e;
+  }
+  return static_cast<uint8_t>(sign | (static_cast<uint32_t>(e + 7) << 3) | keep);
+}
+
+// Eight E4M3 codes (one per byte, lowest first) to bf16, exactly (every
+// E4M3 value has a bf16 representation).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 w) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true));
+  return r;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);

@@ -22,6 +22,8 @@
 // with bf16 operands, q_hat and p are split into hi + lo bf16 parts whose two
 // products accumulate into the same fp32 registers (the MFMA work this
 // doubles is far below the HBM roofline that bounds decode).
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace muse {
@@ -92,6 +94,20 @@ __global__ __launch_bounds__(256) void decode_append_kernel(DecodeArgs a, int hq
     vbase = (page * a.Hkv + h) * D * a.page_tokens + rr;
     vstride = a.page_tokens;
   }
+  if (a.fp8) {
+    // E4M3 codes of x / scale, the division in IEEE fp32 (per-(page, head)
+    // or per-(sequence, head) scales)
+    const int64_t si = a.kind == MUSE_KV_RING ? static_cast<int64_t>(b) * a.Hkv + h
+                                              : (kbase / D / a.page_tokens);  // page * Hkv + h
+    const float ks = a.k_scale[si], vs = a.v_scale[si];
+    uint8_t* kc8 = reinterpret_cast<uint8_t*>(a.kc);
+    uint8_t* vc8 = reinterpret_cast<uint8_t*>(a.vc);
+    kc8[kbase + j] = e4m3_encode(x0 / ks);
+    kc8[kbase + j + D / 2] = e4m3_encode(x1 / ks);
+    vc8[vbase + static_cast<int64_t>(j) * vstride] = e4m3_encode(bf16_bits_to_f32(vp[j]) / vs);
+    vc8[vbase + static_cast<int64_t>(j + D / 2) * vstride] = e4m3_encode(bf16_bits_to_f32(vp[j + D / 2]) / vs);
+    return;
+  }
   a.kc[kbase + j] = f32_to_bf16_bits(x0);
   a.kc[kbase + j + D / 2] = f32_to_bf16_bits(x1);
   a.vc[vbase + static_cast<int64_t>(j) * vstride] = vp[j];
@@ -148,7 +164,7 @@ constexpr int kMaxChunkPages = kPagedChunk / 16 + 2;
 #endif
 constexpr int kDecodeDepth = MUSE_DECODE_DEPTH;
 
-template <int D, int G>
+template <int D, int G, bool FP8>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   constexpr int NW = 4;
   constexpr int DS = D / 32;  // dim steps of QK^T
@@ -246,12 +262,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // holds entry 8g + 4kt + i, so the eight entries a lane needs for P V are
   // contiguous in the head-dim-major V rows (one 16-byte load per fragment).
   constexpr int PD = kDecodeDepth;
+  // one fragment: 8 entries of 16 bits (bf16) or 8 bits (E4M3 codes)
+  using Frag = typename std::conditional<FP8, u32x2, u32x4>::type;
   struct Buf {
-    u32x4 k[2][DS];
-    u32x4 v[DB];
+    Frag k[2][DS];
+    Frag v[DB];
     bool kok, vok;
+    float ks, vs;  // E4M3: scales of the page holding this lane's entries
   };
   Buf bufs[PD];
+  const uint8_t* kc8 = reinterpret_cast<const uint8_t*>(a.kc);
+  const uint8_t* vc8 = reinterpret_cast<const uint8_t*>(a.vc);
+  // ring caches: one scale per (sequence, KV head)
+  const float ring_ks = FP8 && a.kind == MUSE_KV_RING ? a.k_scale[bh] : 1.f;
+  const float ring_vs = FP8 && a.kind == MUSE_KV_RING ? a.v_scale[bh] : 1.f;
   // Loads are issued unconditionally (an absent tile reads the start of the
   // cache instead) and zeroed at use: predicated loads would leave the
   // number of loads in flight unknown and force full waits.
@@ -264,14 +288,34 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds)
-        B.k[kt][ds] = *reinterpret_cast<const u32x4*>(kc + ka + 4 * kt * D + 32 * ds + 8 * g4);
+      for (int ds = 0; ds < DS; ++ds) {
+        if constexpr (FP8)
+          B.k[kt][ds] = *reinterpret_cast<const u32x2*>(kc8 + ka + 4 * kt * D + 32 * ds + 8 * g4);
+        else
+          B.k[kt][ds] = *reinterpret_cast<const u32x4*>(kc + ka + 4 * kt * D + 32 * ds + 8 * g4);
+      }
     const int iv = s0 + 8 * g4;
     B.vok = tile_ok(iv);
     const int64_t va = B.vok ? vaddr(iv) : 0;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-      B.v[db] = *reinterpret_cast<const u32x4*>(vc + va + static_cast<int64_t>(16 * db + col) * vstride);
+    for (int db = 0; db < DB; ++db) {
+      if constexpr (FP8)
+        B.v[db] = *reinterpret_cast<const u32x2*>(vc8 + va + static_cast<int64_t>(16 * db + col) * vstride);
+      else
+        B.v[db] = *reinterpret_cast<const u32x4*>(vc + va + static_cast<int64_t>(16 * db + col) * vstride);
+    }
+    if constexpr (FP8) {
+      // this lane's logits and probabilities are entries iv .. iv + 7: one page
+      if (a.kind == MUSE_KV_RING) {
+        B.ks = ring_ks;
+        B.vs = ring_vs;
+      } else {
+        const int page = B.vok ? sm_page[iv / pt - pg0] : 0;
+        const int64_t si = static_cast<int64_t>(page) * a.Hkv + hk;
+        B.ks = a.k_scale[si];
+        B.vs = a.v_scale[si];
+      }
+    }
   };
 
   auto process = [&](Buf& B, int s0) {
@@ -281,14 +325,29 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) kcur[kt][ds] = B.kok ? B.k[kt][ds] : u32x4{0, 0, 0, 0};
+      for (int ds = 0; ds < DS; ++ds) {
+        u32x4 kw;
+        if constexpr (FP8)
+          kw = e4m3x8_to_bf16x8(B.k[kt][ds]);
+        else
+          kw = B.k[kt][ds];
+        kcur[kt][ds] = B.kok ? kw : u32x4{0, 0, 0, 0};
+      }
     u32x4 vcur[DB];
     const int nv = B.vok ? hr.end - (s0 + 8 * g4) : 0;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
+      u32x4 vw;
+      if constexpr (FP8)
+        vw = e4m3x8_to_bf16x8(B.v[db]);
+      else
+        vw = B.v[db];
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd)
-        vcur[db][wd] = 2 * wd >= nv ? 0u : (2 * wd + 1 >= nv ? (B.v[db][wd] & 0xffffu) : B.v[db][wd]);
+        vcur[db][wd] = 2 * wd >= nv ? 0u : (2 * wd + 1 >= nv ? (vw[wd] & 0xffffu) : vw[wd]);
+    }
+    const float kscale = FP8 ? B.ks : 1.f;
+    const float vscale = FP8 ? B.vs : 1.f;
 
     // S^T tiles: entries s0 + 8*g4 + 4*kt + i, head col
     float s[2][4];
@@ -305,7 +364,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int idx = s0 + 8 * g4 + 4 * kt + i;
-        s[kt][i] = hist_valid(hr, idx) ? acc[i] : NEG;
+        s[kt][i] = hist_valid(hr, idx) ? acc[i] * kscale : NEG;
         tmax = fmaxf(tmax, s[kt][i]);
       }
     }
@@ -322,9 +381,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
       for (int i = 0; i < 4; ++i) {
         const float p = s[kt][i] > NEG ? __builtin_amdgcn_exp2f(s[kt][i] - mnew) : 0.f;
         psum += p;
-        const bf16_t hi = static_cast<bf16_t>(p);
+        const float pv = p * vscale;  // the value scale of this lane's page
+        const bf16_t hi = static_cast<bf16_t>(pv);
         phi[4 * kt + i] = hi;
-        plo[4 * kt + i] = static_cast<bf16_t>(p - static_cast<float>(hi));
+        plo[4 * kt + i] = static_cast<bf16_t>(pv - static_cast<float>(hi));
       }
     lsum = lsum * alpha + psum;
 #pragma unroll
@@ -464,7 +524,10 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t st, hipEvent_t ev0, hipEve
   if (e != hipSuccess) return e;
   const unsigned items = static_cast<unsigned>(a.B) * a.Hkv * a.max_chunks;
   if (ev0 && (e = hipEventRecord(ev0, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(items), dim3(256), 0, st, a);
+  if (a.fp8)
+    hipLaunchKernelGGL((decode_split_kernel<D, G, true>), dim3(items), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_split_kernel<D, G, false>), dim3(items), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;

@@ -92,9 +92,13 @@ struct DecodeArgs {
   const uint16_t* gate;
   const int32_t* kv_len;
   uint16_t* out;
-  // cache
+  // cache (bf16 entries, or E4M3 codes when fp8 is set; element offsets
+  // are the same, the byte size differs)
   uint16_t* kc;
   uint16_t* vc;
+  int fp8;
+  const float* k_scale;  // fp8: [num_pages, Hkv] (paged) or [B, Hkv] (ring)
+  const float* v_scale;
   const int32_t* block_table;
   int kind, capacity, max_pages, page_tokens;
   int64_t num_pages;

@@ -51,7 +51,7 @@ typedef enum muse_status {
   MUSE_ERR_HIP = 4            /* a HIP runtime call or kernel launch failed */
 } muse_status;
 
-enum { MUSE_DTYPE_BF16 = 0, MUSE_DTYPE_F16 = 1, MUSE_DTYPE_F32 = 2 };
+enum { MUSE_DTYPE_BF16 = 0, MUSE_DTYPE_F16 = 1, MUSE_DTYPE_F32 = 2, MUSE_DTYPE_FP8_E4M3 = 3 };
 enum { MUSE_KV_RING = 0, MUSE_KV_PAGED = 1 };
 
 /* One attention layer's settings, named after the models' config keys
@@ -70,7 +70,7 @@ typedef struct muse_attn_params {
 } muse_attn_params;
 
 /* Caller-owned KV cache of one layer, holding keys AFTER norm and RoPE (the
- * cache is updated after those steps: deep dive, section 3.2 notes), bf16.
+ * cache is updated after those steps: deep dive, section 3.2 notes).
  *
  * MUSE_KV_RING (local layers): k is [B, Hkv, capacity, D]; v is stored
  *   transposed per head, [B, Hkv, D, capacity].  Position p lives in slot
@@ -81,18 +81,34 @@ typedef struct muse_attn_params {
  *   [num_pages, Hkv, page_tokens, D]; v is [num_pages, Hkv, D, page_tokens].
  *   Position p of sequence b lives in page block_table[b * max_pages_per_seq
  *   + p / page_tokens], row p mod page_tokens.  With D = 64 and
- *   page_tokens = 32 each (page, head) slice of K (or V) is 4 KiB.
+ *   page_tokens = 32 each (page, head) slice of K (or V) is 4 KiB in bf16.
  * V is head-dim-major inside a page (and inside a ring head) so that both
- * contractions read contiguous runs along their reduction axis. */
+ * contractions read contiguous runs along their reduction axis.
+ *
+ * Element type (dtype):
+ *   MUSE_DTYPE_BF16: entries are bf16; k_scale and v_scale are ignored.
+ *   MUSE_DTYPE_FP8_E4M3: entries are OCP E4M3 codes (one byte: sign, 4
+ *     exponent bits with bias 7, 3 mantissa bits, subnormals, 0x7F/0xFF NaN,
+ *     largest magnitude 448).  A stored value x is the code of x / scale,
+ *     the division in fp32, rounded to nearest with ties to an even mantissa
+ *     and saturated to +-448; it reads back as value(code) * scale.  The
+ *     scales are fp32 device arrays the caller owns and sets: k_scale and
+ *     v_scale are [num_pages, Hkv] for PAGED (one per page and KV head) and
+ *     [B, Hkv] for RING (one per sequence and KV head).  The pages size an
+ *     FP8 cache and leave scale factors out (deep dive, section 7.2); this
+ *     convention is the library's own. */
 typedef struct muse_kv_cache {
   int32_t kind;                /* MUSE_KV_RING or MUSE_KV_PAGED */
   int32_t capacity;            /* RING: entries per (sequence, head); must equal W */
-  void* k;                     /* device, bf16 */
-  void* v;                     /* device, bf16 */
+  void* k;                     /* device, dtype */
+  void* v;                     /* device, dtype */
   const int32_t* block_table;  /* PAGED: device int32 [B, max_pages_per_seq] */
   int32_t max_pages_per_seq;   /* PAGED: row length of block_table */
   int32_t page_tokens;         /* PAGED: positions per page, a multiple of 16 */
   int64_t num_pages;           /* PAGED: pages in the pool (block_table entries must be < this) */
+  int32_t dtype;               /* MUSE_DTYPE_BF16 (0) or MUSE_DTYPE_FP8_E4M3 */
+  const float* k_scale;        /* FP8 only: device fp32, see above */
+  const float* v_scale;        /* FP8 only: device fp32, see above */
 } muse_kv_cache;
 
 /* muse_rope_qknorm: the layer's prologue on its own (deep dive, section 3.2

@@ -39,12 +39,36 @@ def test_library_exports_every_declared_symbol():
         assert name in capi.SIGNATURES, name
 
 
-def test_struct_layouts_match_header():
+def test_struct_layouts_match_header(tmp_path):
+    """Sizes and field offsets of the ctypes mirrors equal what a C compiler
+    makes of the header."""
+    import shutil
+    import subprocess
     capi, _ = _lib()
-    assert ctypes.sizeof(capi.MuseAttnParams) == 36
-    assert capi.MuseKvCache.k.offset == 8
-    assert capi.MuseKvCache.num_pages.offset == 40
-    assert ctypes.sizeof(capi.MuseKvCache) == 48
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = {"muse_attn_params": capi.MuseAttnParams, "muse_kv_cache": capi.MuseKvCache}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "muse_attn.h"', "int main(void) {"]
+    for cname, cls in fields.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            c, f, v = line.split()
+            got[(c, f)] = int(v)
+    for cname, cls in fields.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
 
 
 def test_layer_schedule():

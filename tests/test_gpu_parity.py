@@ -383,3 +383,155 @@ def test_decode_unwritten_entries_ignored(kind, w, d, lens):
         outs.append(y.float().cpu())
     assert torch.isfinite(outs[1]).all()
     assert torch.equal(outs[0], outs[1])
+
+
+# ---------------------------------------------------------------------------
+# Decode over an FP8 (E4M3) cache
+# ---------------------------------------------------------------------------
+
+def make_cache_fp8(kind, layer, B, lens, page_tokens=32, seed=1, dev=DEV):
+    """Like make_cache, with entries stored as E4M3 codes of value / scale
+    (the oracle's quantizer) and seeded per-(page, head) or per-(sequence,
+    head) scales.  Returns the cache and the dequantized histories."""
+    from oracle import fp8
+    d, hkv = layer.d, layer.hkv
+    maxL = int(max(lens))
+    hist_k = synth.bf16_bits_to_f32(synth.normal_bf16_bits(seed, 10, (B, maxL, hkv, d)))
+    hist_v = synth.bf16_bits_to_f32(synth.normal_bf16_bits(seed, 11, (B, maxL, hkv, d)))
+    rng = np.random.default_rng(seed + 100)
+    if kind == "ring":
+        W = layer.window
+        ks = rng.uniform(0.02, 0.5, (B, hkv)).astype(np.float32)
+        vs = rng.uniform(0.02, 0.5, (B, hkv)).astype(np.float32)
+        kc = np.zeros((B, hkv, W, d), dtype=np.uint8)
+        vc = np.zeros((B, hkv, d, W), dtype=np.uint8)
+        dk = np.zeros_like(hist_k, dtype=np.float64)
+        dv = np.zeros_like(hist_v, dtype=np.float64)
+        for b in range(B):
+            L = int(lens[b])
+            for p in range(max(0, L - 1 - W), L - 1):
+                for h in range(hkv):
+                    kc[b, h, p % W] = fp8.quantize(hist_k[b, p, h], ks[b, h])
+                    vc[b, h, :, p % W] = fp8.quantize(hist_v[b, p, h], vs[b, h])
+                    dk[b, p, h] = fp8.dequantize(kc[b, h, p % W], ks[b, h])
+                    dv[b, p, h] = fp8.dequantize(vc[b, h, :, p % W], vs[b, h])
+        cache = ma.KvCache.ring(torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
+                                torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev))
+        return cache, dk, dv, ks, vs
+    pages_per = (maxL + page_tokens - 1) // page_tokens
+    n_pages = B * pages_per + 3
+    perm = np.random.default_rng(seed).permutation(n_pages)[: B * pages_per].astype(np.int32)
+    table = perm.reshape(B, pages_per)
+    ks = rng.uniform(0.02, 0.5, (n_pages, hkv)).astype(np.float32)
+    vs = rng.uniform(0.02, 0.5, (n_pages, hkv)).astype(np.float32)
+    kc = np.zeros((n_pages, hkv, page_tokens, d), dtype=np.uint8)
+    vc = np.zeros((n_pages, hkv, d, page_tokens), dtype=np.uint8)
+    dk = np.zeros_like(hist_k, dtype=np.float64)
+    dv = np.zeros_like(hist_v, dtype=np.float64)
+    for b in range(B):
+        L = int(lens[b])
+        for p in range(L - 1):
+            pg, r = table[b, p // page_tokens], p % page_tokens
+            for h in range(hkv):
+                kc[pg, h, r] = fp8.quantize(hist_k[b, p, h], ks[pg, h])
+                vc[pg, h, :, r] = fp8.quantize(hist_v[b, p, h], vs[pg, h])
+                dk[b, p, h] = fp8.dequantize(kc[pg, h, r], ks[pg, h])
+                dv[b, p, h] = fp8.dequantize(vc[pg, h, :, r], vs[pg, h])
+    cache = ma.KvCache.paged(torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
+                             torch.from_numpy(table).to(dev), page_tokens,
+                             torch.from_numpy(ks).to(dev), torch.from_numpy(vs).to(dev))
+    return cache, dk, dv, ks, vs
+
+
+FP8_CASES = [
+    # (kind, hq, hkv, d, window, theta, scale, out_norm, lens, page_tokens)
+    ("paged", 16, 2, 64, 0, 0.0, SPARK_SCALE, True, [300, 77, 1, 2, 33, 64], 32),
+    ("paged", 32, 2, 128, 0, 0.0, GLIMMER_SCALE, False, [1500, 513, 17], 16),
+    ("ring", 16, 2, 64, 256, 10000.0, SPARK_SCALE, True, [1, 2, 255, 256, 257, 700], 0),
+    ("paged", 16, 2, 64, 128, 10000.0, SPARK_SCALE, True, [500, 128, 129], 32),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=lambda c: f"{c[0]}-hq{c[1]}d{c[3]}w{c[4]}")
+def test_decode_fp8_parity(case):
+    """Decode over E4M3 codes against the oracle on the dequantized cache; the
+    new entry's codes against the oracle's quantizer."""
+    from oracle import fp8
+    kind, hq, hkv, d, w, th, s, on, lens, pt = case
+    layer = Layer(hq=hq, hkv=hkv, d=d, window=w, theta=th, scale=s, out_norm=on, out_eps=1e-6)
+    B = len(lens)
+    lens = np.array(lens, dtype=np.int32)
+    cache, dk, dv, ks, vs = make_cache_fp8(kind, layer, B, lens, page_tokens=pt or 32)
+    new = {n: synth.normal_bf16_bits(2, sid, shp) for n, sid, shp in
+           [("q", 12, (B, hq, d)), ("k", 13, (B, hkv, d)), ("v", 14, (B, hkv, d)), ("g", 15, (B, hq, d))]}
+    dn = {n: to_dev(b) for n, b in new.items()}
+    kv = torch.from_numpy(lens).to(DEV)
+    out = ma.decode(ma.LayerParams.from_layer(layer), dn["q"], dn["k"], dn["v"], dn["g"], kv, int(lens.max()), cache)
+    torch.cuda.synchronize()
+    y = out.float().cpu().numpy()
+    worst = 0.0
+    for b in range(B):
+        L = int(lens[b])
+        fb = {n: _f(v)[b] for n, v in new.items()}
+        ref = oracle.decode_one(fb["q"], fb["k"], fb["v"], fb["g"], dk[b, :max(L - 1, 0)], dv[b, :max(L - 1, 0)],
+                                0, L, layer)
+        worst = max(worst, max_err(y[b], ref))
+    print(f"decode fp8 {case} max_abs_err={worst:.3e}", flush=True)
+    assert worst <= TOL
+    # the new entry's codes: values exactly; keys exactly except where the
+    # fp32 and fp64 normalized keys fall on different sides of a rounding
+    # midpoint (then the codes are neighbours)
+    kh_new = oracle.key_prologue(_f(new["k"]), np.maximum(lens - 1, 0), layer)
+    kc = cache.k.cpu().numpy()
+    vc = cache.v.cpu().numpy()
+    table = cache.block_table.cpu().numpy() if kind == "paged" else None
+    vals = fp8.e4m3_values()
+    for b in range(B):
+        p = int(lens[b]) - 1
+        for h in range(hkv):
+            if kind == "ring":
+                kst, vst, si = kc[b, h, p % w], vc[b, h, :, p % w], (b, h)
+            else:
+                pg = int(table[b, p // pt])
+                kst, vst, si = kc[pg, h, p % pt], vc[pg, h, :, p % pt], (pg, h)
+            assert np.array_equal(vst, fp8.quantize(_f(new["v"])[b, h], vs[si]))
+            want = fp8.quantize(kh_new[b, h], ks[si])
+            diff = want != kst
+            if diff.any():
+                x = (kh_new[b, h].astype(np.float32) / ks[si])[diff].astype(np.float64)
+                mid = (vals[want[diff] & 0x7F] + vals[kst[diff] & 0x7F]) / 2 * np.sign(x)
+                assert np.all(np.abs(np.abs(want[diff].astype(int) & 0x7F) - (kst[diff].astype(int) & 0x7F)) == 1)
+                assert np.allclose(x, mid, rtol=1e-5), (b, h, x, mid)
+
+
+def test_decode_fp8_value_codes_exact():
+    """Every finite E4M3 code read back exactly: one cached entry, q = 0 (equal
+    weights), v_new = 0 and a gate of 30 (sigmoid 1 in fp32), so each output
+    is value(code) * scale / 2, exact in bf16 for power-of-two scales."""
+    from oracle import fp8
+    d, hkv, hq = 64, 4, 8
+    layer = Layer(hq=hq, hkv=hkv, d=d, window=0, theta=0.0, scale=1.0)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    B = (len(codes) + hkv * d - 1) // (hkv * d)
+    vcodes = np.resize(codes, (B, hkv, d)).astype(np.uint8)
+    pt = 16
+    table = np.arange(B, dtype=np.int32).reshape(B, 1)
+    kc = np.zeros((B, hkv, pt, d), dtype=np.uint8)
+    vc = np.zeros((B, hkv, d, pt), dtype=np.uint8)
+    vc[:, :, :, 0] = vcodes
+    ks = np.ones((B, hkv), dtype=np.float32)
+    vs = np.full((B, hkv), 4.0, dtype=np.float32)
+    cache = ma.KvCache.paged(torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV),
+                             torch.from_numpy(table).to(DEV), pt, torch.from_numpy(ks).to(DEV),
+                             torch.from_numpy(vs).to(DEV))
+    q = torch.zeros((B, hq, d), dtype=torch.bfloat16, device=DEV)
+    kn = to_dev(synth.normal_bf16_bits(0, 13, (B, hkv, d)))
+    vn = torch.zeros((B, hkv, d), dtype=torch.bfloat16, device=DEV)
+    g = torch.full((B, hq, d), 30.0, dtype=torch.bfloat16, device=DEV)
+    lens = torch.full((B,), 2, dtype=torch.int32, device=DEV)
+    y = ma.decode(ma.LayerParams.from_layer(layer), q, kn, vn, g, lens, 2, cache)
+    torch.cuda.synchronize()
+    want = fp8.e4m3_decode(vcodes) * 4.0 / 2.0                 # [B, Hkv, D]
+    got = y.float().cpu().numpy().reshape(B, hkv, hq // hkv, d)
+    for j in range(hq // hkv):
+        assert np.array_equal(got[:, :, j, :], want)
