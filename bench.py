@@ -138,15 +138,16 @@ def prefill_case(cfg, steps, warmup, events, torch, ma, keep=False):
     return res
 
 
-def decode_case(cfg, steps, warmup, events, torch, ma, flush=False):
+def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False):
     from synth.device import decode_device_setup
     from global_muse_rope_amd import accounting as acc
     L = cfg.layer
-    s = decode_device_setup(cfg)
+    s = decode_device_setup(cfg, fp8=fp8)
+    ks, vs = s.get("k_scale"), s.get("v_scale")
     if s["kind"] == "ring":
-        s["cache"] = ma.KvCache.ring(s["kc"], s["vc"])
+        s["cache"] = ma.KvCache.ring(s["kc"], s["vc"], ks, vs)
     else:
-        s["cache"] = ma.KvCache.paged(s["kc"], s["vc"], s["block_table"], s["page_tokens"])
+        s["cache"] = ma.KvCache.paged(s["kc"], s["vc"], s["block_table"], s["page_tokens"], ks, vs)
     lp = ma.LayerParams.from_layer(L)
     ws = torch.empty(ma.decode_workspace_size(lp, cfg.batch, s["max_len"], s["cache"]), dtype=torch.uint8,
                      device="cuda")
@@ -159,8 +160,11 @@ def decode_case(cfg, steps, warmup, events, torch, ma, flush=False):
         ma.decode(lp, s["q"], s["k"], s["v"], s["g"], s["kv_len"], s["max_len"], s["cache"], out=out, workspace=ws)
 
     wall, kern = timed_steps(step, steps, warmup, events, torch)
-    kv_bytes = acc.decode_kv_bytes(L.hkv, L.d, s["lengths"], L.window)
-    io = acc.decode_io_bytes(L.hq, L.hkv, L.d, cfg.batch)
+    eb = 1 if fp8 else 2
+    kv_bytes = acc.decode_kv_bytes(L.hkv, L.d, s["lengths"], L.window, eb)
+    if fp8:
+        kv_bytes += acc.decode_scale_bytes(L.hkv, s["lengths"], L.window, s["page_tokens"])
+    io = acc.decode_io_bytes(L.hq, L.hkv, L.d, cfg.batch, eb)
     res = {"kernel_ms": kern, "kv_bytes": kv_bytes, "gbs": (kv_bytes + io) / (kern * 1e-3) / 1e9,
            "ms_per_step": wall, "lengths_sum": int(sum(s["lengths"]))}
     del s, ws, out, scrub
@@ -298,10 +302,11 @@ def traffic_summary(workload, kernel, fetch_csv, write_csv, commands):
 def only_case(name, steps, warmup, torch, ma):
     """Time one workload by itself (for a per-workload kernel trace)."""
     from synth import workloads as wl
-    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE}[name]
+    fp8 = name.endswith("_fp8")
+    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE}[name[:-4] if fp8 else name]
     events = HipEvents()
     if cfg in wl.DECODE:
-        r = decode_case(cfg, steps, warmup, events, torch, ma, flush=cfg.layer.window > 0)
+        r = decode_case(cfg, steps, warmup, events, torch, ma, flush=cfg.layer.window > 0, fp8=fp8)
         print(json.dumps({"workload": name, "kernel": "decode_split_kernel", "kernel_ms": round(r["kernel_ms"], 4),
                           "GB/s": round(r["gbs"], 1), "ms_per_step": round(r["ms_per_step"], 4),
                           "steps": steps, "warmup": warmup}), flush=True)
@@ -395,16 +400,20 @@ def main():
         log(f"device copy {copy_gbs:.0f} GB/s (read + write)")
         result["hbm_copy_gbs"] = round(copy_gbs, 1)
         dec = {}
-        for dcfg, steps, flush in [(wl.SPARK_DECODE_GLOBAL, 10, False), (wl.SPARK_DECODE_LOCAL, 20, True)]:
-            log(f"decode {dcfg.name}")
-            r = decode_case(dcfg, steps, 2, events, torch, ma, flush=flush)
+        for dcfg, steps, flush, fp8 in [(wl.SPARK_DECODE_GLOBAL, 10, False, False),
+                                        (wl.SPARK_DECODE_LOCAL, 20, True, False),
+                                        (wl.SPARK_DECODE_GLOBAL, 10, False, True)]:
+            name = dcfg.name + ("_fp8" if fp8 else "")
+            log(f"decode {name}")
+            r = decode_case(dcfg, steps, 2, events, torch, ma, flush=flush, fp8=fp8)
             log(f"  {r['gbs']:.0f} GB/s, split kernel {r['kernel_ms']:.3f} ms")
-            dec[dcfg.name] = {"value": round(r["gbs"], 1), "unit": "GB/s", "kernel": "decode_split_kernel",
-                              "kernel_ms": round(r["kernel_ms"], 4), "ms_per_step": round(r["ms_per_step"], 4),
-                              "kv_bytes_per_step": r["kv_bytes"], "cache_flushed": flush,
-                              "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS,
-                                           "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
-                                           "frac_of_copy": round(r["gbs"] / copy_gbs, 4)}}
+            dec[name] = {"value": round(r["gbs"], 1), "unit": "GB/s", "kernel": "decode_split_kernel",
+                         "cache_dtype": "e4m3" if fp8 else "bf16",
+                         "kernel_ms": round(r["kernel_ms"], 4), "ms_per_step": round(r["ms_per_step"], 4),
+                         "kv_bytes_per_step": r["kv_bytes"], "cache_flushed": flush,
+                         "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                                      "frac_of_copy": round(r["gbs"] / copy_gbs, 4)}}
         result["decode"] = dec
 
     if not args.quick:

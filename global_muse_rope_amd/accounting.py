@@ -40,16 +40,24 @@ def decode_visible_history(kv_len: int, window: int) -> int:
     return min(kv_len, window) - 1
 
 
-def decode_kv_bytes(hkv: int, d: int, lengths, window: int) -> int:
+def decode_kv_bytes(hkv: int, d: int, lengths, window: int, elem_bytes: int = 2) -> int:
     """Bytes of cached K and V one decode step reads, summed over sequences."""
-    per = kv_bytes_per_token(hkv, d)
+    per = kv_bytes_per_token(hkv, d, elem_bytes)
     return sum(decode_visible_history(int(n), window) * per for n in lengths)
 
 
-def decode_io_bytes(hq: int, hkv: int, d: int, batch: int) -> int:
+def decode_scale_bytes(hkv: int, lengths, window: int, page_tokens: int) -> int:
+    """Bytes of float32 K and V scales an FP8 decode step reads: one pair per
+    (page, head) holding visible history (paged) or per (sequence, head)."""
+    if page_tokens == 0:
+        return len(lengths) * hkv * 8
+    return sum(-(-decode_visible_history(int(n), window) // page_tokens) * hkv * 8 for n in lengths)
+
+
+def decode_io_bytes(hq: int, hkv: int, d: int, batch: int, elem_bytes: int = 2) -> int:
     """Per-step bytes outside the cache: q, gate, new k and v read, output
-    written, new k and v appended (all bf16)."""
-    return batch * d * 2 * (hq + hq + hkv + hkv + hq + 2 * hkv)
+    written (bf16), new k and v appended (cache element size)."""
+    return batch * d * (2 * (hq + hq + hkv + hkv + hq) + 2 * hkv * elem_bytes)
 
 
 def decode_flops(hq: int, d: int, lengths, window: int) -> int:

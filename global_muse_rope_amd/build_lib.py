@@ -23,6 +23,10 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + INCLUDE,
 ]
+# Per-source flags.  The decode kernels keep their MFMA accumulators in
+# ordinary VGPRs: the accumulators are rescaled on a rarely taken branch,
+# and in accumulation registers every pass would copy them out and back.
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -34,7 +38,8 @@ def hipcc() -> str:
 
 def _compile(src: str, defines=(), tag="") -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *["-D" + d for d in defines], "-c", os.path.join(SRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *["-D" + d for d in defines], "-c",
+           os.path.join(SRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -154,15 +154,24 @@ __device__ __forceinline__ bool hist_valid(const HistRange& r, int idx) {
 // ---------------------------------------------------------------------------
 // 2. split
 // ---------------------------------------------------------------------------
-// Block-table entries one paged chunk can touch: chunks of kPagedChunk
-// positions over pages of at least 16 positions, plus one for a chunk start
-// that is not page-aligned.
-constexpr int kMaxChunkPages = kPagedChunk / 16 + 2;
-// Register buffers of 32-entry sub-chunks per wave (PD - 1 in flight).
+// 8-entry blocks of one paged chunk (each lies inside one page: pages hold a
+// multiple of 16 positions and chunks start at multiples of 8).
+constexpr int kChunkBlocks = kPagedChunk / 8;
+// Register buffers of 32-entry sub-chunks per wave (PD - 1 in flight).  An
+// E4M3 sub-chunk carries half the bytes of a bf16 one, so it keeps more in
+// flight for the same bytes per wave.
 #ifndef MUSE_DECODE_DEPTH
 #define MUSE_DECODE_DEPTH 2
 #endif
+#ifndef MUSE_DECODE_DEPTH_FP8
+#define MUSE_DECODE_DEPTH_FP8 2
+#endif
 constexpr int kDecodeDepth = MUSE_DECODE_DEPTH;
+constexpr int kDecodeDepthFp8 = MUSE_DECODE_DEPTH_FP8;
+// The running maximum (log2 units) is raised only when a logit exceeds it by
+// more than this, so unnormalized weights stay below 2^kRescaleSlack and most
+// sub-chunks skip the rescale of the accumulators.
+constexpr float kRescaleSlack = 16.f;
 
 template <int D, int G, bool FP8>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
@@ -173,7 +182,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   __shared__ float sm_m[NW][16];
   __shared__ float sm_l[NW][16];
   __shared__ float sm_o[NW][16][D + 1];
-  __shared__ int sm_page[kMaxChunkPages];
+  // paged: element offsets of each 8-entry block's first K row and first V
+  // column (-1: page absent) and its scale index page * Hkv + hk
+  __shared__ int64_t sm_koff[kChunkBlocks];
+  __shared__ int64_t sm_voff[kChunkBlocks];
+  __shared__ int sm_sidx[kChunkBlocks];
 
   const int item = blockIdx.x;
   const int c = item % a.max_chunks;
@@ -188,7 +201,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const int c1 = min(c0 + a.chunk_tokens, hr.end);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  // wave index as a wave-uniform (scalar) value: the sub-chunk loop and its
+  // full / partial test then branch on scalars instead of lane masks
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 15;  // query head within the group (columns >= G are padding)
   const int g4 = lane >> 4;   // 0..3
@@ -214,41 +229,37 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     }
   }
 
-  // Paged cache: the chunk's block-table entries go to LDS once, so the
-  // address of every prefetch is one LDS read away instead of a dependent
-  // global load (whose wait would also drain the loads already in flight).
-  // Absent or out-of-range pages are stored as -1.
+  // Paged cache: the page lookup of every block is done once per workgroup
+  // (one block per thread), so a prefetch address is one LDS read away
+  // instead of a division and a dependent global load (whose wait would also
+  // drain the loads already in flight).
+  const bool paged = a.kind != MUSE_KV_RING;
   const int pt = a.page_tokens;
-  const int pg0 = a.kind == MUSE_KV_RING ? 0 : c0 / pt;
-  if (a.kind != MUSE_KV_RING) {
-    const int npg = (c1 - 1) / pt - pg0 + 1;
-    for (int i = tid; i < npg; i += NW * kWave) {
-      const int pi = pg0 + i;
-      int page = pi < a.max_pages ? a.block_table[static_cast<int64_t>(b) * a.max_pages + pi] : -1;
-      sm_page[i] = (page >= 0 && page < a.num_pages) ? page : -1;
+  if (paged) {
+    for (int i = tid; i < kChunkBlocks; i += NW * kWave) {
+      const int idx = c0 + 8 * i;
+      int64_t ko = -1, vo = -1;
+      int si = -1;
+      if (idx < c1) {
+        const int pi = idx / pt;
+        const int r = idx - pi * pt;
+        const int page = pi < a.max_pages ? a.block_table[static_cast<int64_t>(b) * a.max_pages + pi] : -1;
+        if (page >= 0 && page < a.num_pages) {
+          si = page * a.Hkv + hk;
+          ko = (static_cast<int64_t>(si) * pt + r) * D;
+          vo = static_cast<int64_t>(si) * D * pt + r;
+        }
+      }
+      sm_koff[i] = ko;
+      sm_voff[i] = vo;
+      sm_sidx[i] = si;
     }
     __syncthreads();
   }
 
   const uint16_t* kc = a.kc;
   const uint16_t* vc = a.vc;
-  // address of (cached index idx) for this (b, hk): K row and V^T column
-  auto kaddr = [&](int idx) -> int64_t {
-    if (a.kind == MUSE_KV_RING) return ((static_cast<int64_t>(bh)) * a.capacity + idx) * D;
-    const int64_t page = sm_page[idx / pt - pg0];
-    return ((page * a.Hkv + hk) * pt + idx % pt) * D;
-  };
-  auto vaddr = [&](int idx) -> int64_t {  // element (dim 0, idx); dim stride = vstride
-    if (a.kind == MUSE_KV_RING) return static_cast<int64_t>(bh) * D * a.capacity + idx;
-    const int64_t page = sm_page[idx / pt - pg0];
-    return (page * a.Hkv + hk) * D * pt + idx % pt;
-  };
-  auto tile_ok = [&](int idx0) -> bool {  // 16-key tile starting at idx0 may be loaded
-    if (idx0 >= hr.end) return false;
-    if (a.kind == MUSE_KV_RING) return true;
-    return sm_page[idx0 / pt - pg0] >= 0;
-  };
-  const int vstride = a.kind == MUSE_KV_RING ? a.capacity : a.page_tokens;
+  const int vstride = paged ? pt : a.capacity;
 
   float m = NEG, lsum = 0.f;
   f32x4 o[DB];
@@ -261,7 +272,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   // waits would drain the loads in flight).  Row r = 4g + i of key tile kt
   // holds entry 8g + 4kt + i, so the eight entries a lane needs for P V are
   // contiguous in the head-dim-major V rows (one 16-byte load per fragment).
-  constexpr int PD = kDecodeDepth;
+  // A lane's K rows lie in 8-entry block col / 4 of the sub-chunk, its logits,
+  // weights and V entries in block g4.
+  constexpr int PD = FP8 ? kDecodeDepthFp8 : kDecodeDepth;
   // one fragment: 8 entries of 16 bits (bf16) or 8 bits (E4M3 codes)
   using Frag = typename std::conditional<FP8, u32x2, u32x4>::type;
   struct Buf {
@@ -273,18 +286,27 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   Buf bufs[PD];
   const uint8_t* kc8 = reinterpret_cast<const uint8_t*>(a.kc);
   const uint8_t* vc8 = reinterpret_cast<const uint8_t*>(a.vc);
-  // ring caches: one scale per (sequence, KV head)
-  const float ring_ks = FP8 && a.kind == MUSE_KV_RING ? a.k_scale[bh] : 1.f;
-  const float ring_vs = FP8 && a.kind == MUSE_KV_RING ? a.v_scale[bh] : 1.f;
-  // Loads are issued unconditionally (an absent tile reads the start of the
+  // Loads are issued unconditionally (an absent block reads the start of the
   // cache instead) and zeroed at use: predicated loads would leave the
   // number of loads in flight unknown and force full waits.
   auto load = [&](Buf& B, int s0) {
-    const int ik = s0 + 8 * (col >> 2);
-    B.kok = tile_ok(ik);
-    // rows ik + (col & 3) and ik + 4 + (col & 3) share one page (pages hold
-    // a multiple of 16 positions and ik is a multiple of 8)
-    const int64_t ka = B.kok ? kaddr(ik + (col & 3)) : 0;
+    int64_t ka, va;
+    if (paged) {
+      const int blk = (s0 - c0) >> 3;
+      const int64_t ko = sm_koff[blk + (col >> 2)];
+      const int64_t vo = sm_voff[blk + g4];
+      B.kok = ko >= 0;
+      B.vok = vo >= 0;
+      ka = B.kok ? ko + (col & 3) * D : 0;
+      va = B.vok ? vo : 0;
+    } else {
+      const int ik = s0 + 8 * (col >> 2);
+      const int iv = s0 + 8 * g4;
+      B.kok = ik < hr.end;
+      B.vok = iv < hr.end;
+      ka = B.kok ? (static_cast<int64_t>(bh) * a.capacity + ik + (col & 3)) * D : 0;
+      va = B.vok ? static_cast<int64_t>(bh) * D * a.capacity + iv : 0;
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -294,9 +316,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         else
           B.k[kt][ds] = *reinterpret_cast<const u32x4*>(kc + ka + 4 * kt * D + 32 * ds + 8 * g4);
       }
-    const int iv = s0 + 8 * g4;
-    B.vok = tile_ok(iv);
-    const int64_t va = B.vok ? vaddr(iv) : 0;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       if constexpr (FP8)
@@ -305,53 +324,57 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         B.v[db] = *reinterpret_cast<const u32x4*>(vc + va + static_cast<int64_t>(16 * db + col) * vstride);
     }
     if constexpr (FP8) {
-      // this lane's logits and probabilities are entries iv .. iv + 7: one page
-      if (a.kind == MUSE_KV_RING) {
-        B.ks = ring_ks;
-        B.vs = ring_vs;
-      } else {
-        const int page = B.vok ? sm_page[iv / pt - pg0] : 0;
-        const int64_t si = static_cast<int64_t>(page) * a.Hkv + hk;
-        B.ks = a.k_scale[si];
-        B.vs = a.v_scale[si];
-      }
+      // issued for both cache kinds so every path has the same loads in flight
+      const int si = paged ? max(sm_sidx[((s0 - c0) >> 3) + g4], 0) : bh;
+      B.ks = a.k_scale[si];
+      B.vs = a.v_scale[si];
     }
   };
 
   auto process = [&](Buf& B, int s0) {
-    // absent tiles read as zeros; V entries at or past the end may never have
-    // been written and are zeroed too, so p = 0 never meets a non-finite value
+    // A sub-chunk whose 32 entries are all visible, written and present (the
+    // common case) skips every per-entry mask; the test is wave-uniform.
+    const bool full = s0 >= hr.lo && s0 + 32 <= hr.end && (hr.skip < s0 || hr.skip >= s0 + 32) &&
+                      __builtin_amdgcn_ballot_w64(!(B.kok && B.vok)) == 0;
     u32x4 kcur[2][DS];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        u32x4 kw;
         if constexpr (FP8)
-          kw = e4m3x8_to_bf16x8(B.k[kt][ds]);
+          kcur[kt][ds] = e4m3x8_to_bf16x8(B.k[kt][ds]);
         else
-          kw = B.k[kt][ds];
-        kcur[kt][ds] = B.kok ? kw : u32x4{0, 0, 0, 0};
+          kcur[kt][ds] = B.k[kt][ds];
       }
     u32x4 vcur[DB];
-    const int nv = B.vok ? hr.end - (s0 + 8 * g4) : 0;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      u32x4 vw;
       if constexpr (FP8)
-        vw = e4m3x8_to_bf16x8(B.v[db]);
+        vcur[db] = e4m3x8_to_bf16x8(B.v[db]);
       else
-        vw = B.v[db];
+        vcur[db] = B.v[db];
+    }
+    if (!full) {
+      // absent blocks read as zeros; V entries at or past the end may never
+      // have been written and are zeroed too, so p = 0 never meets a
+      // non-finite value
 #pragma unroll
-      for (int wd = 0; wd < 4; ++wd)
-        vcur[db][wd] = 2 * wd >= nv ? 0u : (2 * wd + 1 >= nv ? (vw[wd] & 0xffffu) : vw[wd]);
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+          if (!B.kok) kcur[kt][ds] = u32x4{0, 0, 0, 0};
+      const int nv = B.vok ? hr.end - (s0 + 8 * g4) : 0;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd)
+          vcur[db][wd] = 2 * wd >= nv ? 0u : (2 * wd + 1 >= nv ? (vcur[db][wd] & 0xffffu) : vcur[db][wd]);
     }
     const float kscale = FP8 ? B.ks : 1.f;
     const float vscale = FP8 ? B.vs : 1.f;
 
     // S^T tiles: entries s0 + 8*g4 + 4*kt + i, head col
     float s[2][4];
-    float tmax = NEG;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -362,56 +385,83 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qlo[ds], acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = s0 + 8 * g4 + 4 * kt + i;
-        s[kt][i] = hist_valid(hr, idx) ? acc[i] * kscale : NEG;
-        tmax = fmaxf(tmax, s[kt][i]);
-      }
+      for (int i = 0; i < 4; ++i) s[kt][i] = FP8 ? acc[i] * kscale : acc[i];
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float mnew = fmaxf(m, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
+    if (!full) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!hist_valid(hr, s0 + 8 * g4 + 4 * kt + i)) s[kt][i] = NEG;
+    }
+    float tmax = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                       fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    if (__builtin_amdgcn_ballot_w64(tmax > m + kRescaleSlack) != 0) {
+      // the lanes of one column (head) share its maximum
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float mnew = fmaxf(m, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    }
+    float p[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[kt][i] = __builtin_amdgcn_exp2f(s[kt][i] - m);
+    if (!full) {
+      // masked entries of a column that has seen no visible entry yet
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!(s[kt][i] > NEG)) p[kt][i] = 0.f;
+    }
     bf16x8 phi, plo;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = s[kt][i] > NEG ? __builtin_amdgcn_exp2f(s[kt][i] - mnew) : 0.f;
-        psum += p;
-        const float pv = p * vscale;  // the value scale of this lane's page
+        psum += p[kt][i];
+        const float pv = FP8 ? p[kt][i] * vscale : p[kt][i];  // the value scale of this lane's page
         const bf16_t hi = static_cast<bf16_t>(pv);
         phi[4 * kt + i] = hi;
         plo[4 * kt + i] = static_cast<bf16_t>(pv - static_cast<float>(hi));
       }
-    lsum = lsum * alpha + psum;
+    lsum += psum;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      o[db] *= alpha;
       const bf16x8 vf = __builtin_bit_cast(bf16x8, vcur[db]);
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, phi, o[db], 0, 0, 0);
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, plo, o[db], 0, 0, 0);
     }
   };
 
-  // this wave's sub-chunks: w, w + NW, w + 2 NW, ...
+  // this wave's sub-chunks: w, w + NW, w + 2 NW, ...  Every prefetch is
+  // issued, past the end as a repeat of the last sub-chunk, so the number
+  // of loads in flight is the same on every path through the loop.
   const int nsub = (c1 - c0 + 31) / 32;
   const int nmine = nsub > w ? (nsub - w + NW - 1) / NW : 0;
-  auto sub_s0 = [&](int j) { return c0 + 32 * (w + j * NW); };
+  auto sub_s0 = [&](int j) { return c0 + 32 * (w + min(j, nmine - 1) * NW); };
+  if (nmine > 0) {
 #pragma unroll
-  for (int j = 0; j < PD - 1; ++j)
-    if (j < nmine) load(bufs[j], sub_s0(j));
-  for (int j0 = 0; j0 < nmine; j0 += PD) {
+    for (int j = 0; j < PD - 1; ++j) load(bufs[j], sub_s0(j));
+    int j0 = 0;
+    for (; j0 + PD <= nmine; j0 += PD) {
 #pragma unroll
-    for (int u = 0; u < PD; ++u) {
-      const int j = j0 + u;
-      if (j < nmine) {
-        if (j + PD - 1 < nmine) load(bufs[(u + PD - 1) % PD], sub_s0(j + PD - 1));
-        process(bufs[u], sub_s0(j));
+      for (int u = 0; u < PD; ++u) {
+        load(bufs[(u + PD - 1) % PD], sub_s0(j0 + u + PD - 1));
+        process(bufs[u], sub_s0(j0 + u));
       }
     }
+    // fewer than PD sub-chunks left, in bufs[0 .. PD - 2]
+#pragma unroll
+    for (int u = 0; u < PD - 1; ++u)
+      if (j0 + u < nmine) process(bufs[u], sub_s0(j0 + u));
   }
   lsum += __shfl_xor(lsum, 16, kWave);
   lsum += __shfl_xor(lsum, 32, kWave);

@@ -83,6 +83,19 @@ def normal_f32(seed: int, stream_id: int, idx) -> np.ndarray:
     return out
 
 
+def e4m3_codes(seed: int, stream_id: int, idx) -> np.ndarray:
+    """uint8 codes for flat indices ``idx``: one 64-bit word per index; the
+    low 16 bits pick a magnitude code in 0x20 .. 0x47 (0.125 .. 3.75 in the
+    OCP E4M3 encoding), bit 16 the sign.  Data only: no rounding of values."""
+    idx = np.asarray(idx, dtype=np.int64).astype(np.uint64)
+    key = np.uint64(stream_key(seed, stream_id))
+    with np.errstate(over="ignore"):
+        h = _mix64_np(key + idx * np.uint64(GAMMA))
+    mag = (h & np.uint64(0xFFFF)) % np.uint64(40) + np.uint64(0x20)
+    sign = ((h >> np.uint64(16)) & np.uint64(1)) << np.uint64(7)
+    return (mag | sign).astype(np.uint8)
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest-even); returns uint16 bit patterns."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -147,6 +160,16 @@ def normal_bf16_torch(seed: int, stream_id: int, idx):
     r = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
     r = torch.where(r >= 32768, r - 65536, r).to(torch.int16)
     return r.view(torch.bfloat16)
+
+
+def e4m3_codes_torch(seed: int, stream_id: int, idx):
+    """The same codes as ``e4m3_codes`` as a uint8 tensor (any device)."""
+    import torch
+    key = stream_key(seed, stream_id)
+    h = _mix64_torch(idx.to(torch.int64) * _as_i64(GAMMA) + _as_i64(key))
+    mag = torch.remainder(h & 0xFFFF, 40) + 0x20
+    sign = (_lsr(h, 16) & 1) << 7
+    return (mag | sign).to(torch.uint8)
 
 
 def normal_bf16_torch_tensor(seed: int, stream_id: int, shape, device, offset: int = 0):

@@ -9,12 +9,17 @@ like raw projections (mean square 1 per head, as the layer's normalized keys
 have on average) and stored as given; the layer treats cache contents as
 data.  Paged caches place each sequence's pages at positions drawn from a
 seeded permutation of the pool.
+
+FP8 caches hold E4M3 codes drawn directly from the same streams (magnitude
+codes 0x20 .. 0x47 with a random sign, no rounding of any value) and seeded
+float32 scales in [0.3, 0.6) per (page, head) or per (sequence, head).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import normal_bf16_torch, normal_bf16_torch_tensor, bf16_bits_to_f64, f32_to_bf16_bits, normal_f32
+from . import (normal_bf16_torch, normal_bf16_torch_tensor, bf16_bits_to_f64, f32_to_bf16_bits, normal_f32,
+               e4m3_codes, e4m3_codes_torch)
 from .workloads import S_Q, S_K, S_V, S_G, S_CACHE_BASE, decode_lengths
 
 STREAM = {"q": S_Q, "k": S_K, "v": S_V, "g": S_G}
@@ -83,6 +88,25 @@ def cache_values_host(seed, b, h, hkv, which, p0, p1, d):
     return vals
 
 
+def cache_codes_torch(seed, b, h, hkv, which, p0, p1, d, device):
+    """uint8 E4M3 codes [p1 - p0, d] of cached entries at positions p0 .. p1-1."""
+    import torch
+    idx = torch.arange(p0 * d, p1 * d, dtype=torch.int64, device=device)
+    return e4m3_codes_torch(seed, cache_stream(b, h, hkv, which), idx).view(p1 - p0, d)
+
+
+def cache_codes_host(seed, b, h, hkv, which, p0, p1, d):
+    """The same codes on the host (numpy uint8 [p1 - p0, d])."""
+    idx = np.arange(p0 * d, p1 * d, dtype=np.int64)
+    return e4m3_codes(seed, cache_stream(b, h, hkv, which), idx).reshape(p1 - p0, d)
+
+
+def cache_scales(seed, shape):
+    """Seeded float32 scales (k, v) in [0.3, 0.6) of the given shape."""
+    rng = np.random.default_rng(seed + 3)
+    return (rng.uniform(0.3, 0.6, shape).astype(np.float32), rng.uniform(0.3, 0.6, shape).astype(np.float32))
+
+
 def new_token_shapes(cfg):
     L = cfg.layer
     return {"q": (cfg.batch, L.hq, L.d), "k": (cfg.batch, L.hkv, L.d), "v": (cfg.batch, L.hkv, L.d),
@@ -97,11 +121,13 @@ def new_token_host(cfg):
     return out
 
 
-def decode_device_setup(cfg, device="cuda", lengths=None):
+def decode_device_setup(cfg, device="cuda", lengths=None, fp8=False):
     """Ring (window > 0) or paged (global) cache filled for every sequence's
     history, the new-token tensors and kv_len.  Returns a dict of tensors:
     q, k, v, g, kv_len (int32), lengths (numpy), max_len, and the cache
-    pieces kind, kc, vc, block_table, page_tokens."""
+    pieces kind, kc, vc, block_table, page_tokens; with ``fp8`` the pools
+    hold E4M3 codes and the dict adds k_scale, v_scale (device) and
+    scales_host (numpy k, v) and table_host (paged)."""
     import torch
     L = cfg.layer
     d, hkv, B = L.d, L.hkv, cfg.batch
@@ -112,10 +138,23 @@ def decode_device_setup(cfg, device="cuda", lengths=None):
     res["kv_len"] = torch.from_numpy(lengths.astype(np.int32)).to(device)
     res["lengths"] = lengths
     res["max_len"] = max_len
+    edt = torch.uint8 if fp8 else torch.bfloat16
+
+    def values(b, h, which, p0, p1):
+        if fp8:
+            return cache_codes_torch(cfg.seed, b, h, hkv, which, p0, p1, d, device)
+        return cache_values_torch(cfg.seed, b, h, hkv, which, p0, p1, d, device)
+
+    def put_scales(shape):
+        if fp8:
+            ks, vs = cache_scales(cfg.seed, shape)
+            res.update(k_scale=torch.from_numpy(ks).to(device), v_scale=torch.from_numpy(vs).to(device),
+                       scales_host=(ks, vs))
+
     if L.window > 0:
         W = L.window
-        kc = torch.zeros((B, hkv, W, d), dtype=torch.bfloat16, device=device)
-        vc = torch.zeros((B, hkv, d, W), dtype=torch.bfloat16, device=device)
+        kc = torch.zeros((B, hkv, W, d), dtype=edt, device=device)
+        vc = torch.zeros((B, hkv, d, W), dtype=edt, device=device)
         for b in range(B):
             n = int(lengths[b])
             p0, p1 = max(0, n - 1 - W), n - 1
@@ -123,9 +162,10 @@ def decode_device_setup(cfg, device="cuda", lengths=None):
                 continue
             slots = torch.arange(p0, p1, device=device) % W
             for h in range(hkv):
-                kc[b, h, slots, :] = cache_values_torch(cfg.seed, b, h, hkv, "k", p0, p1, d, device)
-                vc[b, h, :, slots] = cache_values_torch(cfg.seed, b, h, hkv, "v", p0, p1, d, device).t()
+                kc[b, h, slots, :] = values(b, h, "k", p0, p1)
+                vc[b, h, :, slots] = values(b, h, "v", p0, p1).t()
         res.update(kind="ring", kc=kc, vc=vc, block_table=None, page_tokens=0)
+        put_scales((B, hkv))
         return res
     pt = cfg.page_tokens
     pages = [(int(n) + pt - 1) // pt for n in lengths]
@@ -137,20 +177,21 @@ def decode_device_setup(cfg, device="cuda", lengths=None):
     for b in range(B):
         table[b, :pages[b]] = perm[off:off + pages[b]]
         off += pages[b]
-    kc = torch.empty((n_pool, hkv, pt, d), dtype=torch.bfloat16, device=device)
-    vc = torch.empty((n_pool, hkv, d, pt), dtype=torch.bfloat16, device=device)
+    kc = torch.empty((n_pool, hkv, pt, d), dtype=edt, device=device)
+    vc = torch.empty((n_pool, hkv, d, pt), dtype=edt, device=device)
     tdev = torch.from_numpy(table).to(device)
     for b in range(B):
         n = int(lengths[b])
         idxp = tdev[b, :pages[b]].long()
         for h in range(hkv):
             for which, dst in (("k", kc), ("v", vc)):
-                vals = torch.zeros((pages[b] * pt, d), dtype=torch.bfloat16, device=device)
-                vals[:n] = cache_values_torch(cfg.seed, b, h, hkv, which, 0, n, d, device)
+                vals = torch.zeros((pages[b] * pt, d), dtype=edt, device=device)
+                vals[:n] = values(b, h, which, 0, n)
                 vals = vals.view(pages[b], pt, d)
                 if which == "k":
                     dst[idxp, h] = vals
                 else:
                     dst[idxp, h] = vals.transpose(1, 2)
-    res.update(kind="paged", kc=kc, vc=vc, block_table=tdev, page_tokens=pt)
+    res.update(kind="paged", kc=kc, vc=vc, block_table=tdev, page_tokens=pt, table_host=table)
+    put_scales((n_pool, hkv))
     return res

@@ -110,13 +110,14 @@ def test_prefill_fullsize_sampled(cfg):
     assert worst <= TOL
 
 
-def _decode_run(cfg):
+def _decode_run(cfg, fp8=False):
     L = cfg.layer
-    s = sd.decode_device_setup(cfg)
+    s = sd.decode_device_setup(cfg, fp8=fp8)
+    ks, vs = s.get("k_scale"), s.get("v_scale")
     if s["kind"] == "ring":
-        cache = ma.KvCache.ring(s["kc"], s["vc"])
+        cache = ma.KvCache.ring(s["kc"], s["vc"], ks, vs)
     else:
-        cache = ma.KvCache.paged(s["kc"], s["vc"], s["block_table"], s["page_tokens"])
+        cache = ma.KvCache.paged(s["kc"], s["vc"], s["block_table"], s["page_tokens"], ks, vs)
     lp = ma.LayerParams.from_layer(L)
     ws = torch.empty(ma.decode_workspace_size(lp, cfg.batch, s["max_len"], cache), dtype=torch.uint8,
                      device=DEV)
@@ -125,8 +126,11 @@ def _decode_run(cfg):
     torch.cuda.synchronize()
     y = out.float().cpu().numpy()
     lengths = s["lengths"]
+    extra = {k: s[k] for k in ("scales_host", "table_host", "page_tokens") if k in s}
     del s, cache, ws, out
     torch.cuda.empty_cache()
+    if fp8:
+        return y, lengths, extra
     return y, lengths
 
 
@@ -174,4 +178,52 @@ def test_decode_fullsize_local_ring_all():
             ref = oracle_decode_pair(cfg, new, b, hk, int(lengths[b]))
             worst = max(worst, max_err(y[b, hk * G:(hk + 1) * G], ref))
     print(f"{cfg.name}: all {cfg.batch * cfg.layer.hkv} pairs, max_abs_err={worst:.3e}", flush=True)
+    assert worst <= TOL
+
+
+def oracle_decode_pair_fp8(cfg, new, b, hk, L_b, extra):
+    """As oracle_decode_pair over an E4M3 cache: the history is the codes
+    regenerated on the host, dequantized with each position's scale (page
+    of the block table, or the sequence's scale for a ring)."""
+    from oracle import fp8
+    lay = cfg.layer
+    G = lay.group
+    p = L_b - 1
+    lo, _ = oracle.visible_range(p, lay.window)
+    ks, vs = extra["scales_host"]
+    pos = np.arange(lo, p)
+    if "table_host" in extra:
+        pages = extra["table_host"][b, pos // extra["page_tokens"]]
+        k_sc, v_sc = ks[pages, hk], vs[pages, hk]
+    else:
+        k_sc = np.full(len(pos), ks[b, hk], dtype=np.float32)
+        v_sc = np.full(len(pos), vs[b, hk], dtype=np.float32)
+    hist = {}
+    for which, sc in (("k", k_sc), ("v", v_sc)):
+        codes = sd.cache_codes_host(cfg.seed, b, hk, lay.hkv, which, lo, p, lay.d)
+        hist[which] = fp8.dequantize(codes, sc[:, None])[:, None, :]
+    hs = slice(hk * G, (hk + 1) * G)
+    return oracle.decode_one(new["q"][b, hs], new["k"][b, hk:hk + 1], new["v"][b, hk:hk + 1], new["g"][b, hs],
+                             hist["k"], hist["v"], lo, L_b, group_layer(lay))
+
+
+@pytest.mark.parametrize("cfg", [wl.SPARK_DECODE_GLOBAL, wl.SPARK_DECODE_LOCAL], ids=lambda c: c.name + "_fp8")
+def test_decode_fullsize_fp8_sampled(cfg):
+    print(f"decode full size fp8 {cfg.name}", flush=True)
+    y, lengths, extra = _decode_run(cfg, fp8=True)
+    assert np.isfinite(y).all()
+    new = sd.new_token_host(cfg)
+    order = np.argsort(lengths)
+    G = cfg.layer.group
+    if cfg.layer.window:
+        pairs = [(b, hk) for b in range(cfg.batch) for hk in range(cfg.layer.hkv)]
+    else:
+        pairs = [(int(order[0]), 0), (int(order[0]), cfg.layer.hkv - 1), (int(order[1]), 5)]
+    worst = 0.0
+    t = time.time()
+    for b, hk in pairs:
+        ref = oracle_decode_pair_fp8(cfg, new, b, hk, int(lengths[b]), extra)
+        worst = max(worst, max_err(y[b, hk * G:(hk + 1) * G], ref))
+    print(f"{cfg.name} fp8: {len(pairs)} pairs max_abs_err={worst:.3e} (oracle {time.time() - t:.1f} s)",
+          flush=True)
     assert worst <= TOL

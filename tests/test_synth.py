@@ -31,3 +31,13 @@ def test_moments():
     assert abs(x.mean()) < 0.01
     assert abs(x.std() - 1) < 0.01
     assert abs(np.mean(x ** 4) - 2.9) < 0.1     # Irwin-Hall(12): kurtosis 3 - 0.1
+
+
+def test_e4m3_codes_numpy_and_torch_agree():
+    import torch
+    idx = np.arange(0, 200000, 7, dtype=np.int64)
+    a = synth.e4m3_codes(5, 33, idx)
+    b = synth.e4m3_codes_torch(5, 33, torch.from_numpy(idx)).numpy()
+    assert np.array_equal(a, b)
+    mag = a & 0x7F
+    assert mag.min() >= 0x20 and mag.max() <= 0x47 and 0.4 < (a >> 7).mean() < 0.6
