@@ -32,7 +32,9 @@ notes; the ones that matter here: the gate logits are an input tensor
 [B, T, Hq, D] (the projection W_G x is outside the layer's hot path); RoPE
 uses the positions given (prefill default 0..T-1); in decode the new token
 sits at position L - 1 where L counts it, and cached keys are taken exactly
-as stored (bf16, already normalized and rotated).
+as stored (bf16, already normalized and rotated).  A prefill chunk continuing
+a cached sequence reads its history the same way, and its own tokens sit at
+positions start .. start + T - 1.
 """
 from .attention import (  # noqa: F401
     layer_is_global,
@@ -52,5 +54,6 @@ from .attention import (  # noqa: F401
     sigmoid,
     prefill,
     decode_one,
+    prefill_chunk,
 )
 from . import fp8  # noqa: F401  (E4M3 cache codes)

@@ -225,3 +225,46 @@ def decode_one(q_new, k_new, v_new, gate, k_hist, v_hist, hist_start: int,
     for h in range(layer.hq):
         o[h] = w[h] @ vals[:, h // g, :]
     return output_epilogue(o, gate, layer)
+
+
+def prefill_chunk(q, k, v, gate, k_hist, v_hist, hist_start: int, start: int,
+                  layer, rows=None) -> np.ndarray:
+    """A chunk of T new tokens of one sequence whose first ``start``
+    positions are already cached (chunked prefill).
+
+    q, gate [T, Hq, D] and k, v [T, Hkv, D] are the chunk's raw projections
+    at positions start .. start + T - 1.  k_hist, v_hist [n, Hkv, D] are the
+    cached entries of positions hist_start .. hist_start + n - 1, taken
+    exactly as stored (keys already normalized and rotated, as decode reads
+    them).  Chunk token t at position P = start + t sees the positions in
+    visible_range(P, W): cached ones below ``start`` and the chunk's own from
+    ``start`` to P, whose keys get the prologue at their positions.  ``rows``
+    (chunk token indices) selects the output rows; q and gate then hold only
+    those rows.  Returns y [n_rows, Hq, D] in float64."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T = k.shape[0]
+    if rows is None:
+        rows = np.arange(T)
+    rows = np.asarray(rows, dtype=np.int64)
+    positions = start + np.arange(T, dtype=np.int64)
+    qh = query_prologue(q, positions[rows], layer)
+    kh_new = key_prologue(k, positions, layer)
+    k_hist = np.asarray(k_hist, dtype=np.float64)
+    v_hist = np.asarray(v_hist, dtype=np.float64)
+    g = layer.group
+    o = np.empty(np.shape(qh), dtype=np.float64)
+    for r, t in enumerate(rows):
+        lo, hi = visible_range(int(start + t), layer.window)
+        if lo < start and (lo < hist_start or hist_start + k_hist.shape[0] < start):
+            raise ValueError("history does not cover the visible range")
+        # keys and values of positions lo .. hi, cached ones first
+        a = lo - hist_start
+        c = start - hist_start
+        keys = np.concatenate([k_hist[a:c] if lo < start else k_hist[:0], kh_new[max(lo - start, 0):t + 1]])
+        vals = np.concatenate([v_hist[a:c] if lo < start else v_hist[:0], v[max(lo - start, 0):t + 1]])
+        w = softmax(logits_for_row(qh[r], keys, g), axis=-1)
+        for h in range(layer.hq):
+            o[r, h] = w[h] @ vals[:, h // g, :]
+    return output_epilogue(o, gate, layer)
+

@@ -511,3 +511,65 @@ def test_planted_mistakes_fail_the_library_pin(monkeypatch, mistake):
     y = A.prefill(q, k, v, g, layer, positions=pos)
     ref = torch_reference(q, k, v, g, layer, pos)
     assert not np.allclose(y, ref, rtol=0, atol=1e-6)
+
+
+# --------------------------------------------------------------------------
+# Chunked prefill: a chunk over a cached history is the tail of the whole
+# sequence's prefill
+# --------------------------------------------------------------------------
+
+CHUNK_LAYERS = [Layer(hq=8, hkv=2, d=16, window=6, theta=10000.0, scale=SPARK_SCALE, out_norm=True, out_eps=1e-6),
+                Layer(hq=8, hkv=2, d=16, window=0, theta=0.0, scale=GLIMMER_SCALE),
+                Layer(hq=6, hkv=3, d=32, window=5, theta=500000.0, scale=GLIMMER_SCALE)]
+
+
+@pytest.mark.parametrize("layer", CHUNK_LAYERS, ids=lambda l: f"hq{l.hq}kv{l.hkv}d{l.d}w{l.window}")
+@pytest.mark.parametrize("start", [0, 1, 5, 6, 13])
+def test_chunk_is_tail_of_whole_prefill(layer, start):
+    rng = np.random.default_rng(20 + start)
+    n = 23
+    q, k, v, g = _rand_layer_inputs(rng, n, layer)
+    full = oracle.prefill(q, k, v, g, layer)
+    _, kh = oracle.qk_prologue(q, k, np.arange(n), layer)
+    # history from position 0, and (local layers) only the window's part
+    hist_starts = [0] + ([max(0, start - layer.window + 1)] if layer.window else [])
+    for hs in hist_starts:
+        y = oracle.prefill_chunk(q[start:], k[start:], v[start:], g[start:], kh[hs:start], v[hs:start], hs, start,
+                                 layer)
+        assert np.allclose(y, full[start:], rtol=0, atol=1e-13)
+    rows = np.array([0, n - start - 1])
+    yr = oracle.prefill_chunk(q[start:][rows], k[start:], v[start:], g[start:][rows], kh[:start], v[:start], 0,
+                              start, layer, rows=rows)
+    assert np.array_equal(yr, oracle.prefill_chunk(q[start:], k[start:], v[start:], g[start:], kh[:start],
+                                                   v[:start], 0, start, layer)[rows])
+
+
+def test_chunk_rejects_short_history():
+    layer = CHUNK_LAYERS[0]
+    rng = np.random.default_rng(30)
+    q, k, v, g = _rand_layer_inputs(rng, 12, layer)
+    _, kh = oracle.qk_prologue(q, k, np.arange(12), layer)
+    with pytest.raises(ValueError):
+        oracle.prefill_chunk(q[8:], k[8:], v[8:], g[8:], kh[4:8], v[4:8], 4, 8, layer)   # needs position 3
+
+
+@pytest.mark.parametrize("mistake", ["positions_from_zero", "history_renormalized", "window_from_chunk_start"])
+def test_planted_chunk_mistakes_fail_the_tail_pin(monkeypatch, mistake):
+    import oracle.attention as A
+    layer = CHUNK_LAYERS[0]
+    rng = np.random.default_rng(31)
+    n, start = 20, 9
+    q, k, v, g = _rand_layer_inputs(rng, n, layer)
+    full = oracle.prefill(q, k, v, g, layer)
+    _, kh = oracle.qk_prologue(q, k, np.arange(n), layer)
+    kh_hist = kh[:start]
+    if mistake == "positions_from_zero":
+        orig = A.key_prologue
+        monkeypatch.setattr(A, "key_prologue", lambda x, pos, lyr: orig(x, np.asarray(pos) - start, lyr))
+    elif mistake == "history_renormalized":
+        kh_hist = A.rms_normalize(kh_hist, layer.qk_eps)
+    elif mistake == "window_from_chunk_start":
+        orig_vr = A.visible_range
+        monkeypatch.setattr(A, "visible_range", lambda i, w: (max(orig_vr(i, w)[0], start), i))
+    y = A.prefill_chunk(q[start:], k[start:], v[start:], g[start:], kh_hist, v[:start], 0, start, layer)
+    assert not np.allclose(y, full[start:], rtol=0, atol=1e-13)
