@@ -195,6 +195,45 @@ def prefill(layer: LayerParams, q, k, v, gate, positions=None, out=None, workspa
     return out
 
 
+def prefill_chunk_workspace_size(layer: LayerParams, batch: int, seq: int, max_start: int) -> int:
+    p = layer.c()
+    return int(_capi.load().muse_attn_prefill_chunk_workspace_size(ctypes.byref(p), batch, seq, max_start))
+
+
+def prefill_chunk(layer: LayerParams, q, k, v, gate, start, max_start: int, cache: KvCache, out=None,
+                  workspace=None):
+    """Chunked prefill: q, gate [B, T, Hq, D]; k, v [B, T, Hkv, D] (bf16) are the chunk's
+    projections at positions start[b] .. start[b] + T - 1 (start: device int32 [B], each
+    <= max_start).  Attends over the cached history and the chunk, writes the chunk's
+    keys and values into the cache, and returns out [B, T, Hq, D] bf16."""
+    torch = _torch()
+    lib = _capi.load()
+    B, T = int(q.shape[0]), int(q.shape[1])
+    _check_bf16("q", q, layer.num_q_heads, layer.head_dim)
+    _check_bf16("k", k, layer.num_kv_heads, layer.head_dim)
+    _check_bf16("v", v, layer.num_kv_heads, layer.head_dim)
+    _check_bf16("gate", gate, layer.num_q_heads, layer.head_dim)
+    for name, t in (("k", k), ("v", v), ("gate", gate)):
+        if int(t.shape[0]) != B or int(t.shape[1]) != T:
+            raise ValueError(f"{name} batch/sequence shape mismatch")
+    if start.dtype != torch.int32 or not start.is_cuda or start.numel() != B:
+        raise ValueError("start must be a device int32 tensor of B entries")
+    if out is None:
+        out = torch.empty((B, T, layer.num_q_heads, layer.head_dim), dtype=torch.bfloat16, device=q.device)
+    _check_bf16("out", out, layer.num_q_heads, layer.head_dim)
+    need = prefill_chunk_workspace_size(layer, B, T, max_start)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    strides = (ctypes.c_int64 * 10)(*[int(s) for t in (q, k, v, gate, out) for s in (t.stride(0), t.stride(1))])
+    p = layer.c()
+    c = cache.c()
+    _capi.check(lib.muse_attn_prefill_chunk(
+        ctypes.byref(p), B, T, q.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr(), strides,
+        start.contiguous().data_ptr(), int(max_start), ctypes.byref(c), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
+    return out
+
+
 def decode_workspace_size(layer: LayerParams, batch: int, max_kv_len: int, cache: KvCache) -> int:
     p = layer.c()
     c = cache.c()

@@ -1,5 +1,6 @@
 // C ABI: host-side argument checks, workspace sizing and kernel dispatch.
 // Every check runs before any launch; the library keeps no device state.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -106,6 +107,24 @@ PrefillWs prefill_ws_layout(const muse_attn_params* p, int32_t B, int32_t T) {
 
 size_t prefill_ws(const muse_attn_params* p, int32_t B, int32_t T) { return prefill_ws_layout(p, B, T).total; }
 
+// Chunked prefill: tiles per sequence cover slots 0 .. start - kbase + T - 1,
+// at most W - 1 + 63 slots of history on a local layer (the window's first
+// position rounded down to a tile) and max_start on a global one.
+int64_t chunk_tiles(const muse_attn_params* p, int32_t T, int32_t max_start) {
+  const int64_t W = p->sliding_window;
+  const int64_t hist = W > 0 ? std::min<int64_t>(max_start, W - 1 + kKeyTile - 1) : max_start;
+  return (hist + T + kKeyTile - 1) / kKeyTile;
+}
+
+PrefillWs chunk_ws_layout(const muse_attn_params* p, int32_t B, int32_t T, int32_t max_start) {
+  PrefillWs w;
+  w.tile_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * chunk_tiles(p, T, max_start) *
+                          tile_chunks(p->head_dim) * 16);
+  w.rope_bytes = p->rope_theta > 0.f ? align256(static_cast<size_t>(B) * T * (p->head_dim / 2) * 8) : 0;
+  w.total = w.tile_bytes + w.rope_bytes;
+  return w;
+}
+
 struct DecodePlan {
   int chunk_tokens;
   int max_chunks;
@@ -162,11 +181,52 @@ int32_t check_cache(const muse_attn_params* p, int32_t B, int32_t max_kv_len, co
   return MUSE_OK;
 }
 
+// {batch, token} strides of q, k, v, gate, out (elements): the caller's, or
+// those of contiguous [B, T, H, D] tensors; checked.
+int32_t layer_strides(const muse_attn_params* p, int32_t T, const int64_t* strides, int64_t* s) {
+  const int D = p->head_dim, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
+  if (strides) {
+    memcpy(s, strides, 10 * sizeof(int64_t));
+  } else {
+    const int64_t hs[5] = {static_cast<int64_t>(Hq) * D, static_cast<int64_t>(Hkv) * D,
+                           static_cast<int64_t>(Hkv) * D, static_cast<int64_t>(Hq) * D,
+                           static_cast<int64_t>(Hq) * D};
+    for (int i = 0; i < 5; ++i) {
+      s[2 * i + 1] = hs[i];
+      s[2 * i] = hs[i] * T;
+    }
+  }
+  const int heads_of[5] = {Hq, Hkv, Hkv, Hq, Hq};
+  for (int i = 0; i < 5; ++i) {
+    if (s[2 * i] % 8 || s[2 * i + 1] % 8 || s[2 * i] < 0 || s[2 * i + 1] < 0)
+      return fail(MUSE_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements");
+    if (s[2 * i + 1] < static_cast<int64_t>(heads_of[i]) * D)
+      return fail(MUSE_ERR_INVALID_ARG, "token stride of tensor %d smaller than H * D", i);
+  }
+  return 0;
+}
+
+CacheView cache_view(const muse_kv_cache* c) {
+  CacheView v{};
+  v.kind = c->kind;
+  v.capacity = c->capacity;
+  v.max_pages = c->max_pages_per_seq;
+  v.page_tokens = c->page_tokens;
+  v.num_pages = c->num_pages;
+  v.block_table = c->block_table;
+  v.k = c->k;
+  v.v = c->v;
+  v.fp8 = c->dtype == MUSE_DTYPE_FP8_E4M3 ? 1 : 0;
+  v.k_scale = c->k_scale;
+  v.v_scale = c->v_scale;
+  return v;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t muse_version(void) { return 101; }
+int32_t muse_version(void) { return 102; }
 
 const char* muse_last_error(void) { return g_err; }
 
@@ -246,24 +306,8 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
     return fail(MUSE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   const int D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
   int64_t s[10];
-  if (strides) {
-    memcpy(s, strides, sizeof(s));
-  } else {
-    const int64_t hs[5] = {static_cast<int64_t>(Hq) * D, static_cast<int64_t>(Hkv) * D,
-                           static_cast<int64_t>(Hkv) * D, static_cast<int64_t>(Hq) * D,
-                           static_cast<int64_t>(Hq) * D};
-    for (int i = 0; i < 5; ++i) {
-      s[2 * i + 1] = hs[i];
-      s[2 * i] = hs[i] * T;
-    }
-  }
-  const int heads_of[5] = {Hq, Hkv, Hkv, Hq, Hq};
-  for (int i = 0; i < 5; ++i) {
-    if (s[2 * i] % 8 || s[2 * i + 1] % 8 || s[2 * i] < 0 || s[2 * i + 1] < 0)
-      return fail(MUSE_ERR_INVALID_ARG, "strides must be non-negative multiples of 8 elements");
-    if (s[2 * i + 1] < static_cast<int64_t>(heads_of[i]) * D)
-      return fail(MUSE_ERR_INVALID_ARG, "token stride of tensor %d smaller than H * D", i);
-  }
+  rc = layer_strides(params, T, strides, s);
+  if (rc) return rc;
   if (!workspace || !aligned16(workspace)) return fail(MUSE_ERR_WORKSPACE, "workspace missing or misaligned");
   const size_t need = prefill_ws(params, B, T);
   if (ws_bytes < need)
@@ -351,6 +395,145 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
     e = hipEventRecord(g_prof_stop, st);
     if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   }
+  return ok();
+}
+
+size_t muse_attn_prefill_chunk_workspace_size(const muse_attn_params* params, int32_t B, int32_t T,
+                                              int32_t max_start) {
+  if (check_params(params) || B < 0 || T < 0 || max_start < 0) return 0;
+  return chunk_ws_layout(params, B, T, max_start).total;
+}
+
+int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32_t T, const void* q,
+                                const void* k, const void* v, const void* gate, const int64_t* strides,
+                                const int32_t* start, int32_t max_start, const muse_kv_cache* cache, void* out,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  int32_t rc = check_params(params);
+  if (rc) return rc;
+  if (B < 0 || T < 0) return fail(MUSE_ERR_INVALID_ARG, "B and T must be >= 0");
+  if (max_start < 0) return fail(MUSE_ERR_INVALID_ARG, "max_start must be >= 0");
+  if (static_cast<int64_t>(max_start) + T > 0x7fffffffLL)
+    return fail(MUSE_ERR_UNSUPPORTED, "max_start + T exceeds the 32-bit position range");
+  rc = check_cache(params, B, std::max(1, max_start + T), cache);
+  if (rc) return rc;
+  if (B == 0 || T == 0) return ok();
+  if (!q || !k || !v || !gate || !out || !start) return fail(MUSE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(out))
+    return fail(MUSE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const int D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
+  int64_t s[10];
+  rc = layer_strides(params, T, strides, s);
+  if (rc) return rc;
+  if (!workspace || !aligned16(workspace)) return fail(MUSE_ERR_WORKSPACE, "workspace missing or misaligned");
+  const PrefillWs wl = chunk_ws_layout(params, B, T, max_start);
+  if (ws_bytes < wl.total)
+    return fail(MUSE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, wl.total);
+  const int64_t n_tiles = chunk_tiles(params, T, max_start);
+  const int G = Hq / Hkv;
+  const int rows = prefill_rows_per_block(D, G);
+  const int bq = rows / G;
+  const int qgroup = prefill_qblock_group();
+  const int64_t nq = (static_cast<int64_t>(T) + bq - 1) / bq;
+  const int64_t nq_pad = ((nq + qgroup - 1) / qgroup) * qgroup;
+  if (nq_pad * B * Hkv > 0x7fffffffLL || n_tiles * Hkv > 0x7fffffffLL || B > 65535)
+    return fail(MUSE_ERR_UNSUPPORTED, "problem too large for one launch");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  u32x4* tiles = static_cast<u32x4*>(workspace);
+  float2* rope = wl.rope_bytes ? reinterpret_cast<float2*>(static_cast<char*>(workspace) + wl.tile_bytes) : nullptr;
+  const CacheView cv = cache_view(cache);
+  hipError_t e;
+  if (rope) {
+    RopeTableArgs ra{};
+    ra.start = start;
+    ra.max_start = max_start;
+    ra.T = T;
+    ra.n_rows = static_cast<int64_t>(B) * T;
+    ra.log2_theta = log2_theta(params);
+    ra.table = rope;
+    e = launch_rope_table(D, ra, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "rope table launch: %s", hipGetErrorString(e));
+  }
+
+  // 1. tile image: cached history (as stored) and the chunk's own keys/values
+  KvPrepArgs kp{};
+  kp.k = static_cast<const uint16_t*>(k);
+  kp.v = static_cast<const uint16_t*>(v);
+  kp.k_sb = s[2];
+  kp.k_st = s[3];
+  kp.v_sb = s[4];
+  kp.v_st = s[5];
+  kp.rope = rope;
+  kp.rope_batched = 1;
+  kp.T = T;
+  kp.Hkv = Hkv;
+  kp.n_tiles = static_cast<int>(n_tiles);
+  kp.eps = params->qk_norm_eps;
+  kp.tiles = tiles;
+  kp.start = start;
+  kp.max_start = max_start;
+  kp.W = params->sliding_window;
+  kp.cache = cv;
+  e = launch_kv_prep(D, B, kp, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "kv_prep launch: %s", hipGetErrorString(e));
+
+  // 2. attention over the tile image
+  PrefillArgs pa{};
+  pa.q = static_cast<const uint16_t*>(q);
+  pa.gate = static_cast<const uint16_t*>(gate);
+  pa.out = static_cast<uint16_t*>(out);
+  pa.tiles = tiles;
+  pa.q_sb = s[0];
+  pa.q_st = s[1];
+  pa.g_sb = s[6];
+  pa.g_st = s[7];
+  pa.o_sb = s[8];
+  pa.o_st = s[9];
+  pa.rope = rope;
+  pa.rope_batched = 1;
+  pa.T = T;
+  pa.Hkv = Hkv;
+  pa.W = params->sliding_window;
+  pa.n_tiles = static_cast<int>(n_tiles);
+  pa.n_qblocks = static_cast<int>(nq);
+  pa.n_qblocks_pad = static_cast<int>(nq_pad);
+  pa.batch_heads = B * Hkv;
+  pa.qscale = q_logit_scale(params);
+  pa.qk_eps = params->qk_norm_eps;
+  pa.out_norm = params->out_norm;
+  pa.out_eps = params->out_norm_eps;
+  pa.start = start;
+  pa.max_start = max_start;
+  if (g_prof_start) {
+    e = hipEventRecord(g_prof_start, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  }
+  e = launch_prefill(D, G, pa, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  if (g_prof_stop) {
+    e = hipEventRecord(g_prof_stop, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  }
+
+  // 3. the chunk's keys and values into the cache (after every read of it)
+  ChunkAppendArgs ca{};
+  ca.k = kp.k;
+  ca.v = kp.v;
+  ca.k_sb = s[2];
+  ca.k_st = s[3];
+  ca.v_sb = s[4];
+  ca.v_st = s[5];
+  ca.rope = rope;
+  ca.start = start;
+  ca.max_start = max_start;
+  ca.T = T;
+  ca.Hkv = Hkv;
+  ca.W = params->sliding_window;
+  ca.eps = params->qk_norm_eps;
+  ca.cache = cv;
+  e = launch_chunk_append(D, B, ca, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "chunk append launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -53,10 +53,41 @@ struct RopeQkArgs {
 // [rows][D/2] with rows = T (positions 0..T-1) or B * T (explicit positions).
 struct RopeTableArgs {
   const int32_t* positions;  // null: position = token index
+  const int32_t* start;      // chunked prefill: position of row b * T + t is start[b] + t
+  int max_start;             // start values outside [0, max_start] count as 0
   int T;
   int64_t n_rows;
   double log2_theta;
   float2* table;
+};
+
+// ---------------------------------------------------------------------------
+// Chunked prefill: a chunk of T tokens at positions start .. start + T - 1
+// continues a sequence whose first `start` positions are cached.  The tile
+// image of sequence b covers key slots s = position - kbase(start, W): local
+// layers start at the window's first position rounded down to a tile, global
+// layers at position 0.  Tiles stay aligned to positions, and query row t of
+// the chunk is key slot t + start - kbase.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int chunk_kbase(int start, int W) {
+  const int lo = start - W + 1;
+  return W > 0 && lo > 0 ? (lo / kKeyTile) * kKeyTile : 0;
+}
+__host__ __device__ inline bool chunk_start_ok(int start, int max_start) {
+  return start >= 0 && start <= max_start;
+}
+
+// A layer's KV cache as the kernels see it (element offsets are the same for
+// bf16 entries and E4M3 codes; the byte size differs).
+struct CacheView {
+  int kind, capacity, max_pages, page_tokens;
+  int64_t num_pages;
+  const int32_t* block_table;
+  void* k;
+  void* v;
+  int fp8;
+  const float* k_scale;  // fp8: [num_pages, Hkv] (paged) or [B, Hkv] (ring)
+  const float* v_scale;
 };
 
 struct KvPrepArgs {
@@ -68,6 +99,24 @@ struct KvPrepArgs {
   int T, Hkv, n_tiles;
   float eps;
   u32x4* tiles;        // [B * Hkv][n_tiles][TileLayout<D>::CHUNKS]
+  // chunked prefill (start != null): slot s of sequence b is position
+  // chunk_kbase(start[b], W) + s; cached positions come from `cache`
+  const int32_t* start;
+  int max_start, W;
+  CacheView cache;
+};
+
+// Writes a chunk's normalized (and rotated) keys and its values into the
+// cache: every position of a paged cache, the last min(T, W) of a ring.
+struct ChunkAppendArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_sb, k_st, v_sb, v_st;
+  const float2* rope;  // rows b * T + t, null on NoPE layers
+  const int32_t* start;
+  int max_start, T, Hkv, W;
+  float eps;
+  CacheView cache;
 };
 
 struct PrefillArgs {
@@ -83,6 +132,11 @@ struct PrefillArgs {
   float qk_eps;
   int out_norm;
   float out_eps;
+  // chunked prefill (null otherwise): query row t of sequence b is key slot
+  // t + start[b] - chunk_kbase(start[b], W); a start outside [0, max_start]
+  // gives zero output rows
+  const int32_t* start;
+  int max_start;
 };
 
 struct DecodeArgs {
@@ -117,6 +171,7 @@ struct DecodeArgs {
 hipError_t launch_rope_qknorm(int d, int out_dtype, const RopeQkArgs& a, hipStream_t st);
 hipError_t launch_rope_table(int d, const RopeTableArgs& a, hipStream_t st);
 hipError_t launch_kv_prep(int d, int B, const KvPrepArgs& a, hipStream_t st);
+hipError_t launch_chunk_append(int d, int B, const ChunkAppendArgs& a, hipStream_t st);
 hipError_t launch_prefill(int d, int g, const PrefillArgs& a, hipStream_t st);
 int prefill_rows_per_block(int d, int g);
 int prefill_qblock_group();

@@ -132,23 +132,33 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int b = bh / a.Hkv;
   const int hk = bh - b * a.Hkv;
   const int t0 = qb * C::BQ;
+  // Chunked prefill: query row t is key slot t + qoff of the tile image
+  // (0 for a whole-sequence prefill).  Every key index below is a slot.
+  int qoff = 0;
+  bool zero_out = false;
+  if (a.start) {
+    const int st = a.start[b];
+    zero_out = !chunk_start_ok(st, a.max_start);
+    qoff = zero_out ? 0 : st - chunk_kbase(st, a.W);
+  }
 
   int tq[MB];  // token of this lane's query column in each row block
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) tq[mb] = t0 + ((w * MB + mb) * 32 + l32) / G;
 
   // ---- key range: masked edge tiles and the unmasked middle ----
-  const int tlast = min(t0 + C::BQ, a.T) - 1;      // last real token of the block
-  const int klo = a.W > 0 ? max(0, t0 - a.W + 1) : 0;
+  const int q0 = t0 + qoff;                           // slot of the block's first query
+  const int tlast = min(t0 + C::BQ, a.T) - 1 + qoff;  // slot of its last real query
+  const int klo = a.W > 0 ? max(0, q0 - a.W + 1) : 0;
   const int tile_lo = klo / kKeyTile;
   const int tile_hi = tlast / kKeyTile;
-  // tiles fully visible to every token of the block: k0 + 63 <= t0 and k0 > tlast - W
+  // tiles fully visible to every token of the block: k0 + 63 <= q0 and k0 > tlast - W
   int mid_lo = tile_lo;
   if (a.W > 0) {
     const int first_full = tlast - a.W + 1;                 // need k0 >= first_full
     mid_lo = max(tile_lo, (max(first_full, 0) + kKeyTile - 1) / kKeyTile);
   }
-  const int mid_hi = min((t0 + 1) / kKeyTile, tile_hi + 1);  // need k0 + 63 <= t0
+  const int mid_hi = min((q0 + 1) / kKeyTile, tile_hi + 1);  // need k0 + 63 <= q0
   const int m_lo = min(mid_lo, mid_hi);
   const int m_hi = max(mid_hi, m_lo);
 
@@ -156,8 +166,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   int lo_t[MB], span[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    lo_t[mb] = a.W > 0 ? max(0, tq[mb] - a.W + 1) : 0;
-    span[mb] = tq[mb] - lo_t[mb];
+    const int qs = tq[mb] + qoff;
+    lo_t[mb] = a.W > 0 ? max(0, qs - a.W + 1) : 0;
+    span[mb] = qs - lo_t[mb];
   }
 
   const u32x4* tsrc = a.tiles + static_cast<int64_t>(bh) * a.n_tiles * TL::CHUNKS;
@@ -496,7 +507,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g[e]));
-        y[e] = (e < 4 ? v0[e] : v1[e - 4]) * sg;
+        y[e] = zero_out ? 0.f : (e < 4 ? v0[e] : v1[e - 4]) * sg;
       }
       u32x4 ow;
 #pragma unroll

@@ -148,6 +148,42 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T,
 
 size_t muse_attn_prefill_workspace_size(const muse_attn_params* params, int32_t B, int32_t T);
 
+/* muse_attn_prefill_chunk: chunked prefill.  Each of B sequences continues
+ * with a chunk of T new tokens after start[b] positions already held in a
+ * KV cache (the step beside decode that fills the caches decode reads:
+ * deep dive, section 7.2 on chunked prefill with KV reuse, and section 3.4
+ * for the window the ring keeps).
+ * Chunk token t of sequence b sits at position P = start[b] + t (RoPE angle
+ * and mask).  Its query sees the visible positions of section 3.4's mask:
+ * cached ones below start[b], read as stored (bf16, or E4M3 code times its
+ * scale), and the chunk's own keys from start[b] to P, normalized and
+ * rotated in fp32 like a whole-sequence prefill.  After the attention the
+ * call writes the chunk's keys (bf16, or the E4M3 code of key / scale) and
+ * values into the cache in place: a PAGED cache gets every position (its
+ * block table must map pages for positions up to start[b] + T - 1; entries
+ * outside [0, num_pages) are skipped and read as zeros), a RING the last
+ * min(T, W) positions at slot p mod W.
+ * q, gate: [B, T, Hq, D]; k, v: [B, T, Hkv, D]; out: [B, T, Hq, D]; bf16.
+ * strides: host int64[10] as for muse_attn_prefill, or NULL.
+ * start: device int32 [B]; each start[b] must lie in [0, max_start]: a
+ *   sequence outside that range gets zero output and no cache write.  On a
+ *   local layer the cache must hold positions max(0, start[b] - W + 1) ..
+ *   start[b] - 1, on a global layer 0 .. start[b] - 1.
+ * max_start: host bound on start (sizes the workspace); for a PAGED cache
+ *   max_start + T must not exceed max_pages_per_seq * page_tokens.
+ * cache: as for muse_attn_decode (a RING needs capacity == W).
+ * workspace: at least muse_attn_prefill_chunk_workspace_size() bytes; it
+ *   holds a tile image of every sequence's visible history plus the chunk.
+ * T == 0 or B == 0 is a no-op. */
+int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32_t T,
+                                const void* q, const void* k, const void* v, const void* gate,
+                                const int64_t* strides, const int32_t* start, int32_t max_start,
+                                const muse_kv_cache* cache, void* out,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+size_t muse_attn_prefill_chunk_workspace_size(const muse_attn_params* params, int32_t B, int32_t T,
+                                              int32_t max_start);
+
 /* muse_attn_decode: one new token per sequence against a KV cache.
  * q_new, gate, out: [B, Hq, D]; k_new, v_new: [B, Hkv, D]; contiguous bf16.
  * kv_len: device int32 [B], the sequence length INCLUDING the new token;
@@ -179,10 +215,10 @@ int32_t muse_layer_is_global(int32_t layer_index, int32_t n_layers);
 /* Message of the last failed call on this thread ("" if none). */
 const char* muse_last_error(void);
 
-/* Profiling aid: on the calling thread, make the next muse_attn_prefill /
- * muse_attn_decode calls record `start` (a hipEvent_t) on their stream just
- * before their main attention kernel (the prefill attention kernel; the decode
- * split kernel) and `stop` just after it, so a caller can time that kernel
+/* Profiling aid: on the calling thread, make the next muse_attn_prefill,
+ * muse_attn_prefill_chunk and muse_attn_decode calls record `start` (a
+ * hipEvent_t) on their stream just before their main attention kernel (the
+ * prefill attention kernel; the decode split kernel) and `stop` just after it, so a caller can time that kernel
  * with hipEventElapsedTime.  Pass NULL, NULL to turn it off.  Nothing is
  * recorded by muse_rope_qknorm.  Returns MUSE_OK, or MUSE_ERR_INVALID_ARG if
  * exactly one of the two is NULL. */
