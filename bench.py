@@ -138,6 +138,35 @@ def prefill_case(cfg, steps, warmup, events, torch, ma, keep=False):
     return res
 
 
+def chunk_case(cfg, steps, warmup, events, torch, ma):
+    """Chunked prefill: the chunk after `start` cached positions.  Each step
+    rewrites the chunk's own cache entries with the same values, so every
+    step sees the same cache."""
+    from synth.device import chunk_device_setup
+    from global_muse_rope_amd import accounting as acc
+    L = cfg.layer
+    lp = ma.LayerParams.from_layer(L)
+    s = chunk_device_setup(cfg)
+    if s["kind"] == "ring":
+        cache = ma.KvCache.ring(s["kc"], s["vc"])
+    else:
+        cache = ma.KvCache.paged(s["kc"], s["vc"], s["block_table"], s["page_tokens"])
+    out = torch.empty((cfg.batch, cfg.seq, L.hq, L.d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(ma.prefill_chunk_workspace_size(lp, cfg.batch, cfg.seq, cfg.start), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        ma.prefill_chunk(lp, s["q"], s["k"], s["v"], s["g"], s["start"], cfg.start, cache, out=out, workspace=ws)
+
+    wall, kern = timed_steps(step, steps, warmup, events, torch)
+    flops = acc.flops_per_pair(L.hq, L.d) * cfg.batch * acc.chunk_pairs(cfg.start, cfg.seq, L.window)
+    res = {"ms_per_step": wall, "tflops": flops / (wall * 1e-3) / 1e12, "kernel_ms": kern,
+           "kernel_tflops": flops / (kern * 1e-3) / 1e12, "flops": flops}
+    del s, cache, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False):
     from synth.device import decode_device_setup
     from global_muse_rope_amd import accounting as acc
@@ -303,9 +332,15 @@ def only_case(name, steps, warmup, torch, ma):
     """Time one workload by itself (for a per-workload kernel trace)."""
     from synth import workloads as wl
     fp8 = name.endswith("_fp8")
-    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE}[name[:-4] if fp8 else name]
+    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE + wl.CHUNK}[name[:-4] if fp8 else name]
     events = HipEvents()
-    if cfg in wl.DECODE:
+    if cfg in wl.CHUNK:
+        r = chunk_case(cfg, steps, warmup, events, torch, ma)
+        print(json.dumps({"workload": name, "kernel": "prefill_kernel", "kernel_ms": round(r["kernel_ms"], 4),
+                          "kernel_TFLOP/s": round(r["kernel_tflops"], 2), "step_TFLOP/s": round(r["tflops"], 2),
+                          "ms_per_step": round(r["ms_per_step"], 4), "steps": steps, "warmup": warmup}),
+              flush=True)
+    elif cfg in wl.DECODE:
         r = decode_case(cfg, steps, warmup, events, torch, ma, flush=cfg.layer.window > 0, fp8=fp8)
         print(json.dumps({"workload": name, "kernel": "decode_split_kernel", "kernel_ms": round(r["kernel_ms"], 4),
                           "GB/s": round(r["gbs"], 1), "ms_per_step": round(r["ms_per_step"], 4),
@@ -415,6 +450,18 @@ def main():
                                       "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
                                       "frac_of_copy": round(r["gbs"] / copy_gbs, 4)}}
         result["decode"] = dec
+
+    if not args.no_decode:
+        chunks = {}
+        for ccfg in wl.CHUNK:
+            log(f"prefill chunk {ccfg.name}")
+            r = chunk_case(ccfg, 5, 1, events, torch, ma)
+            log(f"  {r['tflops']:.1f} TFLOP/s step, kernel {r['kernel_tflops']:.1f} TFLOP/s")
+            chunks[ccfg.name] = {"tflops_step": round(r["tflops"], 2), "ms_per_step": round(r["ms_per_step"], 4),
+                                 "kernel_tflops": round(r["kernel_tflops"], 2),
+                                 "kernel_ms": round(r["kernel_ms"], 4),
+                                 "frac_of_mfma_peak": round(r["kernel_tflops"] / MFMA_PEAK_TFLOPS, 4)}
+        result["prefill_chunk"] = chunks
 
     if not args.quick:
         other = {}

@@ -29,6 +29,12 @@ def prefill_flops(hq: int, d: int, batch: int, seq: int, window: int) -> int:
     return flops_per_pair(hq, d) * batch * visible_pairs(seq, window)
 
 
+def chunk_pairs(start: int, seq: int, window: int) -> int:
+    """Visible (query, key) pairs of a chunk of `seq` tokens at positions
+    start .. start + seq - 1: the tail of the whole sequence's pairs."""
+    return visible_pairs(start + seq, window) - visible_pairs(start, window)
+
+
 def kv_bytes_per_token(hkv: int, d: int, elem_bytes: int = 2) -> int:
     return 2 * hkv * d * elem_bytes
 

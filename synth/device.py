@@ -195,3 +195,66 @@ def decode_device_setup(cfg, device="cuda", lengths=None, fp8=False):
     res.update(kind="paged", kc=kc, vc=vc, block_table=tdev, page_tokens=pt, table_host=table)
     put_scales((n_pool, hkv))
     return res
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill
+# ---------------------------------------------------------------------------
+
+def chunk_device_setup(cfg, device="cuda"):
+    """A chunk workload: the chunk's q, k, v, g [B, T, H, D] (prefill streams,
+    seed + 5) and a cache holding positions 0 .. start - 1 of every sequence
+    (cache streams, the decode recipe): a ring (local layer) keeps the last W,
+    a paged cache maps pages for start + T positions from a seeded
+    permutation.  Returns a dict of tensors plus kind, page_tokens and (paged)
+    table_host."""
+    import torch
+    L = cfg.layer
+    d, hkv, B, T, S = L.d, L.hkv, cfg.batch, cfg.seq, cfg.start
+    res = {n: normal_bf16_torch_tensor(cfg.seed + 5, STREAM[n], shp, device)
+           for n, shp in [("q", (B, T, L.hq, d)), ("k", (B, T, hkv, d)), ("v", (B, T, hkv, d)),
+                          ("g", (B, T, L.hq, d))]}
+    res["start"] = torch.full((B,), S, dtype=torch.int32, device=device)
+    if L.window > 0:
+        W = L.window
+        kc = torch.zeros((B, hkv, W, d), dtype=torch.bfloat16, device=device)
+        vc = torch.zeros((B, hkv, d, W), dtype=torch.bfloat16, device=device)
+        p0 = max(0, S - W)
+        slots = torch.arange(p0, S, device=device) % W
+        for b in range(B):
+            for h in range(hkv):
+                kc[b, h, slots, :] = cache_values_torch(cfg.seed, b, h, hkv, "k", p0, S, d, device)
+                vc[b, h, :, slots] = cache_values_torch(cfg.seed, b, h, hkv, "v", p0, S, d, device).t()
+        res.update(kind="ring", kc=kc, vc=vc, block_table=None, page_tokens=0)
+        return res
+    pt = cfg.page_tokens
+    pages = (S + T + pt - 1) // pt
+    n_pool = B * pages
+    table = np.random.default_rng(cfg.seed + 2).permutation(n_pool).astype(np.int32).reshape(B, pages)
+    kc = torch.zeros((n_pool, hkv, pt, d), dtype=torch.bfloat16, device=device)
+    vc = torch.zeros((n_pool, hkv, d, pt), dtype=torch.bfloat16, device=device)
+    tdev = torch.from_numpy(table).to(device)
+    hp = (S + pt - 1) // pt
+    for b in range(B):
+        idxp = tdev[b, :hp].long()
+        for h in range(hkv):
+            for which, dst in (("k", kc), ("v", vc)):
+                vals = torch.zeros((hp * pt, d), dtype=torch.bfloat16, device=device)
+                vals[:S] = cache_values_torch(cfg.seed, b, h, hkv, which, 0, S, d, device)
+                vals = vals.view(hp, pt, d)
+                dst[idxp, h] = vals if which == "k" else vals.transpose(1, 2)
+    res.update(kind="paged", kc=kc, vc=vc, block_table=tdev, page_tokens=pt, table_host=table)
+    return res
+
+
+def chunk_host_rows(cfg, name, b, rows, heads=None):
+    """float64 values of the chunk tensor `name` (q, k, v or g) at sequence
+    b, chunk rows `rows`, heads `heads`."""
+    L = cfg.layer
+    H = L.hq if name in ("q", "g") else L.hkv
+    rows = np.asarray(rows, dtype=np.int64)
+    heads = np.arange(H) if heads is None else np.asarray(heads, dtype=np.int64)
+    idx = (((b * cfg.seq + rows[:, None, None]) * H + heads[None, :, None]) * L.d
+           + np.arange(L.d)[None, None, :])
+    return bf16_bits_to_f64(f32_to_bf16_bits(normal_f32(cfg.seed + 5, STREAM[name], idx)))
+

@@ -84,6 +84,24 @@ PREFILL = [TINY_LOCAL, TINY_GLOBAL, GLIMMER_LOCAL, GLIMMER_GLOBAL, SPARK_LOCAL, 
 DECODE = [SPARK_DECODE_GLOBAL, SPARK_DECODE_LOCAL]
 
 
+@dataclass(frozen=True)
+class Chunk:
+    """Chunked prefill: `seq` new tokens per sequence after `start` cached
+    positions (paged cache on global layers, ring on local ones)."""
+    name: str
+    layer: Layer
+    batch: int
+    seq: int
+    start: int
+    page_tokens: int = 32
+    seed: int = 0
+
+
+SPARK_CHUNK_GLOBAL = Chunk("spark_global_chunk_2k_at_128k", spark(0, 0.0), 1, 2048, 131072)
+SPARK_CHUNK_LOCAL = Chunk("spark_local_chunk_2k_at_128k", spark(2048, 10000.0), 1, 2048, 131072)
+CHUNK = [SPARK_CHUNK_GLOBAL, SPARK_CHUNK_LOCAL]
+
+
 def decode_lengths(seed: int, batch: int, lo: int, hi: int):
     """KV lengths (new token included), integers uniform in [lo, hi]."""
     import numpy as np

@@ -227,3 +227,52 @@ def test_decode_fullsize_fp8_sampled(cfg):
     print(f"{cfg.name} fp8: {len(pairs)} pairs max_abs_err={worst:.3e} (oracle {time.time() - t:.1f} s)",
           flush=True)
     assert worst <= TOL
+
+
+@pytest.mark.parametrize("cfg", wl.CHUNK, ids=lambda c: c.name)
+def test_prefill_chunk_fullsize_sampled(cfg):
+    """A 2048-token chunk after 131072 cached positions: sampled rows of two
+    KV-head groups against the oracle over the whole visible history, and
+    the appended values in the cache."""
+    L = cfg.layer
+    G = L.group
+    print(f"chunk full size {cfg.name}", flush=True)
+    s = sd.chunk_device_setup(cfg)
+    if s["kind"] == "ring":
+        cache = ma.KvCache.ring(s["kc"], s["vc"])
+    else:
+        cache = ma.KvCache.paged(s["kc"], s["vc"], s["block_table"], s["page_tokens"])
+    lp = ma.LayerParams.from_layer(L)
+    y = ma.prefill_chunk(lp, s["q"], s["k"], s["v"], s["g"], s["start"], cfg.start, cache)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    y = y.float().cpu().numpy()
+    S, T = cfg.start, cfg.seq
+    rows = sample_rows(T, 0, n_random=6)
+    worst = 0.0
+    t = time.time()
+    for hk in sorted({0, L.hkv - 1}):
+        heads = np.arange(hk * G, (hk + 1) * G)
+        hs = max(0, S - L.window + 1) if L.window else 0
+        k_hist = sd.cache_values_host(cfg.seed, 0, hk, L.hkv, "k", hs, S, L.d)[:, None, :]
+        v_hist = sd.cache_values_host(cfg.seed, 0, hk, L.hkv, "v", hs, S, L.d)[:, None, :]
+        kc = sd.chunk_host_rows(cfg, "k", 0, np.arange(T), [hk])
+        vch = sd.chunk_host_rows(cfg, "v", 0, np.arange(T), [hk])
+        q = sd.chunk_host_rows(cfg, "q", 0, rows, heads)
+        g = sd.chunk_host_rows(cfg, "g", 0, rows, heads)
+        ref = oracle.prefill_chunk(q, kc, vch, g, k_hist, v_hist, hs, S, group_layer(L), rows=rows)
+        worst = max(worst, max_err(y[0][rows][:, heads], ref))
+        # the chunk's values were appended (exact copies)
+        for r in rows:
+            p = S + r
+            if s["kind"] == "ring":
+                if r < T - L.window:
+                    continue
+                got = s["vc"][0, hk, :, p % L.window]
+            else:
+                pt = s["page_tokens"]
+                got = s["vc"][int(s["table_host"][0, p // pt]), hk, :, p % pt]
+            assert np.array_equal(got.float().cpu().numpy(), vch[r, 0])
+    print(f"{cfg.name}: {len(rows)} rows x {2 * G} heads, max_abs_err={worst:.3e} (oracle {time.time() - t:.1f} s)",
+          flush=True)
+    assert worst <= TOL
