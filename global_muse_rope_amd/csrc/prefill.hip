@@ -54,6 +54,30 @@ constexpr int kFragQueueD64 = MUSE_PREFILL_QD_D64;
 // their maxima)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// One wave's 64 x 16-byte copy from global memory straight into LDS
+// (global_load_lds_dwordx4; the LDS address comes from M0, uniform over the
+// wave).  The copy is counted by VM_CNT alone: the kernel waits for it with
+// an explicit vmcnt(0) before the barrier that publishes the tile.  Issued
+// through the builtin, the compiler treats it as a flat access that may
+// also touch LDS and, while one is in flight, turns every wait on an LDS
+// fragment read into lgkmcnt(0), draining the fragment queue twice per
+// half-tile.  Written as an instruction of its own the compiler keeps its
+// exact lgkmcnt(7) waits; the statement has no register outputs, and its
+// memory clobber keeps LDS accesses from moving across it.
+#ifndef MUSE_PREFILL_ASM_DMA
+#define MUSE_PREFILL_ASM_DMA 1
+#endif
+__device__ __forceinline__ void dma16_to_lds(const u32x4* src, void* lds_wave_base) {
+#if MUSE_PREFILL_ASM_DMA
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
+#else
+  copy16_to_lds(src, lds_wave_base);
+#endif
+}
+
 template <int D, int G, int NW, int MB>
 struct PrefillCfg {
   static constexpr int ROWS = NW * MB * 32;
@@ -194,7 +218,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     const u32x4* src = tsrc + static_cast<int64_t>(tile) * TL::CHUNKS;
 #pragma unroll
     for (int c = 0; c < TL::CHUNKS; c += C::THREADS)
-      if (c + w * 64 < TL::CHUNKS) copy16_to_lds(src + c + w * 64 + lane, &smem[buf][c + w * 64]);
+      if (c + w * 64 < TL::CHUNKS) dma16_to_lds(src + c + w * 64 + lane, &smem[buf][c + w * 64]);
   };
   // The first three tiles of the range start streaming into LDS before the
   // query prologue, so their latency overlaps the query loads.
@@ -400,7 +424,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) pp[mb][st][e] = static_cast<bf16_t>(0.0f);
 
-  // tiles 0, 1 and 2 of the range are resident after this barrier
+  // tiles 0, 1 and 2 of the range are resident after this barrier (the
+  // explicit wait covers their copies)
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
   // S(first tile, 0..31); the "previous" P is zero, so this PV adds nothing
