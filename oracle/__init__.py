@@ -34,7 +34,8 @@ uses the positions given (prefill default 0..T-1); in decode the new token
 sits at position L - 1 where L counts it, and cached keys are taken exactly
 as stored (bf16, already normalized and rotated).  A prefill chunk continuing
 a cached sequence reads its history the same way, and its own tokens sit at
-positions start .. start + T - 1.
+positions start .. start + T - 1; a drafter's non-causal block sees the same
+history and every block key within the window in both directions.
 """
 from .attention import (  # noqa: F401
     layer_is_global,
@@ -55,5 +56,6 @@ from .attention import (  # noqa: F401
     prefill,
     decode_one,
     prefill_chunk,
+    block_bidirectional,
 )
 from . import fp8  # noqa: F401  (E4M3 cache codes)

@@ -268,3 +268,46 @@ def prefill_chunk(q, k, v, gate, k_hist, v_hist, hist_start: int, start: int,
             o[r, h] = w[h] @ vals[:, h // g, :]
     return output_epilogue(o, gate, layer)
 
+
+def block_bidirectional(q, k, v, gate, k_hist, v_hist, hist_start: int, start: int,
+                        layer, rows=None) -> np.ndarray:
+    """Non-causal block attention of a block-diffusion drafter (deep dive,
+    section 8.2, step 4): the T block tokens at positions start .. start +
+    T - 1 are the queries; keys and values are the cached context entries
+    below ``start`` (taken as stored) followed by the block's own keys and
+    values (prologue at their positions).  No causal mask: key position j is
+    visible to query position P iff |P - j| < W on a layer with window W
+    (both directions), and always on a layer with W = 0; keys exist only up
+    to the block's last position.
+
+    Arguments as for prefill_chunk; the history must reach back to
+    start + t - W + 1 for every row t.  Returns y [n_rows, Hq, D]."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T = k.shape[0]
+    if rows is None:
+        rows = np.arange(T)
+    rows = np.asarray(rows, dtype=np.int64)
+    positions = start + np.arange(T, dtype=np.int64)
+    qh = query_prologue(q, positions[rows], layer)
+    kh_new = key_prologue(k, positions, layer)
+    k_hist = np.asarray(k_hist, dtype=np.float64)
+    v_hist = np.asarray(v_hist, dtype=np.float64)
+    last = start + T - 1
+    g = layer.group
+    o = np.empty(np.shape(qh), dtype=np.float64)
+    for r, t in enumerate(rows):
+        p = int(start + t)
+        lo = 0 if layer.window == 0 else max(0, p - layer.window + 1)
+        hi = last if layer.window == 0 else min(last, p + layer.window - 1)
+        if lo < start and (lo < hist_start or hist_start + k_hist.shape[0] < start):
+            raise ValueError("history does not cover the visible range")
+        a = lo - hist_start
+        c = start - hist_start
+        keys = np.concatenate([k_hist[a:c] if lo < start else k_hist[:0], kh_new[max(lo - start, 0):hi - start + 1]])
+        vals = np.concatenate([v_hist[a:c] if lo < start else v_hist[:0], v[max(lo - start, 0):hi - start + 1]])
+        w = softmax(logits_for_row(qh[r], keys, g), axis=-1)
+        for h in range(layer.hq):
+            o[r, h] = w[h] @ vals[:, h // g, :]
+    return output_epilogue(o, gate, layer)
+

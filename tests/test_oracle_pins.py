@@ -573,3 +573,111 @@ def test_planted_chunk_mistakes_fail_the_tail_pin(monkeypatch, mistake):
         monkeypatch.setattr(A, "visible_range", lambda i, w: (max(orig_vr(i, w)[0], start), i))
     y = A.prefill_chunk(q[start:], k[start:], v[start:], g[start:], kh_hist, v[:start], 0, start, layer)
     assert not np.allclose(y, full[start:], rtol=0, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Non-causal block attention (block-diffusion drafter)
+# --------------------------------------------------------------------------
+
+def torch_block_reference(q, k, v, g, k_hist, v_hist, start, layer):
+    """Independent formulation: PyTorch rms_norm, complex RoPE and SDPA with an
+    explicit |i - j| < W mask over the concatenated [history; block] keys."""
+    import torch
+    F = torch.nn.functional
+    d = q.shape[-1]
+    T = q.shape[0]
+    hs = start - k_hist.shape[0]
+    pos_q = torch.arange(start, start + T, dtype=torch.float64)
+    qh = F.rms_norm(torch.from_numpy(q).double(), (d,), eps=layer.qk_eps) * layer.scale
+    kh = F.rms_norm(torch.from_numpy(k).double(), (d,), eps=layer.qk_eps)
+    if layer.theta:
+        h = d // 2
+        freqs = torch.tensor(layer.theta, dtype=torch.float64) ** (-torch.arange(h, dtype=torch.float64) * 2 / d)
+        rot = torch.polar(torch.ones(T, h, dtype=torch.float64), pos_q[:, None] * freqs[None, :])[:, None, :]
+
+        def apply(x):
+            z = torch.complex(x[..., :h], x[..., h:]) * rot
+            return torch.cat([z.real, z.imag], dim=-1)
+        qh, kh = apply(qh), apply(kh)
+    keys = torch.cat([torch.from_numpy(k_hist).double(), kh])
+    vals = torch.cat([torch.from_numpy(v_hist).double(), torch.from_numpy(v).double()])
+    i = pos_q[:, None]
+    j = torch.arange(hs, start + T, dtype=torch.float64)[None, :]
+    mask = torch.ones(T, keys.shape[0], dtype=torch.bool)
+    if layer.window:
+        mask = (i - j).abs() < layer.window
+    o = F.scaled_dot_product_attention(qh.transpose(0, 1)[None], keys.transpose(0, 1)[None],
+                                       vals.transpose(0, 1)[None], attn_mask=mask, enable_gqa=True)[0].transpose(0, 1)
+    if layer.out_norm:
+        o = F.rms_norm(o, (d,), eps=layer.out_eps)
+    return (o * torch.sigmoid(torch.from_numpy(g).double())).numpy()
+
+
+@pytest.mark.parametrize("layer", CHUNK_LAYERS, ids=lambda l: f"hq{l.hq}kv{l.hkv}d{l.d}w{l.window}")
+@pytest.mark.parametrize("start,T", [(0, 7), (9, 4), (20, 6)])
+def test_block_matches_library_formulation(layer, start, T):
+    rng = np.random.default_rng(40 + start)
+    q, k, v, g = _rand_layer_inputs(rng, T, layer)
+    hs = max(0, start - layer.window + 1) if layer.window else 0
+    k_hist = rng.standard_normal((start - hs, layer.hkv, layer.d))
+    v_hist = rng.standard_normal((start - hs, layer.hkv, layer.d))
+    y = oracle.block_bidirectional(q, k, v, g, k_hist, v_hist, hs, start, layer)
+    ref = torch_block_reference(q, k, v, g, k_hist, v_hist, start, layer)
+    assert np.allclose(y, ref, rtol=0, atol=1e-12)
+
+
+def test_block_last_row_equals_causal_chunk_and_single_token_equals_decode():
+    """The block's last row sees exactly what a causal chunk's last row sees;
+    a one-token block is a decode step over the same history."""
+    rng = np.random.default_rng(50)
+    for layer in CHUNK_LAYERS:
+        n, start = 18, 11
+        q, k, v, g = _rand_layer_inputs(rng, n, layer)
+        _, kh = oracle.qk_prologue(q, k, np.arange(n), layer)
+        yb = oracle.block_bidirectional(q[start:], k[start:], v[start:], g[start:], kh[:start], v[:start], 0, start,
+                                        layer)
+        yc = oracle.prefill_chunk(q[start:], k[start:], v[start:], g[start:], kh[:start], v[:start], 0, start, layer)
+        assert np.allclose(yb[-1], yc[-1], rtol=0, atol=1e-13)
+        y1 = oracle.block_bidirectional(q[start:start + 1], k[start:start + 1], v[start:start + 1],
+                                        g[start:start + 1], kh[:start], v[:start], 0, start, layer)
+        yd = oracle.decode_one(q[start], k[start], v[start], g[start], kh[:start], v[:start], 0, start + 1, layer)
+        assert np.allclose(y1[0], yd, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("mistake", ["causal", "one_sided_window"])
+def test_planted_block_mistakes_fail_the_library_pin(mistake):
+    """A causal mask, or a window without its forward edge, in place of the
+    bidirectional window fails the library pin."""
+    layer = CHUNK_LAYERS[0]                    # W = 6
+    rng = np.random.default_rng(51)
+    start, T = 9, 8                            # T > W: the forward window edge matters
+    q, k, v, g = _rand_layer_inputs(rng, T, layer)
+    hs = start - layer.window + 1
+    k_hist = rng.standard_normal((start - hs, layer.hkv, layer.d))
+    v_hist = rng.standard_normal((start - hs, layer.hkv, layer.d))
+    ref = torch_block_reference(q, k, v, g, k_hist, v_hist, start, layer)
+    assert np.allclose(oracle.block_bidirectional(q, k, v, g, k_hist, v_hist, hs, start, layer), ref,
+                       rtol=0, atol=1e-12)
+    if mistake == "causal":
+        y = oracle.prefill_chunk(q, k, v, g, k_hist, v_hist, hs, start, layer)
+    else:
+        y = _block_one_sided(q, k, v, g, k_hist, v_hist, hs, start, layer)
+    assert not np.allclose(y, ref, rtol=0, atol=1e-12)
+
+
+def _block_one_sided(q, k, v, g, k_hist, v_hist, hs, start, layer):
+    """The block attention with the forward window edge dropped (every later
+    block key visible even beyond W): a plausible slip."""
+    T = k.shape[0]
+    pos = start + np.arange(T)
+    qh = oracle.query_prologue(q, pos, layer)
+    kh = oracle.key_prologue(k, pos, layer)
+    keys = np.concatenate([k_hist, kh])
+    vals = np.concatenate([v_hist, v])
+    o = np.empty_like(qh)
+    for t in range(T):
+        lo = max(0, start + t - layer.window + 1) - hs
+        w = oracle.softmax(oracle.logits_for_row(qh[t], keys[lo:], layer.group), axis=-1)
+        for h in range(layer.hq):
+            o[t, h] = w[h] @ vals[lo:, h // layer.group, :]
+    return oracle.output_epilogue(o, g, layer)
