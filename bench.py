@@ -138,7 +138,7 @@ def prefill_case(cfg, steps, warmup, events, torch, ma, keep=False):
     return res
 
 
-def chunk_case(cfg, steps, warmup, events, torch, ma):
+def chunk_case(cfg, steps, warmup, events, torch, ma, draft=False):
     """Chunked prefill: the chunk after `start` cached positions.  Each step
     rewrites the chunk's own cache entries with the same values, so every
     step sees the same cache."""
@@ -155,11 +155,14 @@ def chunk_case(cfg, steps, warmup, events, torch, ma):
     ws = torch.empty(ma.prefill_chunk_workspace_size(lp, cfg.batch, cfg.seq, cfg.start), dtype=torch.uint8,
                      device="cuda")
 
+    fn = ma.draft_block if draft else ma.prefill_chunk
+
     def step():
-        ma.prefill_chunk(lp, s["q"], s["k"], s["v"], s["g"], s["start"], cfg.start, cache, out=out, workspace=ws)
+        fn(lp, s["q"], s["k"], s["v"], s["g"], s["start"], cfg.start, cache, out=out, workspace=ws)
 
     wall, kern = timed_steps(step, steps, warmup, events, torch)
-    flops = acc.flops_per_pair(L.hq, L.d) * cfg.batch * acc.chunk_pairs(cfg.start, cfg.seq, L.window)
+    pairs = (acc.block_pairs if draft else acc.chunk_pairs)(cfg.start, cfg.seq, L.window)
+    flops = acc.flops_per_pair(L.hq, L.d) * cfg.batch * pairs
     res = {"ms_per_step": wall, "tflops": flops / (wall * 1e-3) / 1e12, "kernel_ms": kern,
            "kernel_tflops": flops / (kern * 1e-3) / 1e12, "flops": flops}
     del s, cache, out, ws
@@ -332,10 +335,10 @@ def only_case(name, steps, warmup, torch, ma):
     """Time one workload by itself (for a per-workload kernel trace)."""
     from synth import workloads as wl
     fp8 = name.endswith("_fp8")
-    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE + wl.CHUNK}[name[:-4] if fp8 else name]
+    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE + wl.CHUNK + wl.DRAFT}[name[:-4] if fp8 else name]
     events = HipEvents()
-    if cfg in wl.CHUNK:
-        r = chunk_case(cfg, steps, warmup, events, torch, ma)
+    if cfg in wl.CHUNK or cfg in wl.DRAFT:
+        r = chunk_case(cfg, steps, warmup, events, torch, ma, draft=cfg in wl.DRAFT)
         print(json.dumps({"workload": name, "kernel": "prefill_kernel", "kernel_ms": round(r["kernel_ms"], 4),
                           "kernel_TFLOP/s": round(r["kernel_tflops"], 2), "step_TFLOP/s": round(r["tflops"], 2),
                           "ms_per_step": round(r["ms_per_step"], 4), "steps": steps, "warmup": warmup}),
@@ -462,6 +465,15 @@ def main():
                                  "kernel_ms": round(r["kernel_ms"], 4),
                                  "frac_of_mfma_peak": round(r["kernel_tflops"] / MFMA_PEAK_TFLOPS, 4)}
         result["prefill_chunk"] = chunks
+        draft = {}
+        for bcfg in wl.DRAFT:
+            log(f"draft block {bcfg.name}")
+            r = chunk_case(bcfg, 20, 3, events, torch, ma, draft=True)
+            log(f"  {r['ms_per_step'] * 1e3:.1f} us per step, kernel {r['kernel_tflops']:.1f} TFLOP/s")
+            draft[bcfg.name] = {"us_per_step": round(r["ms_per_step"] * 1e3, 2),
+                                "kernel_us": round(r["kernel_ms"] * 1e3, 2),
+                                "tflops_step": round(r["tflops"], 2), "kernel_tflops": round(r["kernel_tflops"], 2)}
+        result["draft_block"] = draft
 
     if not args.quick:
         other = {}

@@ -206,6 +206,24 @@ def prefill_chunk(layer: LayerParams, q, k, v, gate, start, max_start: int, cach
     projections at positions start[b] .. start[b] + T - 1 (start: device int32 [B], each
     <= max_start).  Attends over the cached history and the chunk, writes the chunk's
     keys and values into the cache, and returns out [B, T, Hq, D] bf16."""
+    return _chunk_like("muse_attn_prefill_chunk", layer, q, k, v, gate, start, max_start, cache, out, workspace)
+
+
+def draft_block_workspace_size(layer: LayerParams, batch: int, seq: int, max_start: int) -> int:
+    p = layer.c()
+    return int(_capi.load().muse_attn_draft_block_workspace_size(ctypes.byref(p), batch, seq, max_start))
+
+
+def draft_block(layer: LayerParams, q, k, v, gate, start, max_start: int, cache: KvCache, out=None,
+                workspace=None):
+    """A block-diffusion drafter's block: the T block tokens at positions start[b] ..
+    start[b] + T - 1 attend to the cached context and to every block key within the
+    window in both directions (no causal mask).  The cache is read only.  Shapes as for
+    prefill_chunk; returns out [B, T, Hq, D] bf16."""
+    return _chunk_like("muse_attn_draft_block", layer, q, k, v, gate, start, max_start, cache, out, workspace)
+
+
+def _chunk_like(entry, layer, q, k, v, gate, start, max_start, cache, out, workspace):
     torch = _torch()
     lib = _capi.load()
     B, T = int(q.shape[0]), int(q.shape[1])
@@ -227,7 +245,7 @@ def prefill_chunk(layer: LayerParams, q, k, v, gate, start, max_start: int, cach
     strides = (ctypes.c_int64 * 10)(*[int(s) for t in (q, k, v, gate, out) for s in (t.stride(0), t.stride(1))])
     p = layer.c()
     c = cache.c()
-    _capi.check(lib.muse_attn_prefill_chunk(
+    _capi.check(getattr(lib, entry)(
         ctypes.byref(p), B, T, q.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr(), strides,
         start.contiguous().data_ptr(), int(max_start), ctypes.byref(c), out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))

@@ -68,6 +68,8 @@ SIGNATURES = {
     "muse_attn_prefill_workspace_size": (_sz, [_P, _i32, _i32]),
     "muse_attn_prefill_chunk": (_i32, [_P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _C, _vp, _vp, _sz, _vp]),
     "muse_attn_prefill_chunk_workspace_size": (_sz, [_P, _i32, _i32, _i32]),
+    "muse_attn_draft_block": (_i32, [_P, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _C, _vp, _vp, _sz, _vp]),
+    "muse_attn_draft_block_workspace_size": (_sz, [_P, _i32, _i32, _i32]),
     "muse_attn_decode": (_i32, [_P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _C, _vp, _vp, _sz, _vp]),
     "muse_attn_decode_workspace_size": (_sz, [_P, _i32, _i32, _C]),
     "muse_layer_is_global": (_i32, [_i32, _i32]),

@@ -29,6 +29,15 @@ def prefill_flops(hq: int, d: int, batch: int, seq: int, window: int) -> int:
     return flops_per_pair(hq, d) * batch * visible_pairs(seq, window)
 
 
+def block_pairs(start: int, seq: int, window: int) -> int:
+    """Visible pairs of a non-causal block of `seq` tokens at positions start
+    .. start + seq - 1: row t sees back to start + t - W + 1 (or position 0)
+    and forward to the block's last position."""
+    if window == 0:
+        return seq * (start + seq)
+    return sum(start + seq - max(0, start + t - window + 1) for t in range(seq))
+
+
 def chunk_pairs(start: int, seq: int, window: int) -> int:
     """Visible (query, key) pairs of a chunk of `seq` tokens at positions
     start .. start + seq - 1: the tail of the whole sequence's pairs."""

@@ -226,7 +226,7 @@ CacheView cache_view(const muse_kv_cache* c) {
 
 extern "C" {
 
-int32_t muse_version(void) { return 102; }
+int32_t muse_version(void) { return 103; }
 
 const char* muse_last_error(void) { return g_err; }
 
@@ -404,17 +404,25 @@ size_t muse_attn_prefill_chunk_workspace_size(const muse_attn_params* params, in
   return chunk_ws_layout(params, B, T, max_start).total;
 }
 
-int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32_t T, const void* q,
-                                const void* k, const void* v, const void* gate, const int64_t* strides,
-                                const int32_t* start, int32_t max_start, const muse_kv_cache* cache, void* out,
-                                void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Chunked prefill and the drafter's non-causal block: the same three steps
+// (tile image of history + chunk, attention, and for the chunk the cache
+// write), with the causal mask or the bidirectional window.
+int32_t chunk_call(const muse_attn_params* params, int32_t B, int32_t T, const void* q, const void* k,
+                   const void* v, const void* gate, const int64_t* strides, const int32_t* start,
+                   int32_t max_start, const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes,
+                   void* stream, bool noncausal) {
   int32_t rc = check_params(params);
   if (rc) return rc;
   if (B < 0 || T < 0) return fail(MUSE_ERR_INVALID_ARG, "B and T must be >= 0");
   if (max_start < 0) return fail(MUSE_ERR_INVALID_ARG, "max_start must be >= 0");
   if (static_cast<int64_t>(max_start) + T > 0x7fffffffLL)
     return fail(MUSE_ERR_UNSUPPORTED, "max_start + T exceeds the 32-bit position range");
-  rc = check_cache(params, B, std::max(1, max_start + T), cache);
+  // a chunk is written after positions up to max_start + T - 1; a block only
+  // reads positions below max_start
+  rc = check_cache(params, B, std::max(1, noncausal ? max_start : max_start + T), cache);
   if (rc) return rc;
   if (B == 0 || T == 0) return ok();
   if (!q || !k || !v || !gate || !out || !start) return fail(MUSE_ERR_INVALID_ARG, "a tensor pointer is NULL");
@@ -505,6 +513,7 @@ int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32
   pa.out_eps = params->out_norm_eps;
   pa.start = start;
   pa.max_start = max_start;
+  pa.noncausal = noncausal ? 1 : 0;
   if (g_prof_start) {
     e = hipEventRecord(g_prof_start, st);
     if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
@@ -515,6 +524,8 @@ int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32
     e = hipEventRecord(g_prof_stop, st);
     if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   }
+
+  if (noncausal) return ok();  // a drafter's block is not kept in the cache
 
   // 3. the chunk's keys and values into the cache (after every read of it)
   ChunkAppendArgs ca{};
@@ -535,6 +546,30 @@ int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32
   e = launch_chunk_append(D, B, ca, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "chunk append launch: %s", hipGetErrorString(e));
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32_t T, const void* q,
+                                const void* k, const void* v, const void* gate, const int64_t* strides,
+                                const int32_t* start, int32_t max_start, const muse_kv_cache* cache, void* out,
+                                void* workspace, size_t ws_bytes, void* stream) {
+  return chunk_call(params, B, T, q, k, v, gate, strides, start, max_start, cache, out, workspace, ws_bytes, stream,
+                    false);
+}
+
+size_t muse_attn_draft_block_workspace_size(const muse_attn_params* params, int32_t B, int32_t T,
+                                            int32_t max_start) {
+  return muse_attn_prefill_chunk_workspace_size(params, B, T, max_start);
+}
+
+int32_t muse_attn_draft_block(const muse_attn_params* params, int32_t B, int32_t T, const void* q, const void* k,
+                              const void* v, const void* gate, const int64_t* strides, const int32_t* start,
+                              int32_t max_start, const muse_kv_cache* cache, void* out, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  return chunk_call(params, B, T, q, k, v, gate, strides, start, max_start, cache, out, workspace, ws_bytes, stream,
+                    true);
 }
 
 size_t muse_attn_decode_workspace_size(const muse_attn_params* params, int32_t B, int32_t max_kv_len,

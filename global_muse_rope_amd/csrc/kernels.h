@@ -137,6 +137,9 @@ struct PrefillArgs {
   // gives zero output rows
   const int32_t* start;
   int max_start;
+  // 1: no causal mask; key slot j is visible to query slot i iff |i - j| < W
+  // (every key on a window-0 layer), up to the last key slot
+  int noncausal;
 };
 
 struct DecodeArgs {

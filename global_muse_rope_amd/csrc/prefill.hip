@@ -171,18 +171,26 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   for (int mb = 0; mb < MB; ++mb) tq[mb] = t0 + ((w * MB + mb) * 32 + l32) / G;
 
   // ---- key range: masked edge tiles and the unmasked middle ----
+  // The last key visible to query slot qs: qs itself (causal), or with no
+  // causal mask qs + W - 1 (every key if W = 0), up to the last key slot.
+  const int kmax = a.T - 1 + qoff;
+  auto key_hi = [&](int qs) {
+    if (!a.noncausal) return qs;
+    return a.W > 0 ? min(kmax, qs + a.W - 1) : kmax;
+  };
   const int q0 = t0 + qoff;                           // slot of the block's first query
   const int tlast = min(t0 + C::BQ, a.T) - 1 + qoff;  // slot of its last real query
   const int klo = a.W > 0 ? max(0, q0 - a.W + 1) : 0;
   const int tile_lo = klo / kKeyTile;
-  const int tile_hi = tlast / kKeyTile;
-  // tiles fully visible to every token of the block: k0 + 63 <= q0 and k0 > tlast - W
+  const int tile_hi = key_hi(tlast) / kKeyTile;
+  // tiles fully visible to every token of the block: k0 + 63 <= key_hi(q0)
+  // and k0 > tlast - W
   int mid_lo = tile_lo;
   if (a.W > 0) {
     const int first_full = tlast - a.W + 1;                 // need k0 >= first_full
     mid_lo = max(tile_lo, (max(first_full, 0) + kKeyTile - 1) / kKeyTile);
   }
-  const int mid_hi = min((q0 + 1) / kKeyTile, tile_hi + 1);  // need k0 + 63 <= q0
+  const int mid_hi = min((key_hi(q0) + 1) / kKeyTile, tile_hi + 1);
   const int m_lo = min(mid_lo, mid_hi);
   const int m_hi = max(mid_hi, m_lo);
 
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   for (int mb = 0; mb < MB; ++mb) {
     const int qs = tq[mb] + qoff;
     lo_t[mb] = a.W > 0 ? max(0, qs - a.W + 1) : 0;
-    span[mb] = qs - lo_t[mb];
+    span[mb] = key_hi(qs) - lo_t[mb];
   }
 
   const u32x4* tsrc = a.tiles + static_cast<int64_t>(bh) * a.n_tiles * TL::CHUNKS;

@@ -184,6 +184,30 @@ int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32
 size_t muse_attn_prefill_chunk_workspace_size(const muse_attn_params* params, int32_t B, int32_t T,
                                               int32_t max_start);
 
+/* muse_attn_draft_block: the non-causal block attention of a
+ * block-diffusion drafter (deep dive, section 8.2, the drafter's fourth
+ * step).  Each of B sequences has start[b] context positions in the cache
+ * and a block of T tokens at positions start[b] .. start[b] + T - 1.  The
+ * block's queries attend to the cached context (as stored) followed by the
+ * block's own keys and values, with no causal mask: key position j is
+ * visible to query position P iff |P - j| < W on a layer with window W (both
+ * directions), and on a window-0 layer always, keys existing up to the
+ * block's last position.  The block is not written into the cache (a
+ * drafter drops it before the next block).
+ * Arguments as for muse_attn_prefill_chunk, except that the cache only needs
+ * positions below start[b] (a PAGED cache: max_start <= max_pages_per_seq *
+ * page_tokens) and is left unchanged; a start outside [0, max_start] gives
+ * zero output.
+ * workspace: at least muse_attn_draft_block_workspace_size() bytes. */
+int32_t muse_attn_draft_block(const muse_attn_params* params, int32_t B, int32_t T,
+                              const void* q, const void* k, const void* v, const void* gate,
+                              const int64_t* strides, const int32_t* start, int32_t max_start,
+                              const muse_kv_cache* cache, void* out,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+size_t muse_attn_draft_block_workspace_size(const muse_attn_params* params, int32_t B, int32_t T,
+                                            int32_t max_start);
+
 /* muse_attn_decode: one new token per sequence against a KV cache.
  * q_new, gate, out: [B, Hq, D]; k_new, v_new: [B, Hkv, D]; contiguous bf16.
  * kv_len: device int32 [B], the sequence length INCLUDING the new token;
@@ -216,7 +240,8 @@ int32_t muse_layer_is_global(int32_t layer_index, int32_t n_layers);
 const char* muse_last_error(void);
 
 /* Profiling aid: on the calling thread, make the next muse_attn_prefill,
- * muse_attn_prefill_chunk and muse_attn_decode calls record `start` (a
+ * muse_attn_prefill_chunk, muse_attn_draft_block and muse_attn_decode calls
+ * record `start` (a
  * hipEvent_t) on their stream just before their main attention kernel (the
  * prefill attention kernel; the decode split kernel) and `stop` just after it, so a caller can time that kernel
  * with hipEventElapsedTime.  Pass NULL, NULL to turn it off.  Nothing is

@@ -101,6 +101,16 @@ SPARK_CHUNK_GLOBAL = Chunk("spark_global_chunk_2k_at_128k", spark(0, 0.0), 1, 20
 SPARK_CHUNK_LOCAL = Chunk("spark_local_chunk_2k_at_128k", spark(2048, 10000.0), 1, 2048, 131072)
 CHUNK = [SPARK_CHUNK_GLOBAL, SPARK_CHUNK_LOCAL]
 
+# A block-diffusion drafter's non-causal block (deep dive, section 8.2): the
+# Glimmer assistant's attention shape (32 query heads, 8 KV heads, head width
+# 128, window 2048, 16-token blocks), 16 sequences each with 131072 context
+# positions (its ring keeps the last 2048).  The multiplier and RoPE base
+# follow the Glimmer workloads.
+GLIMMER_DRAFT_BLOCK = Chunk("glimmer_assistant_block16_at_128k",
+                            Layer(hq=32, hkv=8, d=128, window=2048, theta=10000.0, scale=GLIMMER_SCALE),
+                            16, 16, 131072)
+DRAFT = [GLIMMER_DRAFT_BLOCK]
+
 
 def decode_lengths(seed: int, batch: int, lo: int, hi: int):
     """KV lengths (new token included), integers uniform in [lo, hi]."""

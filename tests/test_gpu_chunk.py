@@ -229,3 +229,53 @@ def test_prefill_chunk_zero_start_matches_prefill():
     y2 = ma.prefill(lp, dv["q"], dv["k"], dv["v"], dv["g"])
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+# ---------------------------------------------------------------------------
+# Non-causal drafter block over a cached context
+# ---------------------------------------------------------------------------
+
+def run_block_case(kind, layer, starts, T, page_tokens=32, use_fp8=False):
+    B = len(starts)
+    d = layer.d
+    cache, hk, hv, kc0, vc0, ks, vs, table = make_chunk_cache(kind, layer, starts, T, page_tokens, use_fp8)
+    bits = {n: synth.normal_bf16_bits(8, sid, shp) for n, sid, shp in
+            [("q", 1, (B, T, layer.hq, d)), ("k", 2, (B, T, layer.hkv, d)), ("v", 3, (B, T, layer.hkv, d)),
+             ("g", 4, (B, T, layer.hq, d))]}
+    dv = {n: to_dev(b) for n, b in bits.items()}
+    k_before = cache.k.clone()
+    v_before = cache.v.clone()
+    st = torch.tensor(starts, dtype=torch.int32, device=DEV)
+    y = ma.draft_block(ma.LayerParams.from_layer(layer), dv["q"], dv["k"], dv["v"], dv["g"], st, int(max(starts)),
+                       cache)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+    worst = 0.0
+    for b, s in enumerate(starts):
+        hs = max(0, s - layer.window + 1) if layer.window else 0
+        ref = oracle.block_bidirectional(_f(bits["q"])[b], _f(bits["k"])[b], _f(bits["v"])[b], _f(bits["g"])[b],
+                                         hk[b, hs:s], hv[b, hs:s], hs, s, layer)
+        worst = max(worst, max_err(y[b], ref))
+    print(f"block {kind} fp8={use_fp8} {layer} starts={starts} T={T} max_abs_err={worst:.3e}", flush=True)
+    assert worst <= TOL
+    # the drafter's block is not kept: the cache is bit-for-bit unchanged
+    assert torch.equal(cache.k, k_before) and torch.equal(cache.v, v_before)
+
+
+BLOCK_CASES = [
+    # (kind, layer, starts, T, page_tokens)
+    ("ring", Layer(hq=32, hkv=8, d=128, window=2048, theta=10000.0, scale=GLIMMER_SCALE), [0, 5, 2047, 2048, 3000],
+     16, 0),                                                                  # a 16-token drafter block
+    ("paged", Layer(hq=128, hkv=16, d=64, window=2048, theta=10000.0, scale=SPARK_SCALE, out_norm=True,
+                    out_eps=1e-6), [0, 700, 2600], 8, 32),                     # an 8-token block, windowed pages
+    ("paged", Layer(window=0, theta=0.0, **SPARK_SMALL), [0, 1, 100, 1000], 16, 32),
+    ("paged", Layer(window=0, theta=0.0, **SPARK_SMALL), [0, 63, 300], 150, 16),   # block wider than a tile
+    ("ring", Layer(window=64, theta=10000.0, **SPARK_SMALL), [0, 30, 200], 100, 0),  # block wider than W
+]
+
+
+@pytest.mark.parametrize("use_fp8", [False, True], ids=["bf16", "e4m3"])
+@pytest.mark.parametrize("case", BLOCK_CASES, ids=lambda c: f"{c[0]}-hq{c[1].hq}d{c[1].d}w{c[1].window}T{c[3]}")
+def test_draft_block_parity(case, use_fp8):
+    kind, layer, starts, T, pt = case
+    run_block_case(kind, layer, starts, T, page_tokens=pt or 32, use_fp8=use_fp8)
