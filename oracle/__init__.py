@@ -59,3 +59,4 @@ from .attention import (  # noqa: F401
     block_bidirectional,
 )
 from . import fp8  # noqa: F401  (E4M3 cache codes)
+from . import block  # noqa: F401  (the attention half of a decoder block)
