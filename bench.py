@@ -170,6 +170,39 @@ def chunk_case(cfg, steps, warmup, events, torch, ma, draft=False):
     return res
 
 
+def block_case(cfg, steps, warmup, events, torch, ma):
+    """The attention half of a decoder block with seeded synthetic weights
+    (bf16; the residual gate in fp32) on seeded unit-RMS hidden states."""
+    from synth import normal_bf16_torch_tensor
+    from global_muse_rope_amd import accounting as acc
+    L = cfg.layer
+    H = cfg.hidden
+    n = (2 * L.hq + 2 * L.hkv) * L.d
+    gen = torch.Generator(device="cuda").manual_seed(cfg.seed)
+
+    def rnd(shape, scale, dtype=torch.bfloat16):
+        return (torch.randn(shape, generator=gen, device="cuda") * scale).to(dtype)
+
+    w = ma.BlockWeights(in_norm=rnd((H,), 0.1), w_qkvg=rnd((n, H), H ** -0.5), w_o=rnd((H, L.hq * L.d),
+                        (L.hq * L.d) ** -0.5),
+                        residual_gate=rnd((H,), 0.5, torch.float32) if cfg.spark else None,
+                        post_norm=None if cfg.spark else rnd((H,), 0.1))
+    lp = ma.LayerParams.from_layer(L)
+    x = normal_bf16_torch_tensor(cfg.seed, 9, (cfg.batch, cfg.seq, H), "cuda")
+    out = torch.empty_like(x)
+    ws = torch.empty(ma.block_prefill_workspace_size(lp, w, cfg.batch, cfg.seq), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ma.attention_block_prefill(lp, w, x, out=out, workspace=ws)
+
+    wall, kern = timed_steps(step, steps, warmup, events, torch)
+    flops = acc.block_flops(L.hq, L.hkv, L.d, H, cfg.batch, cfg.seq, L.window)
+    res = {"ms_per_step": wall, "tflops": flops / (wall * 1e-3) / 1e12, "attn_kernel_ms": kern, "flops": flops}
+    del w, x, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False):
     from synth.device import decode_device_setup
     from global_muse_rope_amd import accounting as acc
@@ -335,9 +368,14 @@ def only_case(name, steps, warmup, torch, ma):
     """Time one workload by itself (for a per-workload kernel trace)."""
     from synth import workloads as wl
     fp8 = name.endswith("_fp8")
-    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE + wl.CHUNK + wl.DRAFT}[name[:-4] if fp8 else name]
+    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE + wl.CHUNK + wl.DRAFT + wl.BLOCKS}[name[:-4] if fp8 else name]
     events = HipEvents()
-    if cfg in wl.CHUNK or cfg in wl.DRAFT:
+    if cfg in wl.BLOCKS:
+        r = block_case(cfg, steps, warmup, events, torch, ma)
+        print(json.dumps({"workload": name, "ms_per_step": round(r["ms_per_step"], 4),
+                          "step_TFLOP/s": round(r["tflops"], 2), "attn_kernel_ms": round(r["attn_kernel_ms"], 4),
+                          "steps": steps, "warmup": warmup}), flush=True)
+    elif cfg in wl.CHUNK or cfg in wl.DRAFT:
         r = chunk_case(cfg, steps, warmup, events, torch, ma, draft=cfg in wl.DRAFT)
         print(json.dumps({"workload": name, "kernel": "prefill_kernel", "kernel_ms": round(r["kernel_ms"], 4),
                           "kernel_TFLOP/s": round(r["kernel_tflops"], 2), "step_TFLOP/s": round(r["tflops"], 2),
@@ -474,6 +512,14 @@ def main():
                                 "kernel_us": round(r["kernel_ms"] * 1e3, 2),
                                 "tflops_step": round(r["tflops"], 2), "kernel_tflops": round(r["kernel_tflops"], 2)}
         result["draft_block"] = draft
+        blocks = {}
+        for kcfg in wl.BLOCKS:
+            log(f"attention block {kcfg.name}")
+            r = block_case(kcfg, 5, 1, events, torch, ma)
+            log(f"  {r['ms_per_step']:.3f} ms per step, {r['tflops']:.1f} TFLOP/s")
+            blocks[kcfg.name] = {"ms_per_step": round(r["ms_per_step"], 4), "tflops_step": round(r["tflops"], 2),
+                                 "attn_kernel_ms": round(r["attn_kernel_ms"], 4)}
+        result["attention_block"] = blocks
 
     if not args.quick:
         other = {}

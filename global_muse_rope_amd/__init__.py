@@ -285,3 +285,57 @@ def decode(layer: LayerParams, q_new, k_new, v_new, gate, kv_len, max_kv_len: in
         kv_len.data_ptr(), int(max_kv_len), ctypes.byref(c), out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream()))
     return out
+
+
+@dataclass
+class BlockWeights:
+    """Weights of a decoder block's attention half (see muse_block_weights):
+    in_norm [hidden] bf16; w_qkvg [(2 Hq + 2 Hkv) D, hidden] bf16; w_o [hidden, Hq D]
+    bf16; post_norm [hidden] bf16 (plain residual add) or residual_gate [hidden] fp32."""
+    in_norm: object
+    w_qkvg: object
+    w_o: object
+    post_norm: object = None
+    residual_gate: object = None
+    temperature: float = 0.3
+
+    @property
+    def hidden(self) -> int:
+        return int(self.in_norm.shape[0])
+
+    def c(self):
+        def ptr(t):
+            return t.data_ptr() if t is not None else None
+        return _capi.MuseBlockWeights(self.hidden, ptr(self.in_norm), ptr(self.w_qkvg), ptr(self.w_o),
+                                      ptr(self.post_norm), ptr(self.residual_gate), float(self.temperature))
+
+
+def block_prefill_workspace_size(layer: LayerParams, weights: BlockWeights, batch: int, seq: int) -> int:
+    p = layer.c()
+    w = weights.c()
+    return int(_capi.load().muse_attn_block_prefill_workspace_size(ctypes.byref(p), ctypes.byref(w), batch, seq))
+
+
+def attention_block_prefill(layer: LayerParams, weights: BlockWeights, x, out=None, workspace=None):
+    """The attention half of a decoder block on x [B, T, hidden] (bf16, contiguous):
+    input norm, projections, the layer, o_proj, post-norm and residual.  Returns
+    out [B, T, hidden] bf16."""
+    torch = _torch()
+    lib = _capi.load()
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() != 3:
+        raise ValueError("x must be a contiguous device bf16 tensor [B, T, hidden]")
+    B, T, H = (int(s) for s in x.shape)
+    if H != weights.hidden:
+        raise ValueError("x width does not match the weights")
+    if out is None:
+        out = torch.empty_like(x)
+    need = block_prefill_workspace_size(layer, weights, B, T)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    p = layer.c()
+    w = weights.c()
+    _capi.check(lib.muse_attn_block_prefill(ctypes.byref(p), ctypes.byref(w), B, T, x.data_ptr(), out.data_ptr(),
+                                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                            _stream()))
+    return out
+

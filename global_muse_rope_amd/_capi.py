@@ -55,7 +55,20 @@ class MuseKvCache(ctypes.Structure):
     ]
 
 
+class MuseBlockWeights(ctypes.Structure):
+    _fields_ = [
+        ("hidden", ctypes.c_int32),
+        ("in_norm", ctypes.c_void_p),
+        ("w_qkvg", ctypes.c_void_p),
+        ("w_o", ctypes.c_void_p),
+        ("post_norm", ctypes.c_void_p),
+        ("residual_gate", ctypes.c_void_p),
+        ("residual_gate_temperature", ctypes.c_float),
+    ]
+
+
 _P = ctypes.POINTER(MuseAttnParams)
+_BW = ctypes.POINTER(MuseBlockWeights)
 _C = ctypes.POINTER(MuseKvCache)
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -72,6 +85,8 @@ SIGNATURES = {
     "muse_attn_draft_block_workspace_size": (_sz, [_P, _i32, _i32, _i32]),
     "muse_attn_decode": (_i32, [_P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _C, _vp, _vp, _sz, _vp]),
     "muse_attn_decode_workspace_size": (_sz, [_P, _i32, _i32, _C]),
+    "muse_attn_block_prefill": (_i32, [_P, _BW, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "muse_attn_block_prefill_workspace_size": (_sz, [_P, _BW, _i32, _i32]),
     "muse_layer_is_global": (_i32, [_i32, _i32]),
     "muse_last_error": (ctypes.c_char_p, []),
     "muse_version": (_i32, []),

@@ -91,3 +91,12 @@ def kv_cache_bytes(hkv: int, d: int, n_global: int, n_local: int, context: int,
     """KV(c) = n_global * b * c + n_local * b * min(c, W)."""
     b = kv_bytes_per_token(hkv, d, elem_bytes)
     return n_global * b * context + n_local * b * min(context, window)
+
+
+def block_flops(hq: int, hkv: int, d: int, hidden: int, batch: int, seq: int, window: int) -> int:
+    """The attention half of a decoder block: the q/k/v/gate and o projections
+    (2 flops per multiply-add) plus the layer's attention flops."""
+    rows = batch * seq
+    proj = 2 * rows * hidden * (2 * hq + 2 * hkv) * d + 2 * rows * hq * d * hidden
+    return proj + prefill_flops(hq, d, batch, seq, window)
+

@@ -15,7 +15,7 @@ SRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuse_attn.so")
-SOURCES = ["api.hip", "prologue.hip", "prefill.hip", "decode.hip"]
+SOURCES = ["api.hip", "prologue.hip", "prefill.hip", "decode.hip", "block.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -54,7 +54,8 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, defines, tag), SOURCES))
     tmp = out + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+    # hipBLASLt runs the block's two projection GEMMs
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp, "-lhipblaslt"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

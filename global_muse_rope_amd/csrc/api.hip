@@ -222,11 +222,31 @@ CacheView cache_view(const muse_kv_cache* c) {
   return v;
 }
 
+// The block's workspace: h, the q/k/v/gate projection, o and the o_proj
+// output (bf16 rows), the GEMM scratch, then the layer's own workspace.
+constexpr size_t kBlockGemmScratch = size_t(64) << 20;
+struct BlockWs {
+  size_t h, proj, o, a, gemm, attn, total;
+};
+BlockWs block_ws_layout(const muse_attn_params* p, const muse_block_weights* w, int32_t B, int32_t T) {
+  const size_t R = static_cast<size_t>(B) * T;
+  const size_t D = p->head_dim, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
+  BlockWs l;
+  l.h = 0;
+  l.proj = l.h + align256(R * w->hidden * 2);
+  l.o = l.proj + align256(R * (2 * Hq + 2 * Hkv) * D * 2);
+  l.a = l.o + align256(R * Hq * D * 2);
+  l.gemm = l.a + align256(R * w->hidden * 2);
+  l.attn = l.gemm + kBlockGemmScratch;
+  l.total = l.attn + prefill_ws(p, B, T);
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t muse_version(void) { return 103; }
+int32_t muse_version(void) { return 104; }
 
 const char* muse_last_error(void) { return g_err; }
 
@@ -640,6 +660,84 @@ int32_t muse_attn_decode(const muse_attn_params* params, int32_t B, const void* 
   a.part = reinterpret_cast<float*>(ws);
   hipError_t e = launch_decode(D, Hq / Hkv, a, static_cast<hipStream_t>(stream), g_prof_start, g_prof_stop);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t muse_attn_block_prefill_workspace_size(const muse_attn_params* params, const muse_block_weights* weights,
+                                              int32_t B, int32_t T) {
+  if (check_params(params) || !weights || B < 0 || T < 0) return 0;
+  return block_ws_layout(params, weights, B, T).total;
+}
+
+int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block_weights* w, int32_t B, int32_t T,
+                                const void* x, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  int32_t rc = check_params(params);
+  if (rc) return rc;
+  if (!w) return fail(MUSE_ERR_INVALID_ARG, "weights is NULL");
+  if (B < 0 || T < 0) return fail(MUSE_ERR_INVALID_ARG, "B and T must be >= 0");
+  if (w->hidden <= 0 || w->hidden % 8 != 0 || w->hidden > kBlockMaxHidden)
+    return fail(MUSE_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 8 up to %d", w->hidden,
+                kBlockMaxHidden);
+  if (!w->in_norm || !w->w_qkvg || !w->w_o) return fail(MUSE_ERR_INVALID_ARG, "a weight pointer is NULL");
+  if (w->residual_gate ? !(w->residual_gate_temperature > 0.f) : !w->post_norm)
+    return fail(MUSE_ERR_INVALID_ARG, "a plain add needs post_norm; a residual gate a positive temperature");
+  if (B == 0 || T == 0) return ok();
+  if (!x || !out) return fail(MUSE_ERR_INVALID_ARG, "x or out is NULL");
+  const void* ptrs[] = {x, out, w->in_norm, w->w_qkvg, w->w_o, w->post_norm, w->residual_gate};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MUSE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (!workspace || !aligned16(workspace)) return fail(MUSE_ERR_WORKSPACE, "workspace missing or misaligned");
+  const BlockWs l = block_ws_layout(params, w, B, T);
+  if (ws_bytes < l.total) return fail(MUSE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, l.total);
+  if (static_cast<int64_t>(B) * T > 0x7fffffffLL) return fail(MUSE_ERR_UNSUPPORTED, "too many rows for one launch");
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t R = static_cast<int64_t>(B) * T;
+  const int64_t D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
+  const int64_t N = (2 * Hq + 2 * Hkv) * D;
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + l.h);
+  uint16_t* proj = reinterpret_cast<uint16_t*>(ws + l.proj);
+  uint16_t* o = reinterpret_cast<uint16_t*>(ws + l.o);
+  uint16_t* a = reinterpret_cast<uint16_t*>(ws + l.a);
+
+  BlockNormArgs na{};
+  na.x = static_cast<const uint16_t*>(x);
+  na.w = static_cast<const uint16_t*>(w->in_norm);
+  na.out = h;
+  na.rows = R;
+  na.hidden = w->hidden;
+  na.eps = 1e-5f;
+  hipError_t e = launch_block_input_norm(na, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "input norm launch: %s", hipGetErrorString(e));
+
+  char msg[256];
+  if (block_gemm(R, N, w->hidden, h, w->w_qkvg, proj, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
+    return fail(MUSE_ERR_HIP, "q/k/v/gate projection: %s", msg);
+
+  // the layer on strided views of the projection: q, k, v, gate columns
+  const int64_t strides[10] = {T * N, N, T * N, N, T * N, N, T * N, N, T * Hq * D, Hq * D};
+  rc = muse_attn_prefill(params, B, T, proj, proj + Hq * D, proj + (Hq + Hkv) * D, proj + (Hq + 2 * Hkv) * D,
+                         strides, nullptr, o, ws + l.attn, l.total - l.attn, stream);
+  if (rc) return rc;
+
+  if (block_gemm(R, w->hidden, Hq * D, o, w->w_o, a, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
+    return fail(MUSE_ERR_HIP, "o_proj: %s", msg);
+
+  BlockResidualArgs ra{};
+  ra.x = static_cast<const uint16_t*>(x);
+  ra.branch = a;
+  ra.post_norm = static_cast<const uint16_t*>(w->post_norm);
+  ra.gate = w->residual_gate;
+  ra.out = static_cast<uint16_t*>(out);
+  ra.rows = R;
+  ra.hidden = w->hidden;
+  ra.eps = 1e-8f;
+  ra.temperature = w->residual_gate_temperature;
+  ra.alpha_sq_floor = 1e-3f;
+  e = launch_block_residual(ra, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "residual launch: %s", hipGetErrorString(e));
   return ok();
 }
 

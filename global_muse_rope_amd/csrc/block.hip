@@ -1,0 +1,213 @@
+// The attention half of a decoder block around the layer (Muse Spark Open
+// deep dive, section 2.1 forward walk; section 5.1 for Glimmer, 5.2-5.3 for
+// Spark): input RMSNorm, the q/k/v/gate projections, the layer, o_proj, the
+// post-attention norm and the residual.
+//
+// The two projections are plain GEMMs and go to hipBLASLt; the norms and the
+// residual are row kernels here, one workgroup per token row:
+//   input_layernorm: centered RMSNorm, x / sqrt(mean(x^2) + 1e-5) * (1 + w),
+//     the gain formed and applied in fp32 and rounded once to bf16;
+//   Glimmer: out = x + a / sqrt(mean(a^2) + 1e-8) * (1 + w_post);
+//   Spark:   out = alpha * x + beta * a / sqrt(mean(a^2) + 1e-8), with
+//     beta = sigmoid(g / T), alpha = sqrt(max(sigmoid(-g / T) (1 + beta), 1e-3))
+//     (the norm-preserving residual gate, its coefficients in fp32).
+#include <hipblaslt/hipblaslt.h>
+
+#include <cstdio>
+#include <mutex>
+
+#include "kernels.h"
+
+namespace muse {
+
+namespace {
+constexpr int kRowThreads = 256;
+constexpr int kMaxChunksPerThread = kBlockMaxHidden / 8 / kRowThreads;
+
+// sum over the workgroup (4 waves)
+__device__ __forceinline__ float row_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float s = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return s;
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return 1.0f / (1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+}  // namespace
+
+__global__ __launch_bounds__(kRowThreads) void block_input_norm_kernel(BlockNormArgs a) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nch = a.hidden / 8;
+  const uint16_t* xr = a.x + row * a.hidden;
+  float v[kMaxChunksPerThread][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerThread; ++i) {
+    const int c = threadIdx.x + i * kRowThreads;
+    u32x4 w = {0, 0, 0, 0};
+    if (c < nch) w = *reinterpret_cast<const u32x4*>(xr + 8 * c);
+    unpack_bf16x8(w, v[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
+  }
+  ss = row_sum(ss, red);
+  const float rs = 1.0f / sqrtf(ss / a.hidden + a.eps);
+  uint16_t* orow = a.out + row * a.hidden;
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerThread; ++i) {
+    const int c = threadIdx.x + i * kRowThreads;
+    if (c >= nch) continue;
+    float g[8];
+    unpack_bf16x8(*reinterpret_cast<const u32x4*>(a.w + 8 * c), g);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = pack_bf16x2(v[i][2 * e] * rs * (1.0f + g[2 * e]), v[i][2 * e + 1] * rs * (1.0f + g[2 * e + 1]));
+    *reinterpret_cast<u32x4*>(orow + 8 * c) = o;
+  }
+}
+
+__global__ __launch_bounds__(kRowThreads) void block_residual_kernel(BlockResidualArgs a) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int nch = a.hidden / 8;
+  const uint16_t* ar = a.branch + row * a.hidden;
+  float v[kMaxChunksPerThread][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerThread; ++i) {
+    const int c = threadIdx.x + i * kRowThreads;
+    u32x4 w = {0, 0, 0, 0};
+    if (c < nch) w = *reinterpret_cast<const u32x4*>(ar + 8 * c);
+    unpack_bf16x8(w, v[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
+  }
+  ss = row_sum(ss, red);
+  const float rs = 1.0f / sqrtf(ss / a.hidden + a.eps);
+  const uint16_t* xr = a.x + row * a.hidden;
+  uint16_t* orow = a.out + row * a.hidden;
+#pragma unroll
+  for (int i = 0; i < kMaxChunksPerThread; ++i) {
+    const int c = threadIdx.x + i * kRowThreads;
+    if (c >= nch) continue;
+    float x[8], y[8];
+    unpack_bf16x8(*reinterpret_cast<const u32x4*>(xr + 8 * c), x);
+    if (a.gate) {
+      // Spark: norm-preserving residual gate over the weightless-normed branch
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gate + 8 * c);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gate + 8 * c + 4);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float w = (e < 4 ? g0[e] : g1[e - 4]) / a.temperature;
+        const float beta = sigmoidf_(w);
+        const float alpha = sqrtf(fmaxf(sigmoidf_(-w) * (1.0f + beta), a.alpha_sq_floor));
+        y[e] = alpha * x[e] + beta * (v[i][e] * rs);
+      }
+    } else {
+      // Glimmer: centered post-norm, then the plain residual add
+      float g[8];
+      unpack_bf16x8(*reinterpret_cast<const u32x4*>(a.post_norm + 8 * c), g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = x[e] + v[i][e] * rs * (1.0f + g[e]);
+    }
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(orow + 8 * c) = o;
+  }
+}
+
+hipError_t launch_block_input_norm(const BlockNormArgs& a, hipStream_t st) {
+  if (a.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(block_input_norm_kernel, dim3(static_cast<unsigned>(a.rows)), dim3(kRowThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_residual(const BlockResidualArgs& a, hipStream_t st) {
+  if (a.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(block_residual_kernel, dim3(static_cast<unsigned>(a.rows)), dim3(kRowThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// GEMM through hipBLASLt: out[rows, n] = act[rows, k] * w[n, k]^T, all
+// row-major bf16, fp32 accumulation.  In hipBLASLt's column-major terms
+// that is D[n, rows] = op_T(W') * act', with W' = w viewed as [k, n] and
+// act' = act viewed as [k, rows].  One handle per device, created on first
+// use (host state only); the caller's workspace is the GEMM's scratch.
+// ---------------------------------------------------------------------------
+namespace {
+std::mutex g_lt_mu;
+hipblasLtHandle_t g_lt[64] = {};
+}  // namespace
+
+int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, void* out, void* ws,
+               size_t ws_bytes, hipStream_t st, char* err, size_t errlen) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    snprintf(err, errlen, "no current device");
+    return 1;
+  }
+  hipblasLtHandle_t h;
+  {
+    std::lock_guard<std::mutex> lk(g_lt_mu);
+    if (!g_lt[dev] && hipblasLtCreate(&g_lt[dev]) != HIPBLAS_STATUS_SUCCESS) {
+      g_lt[dev] = nullptr;
+      snprintf(err, errlen, "hipblasLtCreate failed");
+      return 1;
+    }
+    h = g_lt[dev];
+  }
+  hipblasLtMatmulDesc_t desc = nullptr;
+  hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, lc = nullptr;
+  hipblasLtMatmulPreference_t pref = nullptr;
+  int rc = 1;
+  do {
+    if (hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) != HIPBLAS_STATUS_SUCCESS) break;
+    const int32_t opT = HIPBLAS_OP_T, opN = HIPBLAS_OP_N;
+    if (hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opT, sizeof(opT)) != HIPBLAS_STATUS_SUCCESS ||
+        hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opN, sizeof(opN)) != HIPBLAS_STATUS_SUCCESS)
+      break;
+    if (hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, k, n, k) != HIPBLAS_STATUS_SUCCESS) break;
+    if (hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, k, rows, k) != HIPBLAS_STATUS_SUCCESS) break;
+    if (hipblasLtMatrixLayoutCreate(&lc, HIP_R_16BF, n, rows, n) != HIPBLAS_STATUS_SUCCESS) break;
+    if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) break;
+    const uint64_t wsb = ws_bytes;
+    if (hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb)) !=
+        HIPBLAS_STATUS_SUCCESS)
+      break;
+    hipblasLtMatmulHeuristicResult_t res[1];
+    int found = 0;
+    if (hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, 1, res, &found) != HIPBLAS_STATUS_SUCCESS ||
+        found < 1) {
+      snprintf(err, errlen, "hipBLASLt found no algorithm for %lld x %lld x %lld", static_cast<long long>(rows),
+               static_cast<long long>(n), static_cast<long long>(k));
+      rc = 2;
+      break;
+    }
+    const float one = 1.0f, zero = 0.0f;
+    if (hipblasLtMatmul(h, desc, &one, w, la, act, lb, &zero, out, lc, out, lc, &res[0].algo, ws, wsb, st) !=
+        HIPBLAS_STATUS_SUCCESS) {
+      snprintf(err, errlen, "hipblasLtMatmul failed");
+      rc = 2;
+      break;
+    }
+    rc = 0;
+  } while (false);
+  if (rc == 1) snprintf(err, errlen, "hipBLASLt descriptor setup failed");
+  if (pref) hipblasLtMatmulPreferenceDestroy(pref);
+  if (lc) hipblasLtMatrixLayoutDestroy(lc);
+  if (lb) hipblasLtMatrixLayoutDestroy(lb);
+  if (la) hipblasLtMatrixLayoutDestroy(la);
+  if (desc) hipblasLtMatmulDescDestroy(desc);
+  return rc;
+}
+
+}  // namespace muse

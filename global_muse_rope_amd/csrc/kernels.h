@@ -171,6 +171,38 @@ struct DecodeArgs {
   float* part;    // [B * Hkv][max_chunks][G * (D + 2)] partial results
 };
 
+// ---------------------------------------------------------------------------
+// The attention half of a decoder block: row kernels around two GEMMs.
+// ---------------------------------------------------------------------------
+constexpr int kBlockMaxHidden = 8192;
+
+struct BlockNormArgs {
+  const uint16_t* x;  // [rows, hidden] bf16
+  const uint16_t* w;  // [hidden] bf16 weight (gain 1 + w)
+  uint16_t* out;      // [rows, hidden] bf16
+  int64_t rows;
+  int hidden;
+  float eps;
+};
+
+struct BlockResidualArgs {
+  const uint16_t* x;          // residual stream [rows, hidden] bf16
+  const uint16_t* branch;     // o_proj output [rows, hidden] bf16
+  const uint16_t* post_norm;  // plain add: [hidden] bf16 weight (gain 1 + w)
+  const float* gate;          // residual gate: [hidden] fp32 parameter (null: plain add)
+  uint16_t* out;
+  int64_t rows;
+  int hidden;
+  float eps, temperature, alpha_sq_floor;
+};
+
+hipError_t launch_block_input_norm(const BlockNormArgs& a, hipStream_t st);
+hipError_t launch_block_residual(const BlockResidualArgs& a, hipStream_t st);
+// out[rows, n] = act[rows, k] * w[n, k]^T (bf16, fp32 accumulation); returns
+// 0, or non-zero with a message in err
+int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, void* out, void* ws,
+               size_t ws_bytes, hipStream_t st, char* err, size_t errlen);
+
 hipError_t launch_rope_qknorm(int d, int out_dtype, const RopeQkArgs& a, hipStream_t st);
 hipError_t launch_rope_table(int d, const RopeTableArgs& a, hipStream_t st);
 hipError_t launch_kv_prep(int d, int B, const KvPrepArgs& a, hipStream_t st);

@@ -231,6 +231,41 @@ int32_t muse_attn_decode(const muse_attn_params* params, int32_t B,
 size_t muse_attn_decode_workspace_size(const muse_attn_params* params, int32_t B,
                                        int32_t max_kv_len, const muse_kv_cache* cache);
 
+/* The attention half of one decoder block around the layer (deep dive,
+ * section 2.1 forward walk; section 5.1 for Glimmer's sandwich norms, 5.2 for
+ * Spark's norm-preserving residual gate, 5.3 for the RMSNorm variants):
+ *   h   = x / sqrt(mean(x^2) + 1e-5) * (1 + in_norm)      input_layernorm
+ *   q, k, v, gate = h W_q^T, h W_k^T, h W_v^T, h W_g^T     (no biases)
+ *   o   = the layer (as muse_attn_prefill, positions 0 .. T-1)
+ *   a   = o W_o^T                                         o_proj
+ *   f   = a / sqrt(mean(a^2) + 1e-8), times (1 + post_norm) with a plain add
+ *   out = x + f (residual_gate NULL), or alpha * x + beta * f with
+ *         beta = sigmoid(g / T), alpha = sqrt(max(sigmoid(-g / T) (1 + beta), 1e-3))
+ * Norm gains are formed and applied in fp32; every intermediate tensor (h,
+ * the projections, o, a) is bf16; the GEMMs accumulate in fp32. */
+typedef struct muse_block_weights {
+  int32_t hidden;                  /* model width: 8192 (Spark) or 6656 (Glimmer); a multiple of 8, <= 8192 */
+  const void* in_norm;             /* [hidden] bf16: input_layernorm weight w (gain 1 + w) */
+  const void* w_qkvg;              /* [(2 Hq + 2 Hkv) D, hidden] bf16: rows of W_q, W_k, W_v, W_g stacked */
+  const void* w_o;                 /* [hidden, Hq D] bf16 */
+  const void* post_norm;           /* plain add: [hidden] bf16 post_attention_layernorm weight (gain 1 + w) */
+  const float* residual_gate;      /* [hidden] fp32 residual-gate parameter g, or NULL for a plain add */
+  float residual_gate_temperature; /* T, 0.3 */
+} muse_block_weights;
+
+/* muse_attn_block_prefill: the block's attention half over B sequences of T
+ * tokens.  x, out: [B, T, hidden] bf16, contiguous.  The projections run as
+ * hipBLASLt GEMMs on `stream` with the caller's workspace as their scratch
+ * (the library keeps one host-side hipBLASLt handle per device).
+ * workspace: at least muse_attn_block_prefill_workspace_size() bytes.
+ * T == 0 or B == 0 is a no-op. */
+int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block_weights* weights,
+                                int32_t B, int32_t T, const void* x, void* out,
+                                void* workspace, size_t ws_bytes, void* stream);
+
+size_t muse_attn_block_prefill_workspace_size(const muse_attn_params* params,
+                                              const muse_block_weights* weights, int32_t B, int32_t T);
+
 /* Layer schedule: layer i of n_layers is global (full attention, NoPE) iff
  * (n_layers - 1 - i) mod 4 == 0 (deep dive, section 2.2 equation).
  * Returns 1 (global), 0 (local) or -1 for i outside [0, n_layers). */

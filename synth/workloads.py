@@ -112,6 +112,23 @@ GLIMMER_DRAFT_BLOCK = Chunk("glimmer_assistant_block16_at_128k",
 DRAFT = [GLIMMER_DRAFT_BLOCK]
 
 
+@dataclass(frozen=True)
+class Block:
+    """The attention half of a decoder block (input norm, projections, the
+    layer, o_proj, post-norm and residual) on `seq` tokens."""
+    name: str
+    layer: Layer
+    hidden: int
+    spark: bool      # True: weightless post-norm + residual gate; False: centered post-norm + add
+    batch: int
+    seq: int
+    seed: int = 0
+
+
+SPARK_BLOCK_LOCAL = Block("spark_attn_block_local_4k", spark(2048, 10000.0), 8192, True, 1, 4096)
+BLOCKS = [SPARK_BLOCK_LOCAL]
+
+
 def decode_lengths(seed: int, batch: int, lo: int, hi: int):
     """KV lengths (new token included), integers uniform in [lo, hi]."""
     import numpy as np

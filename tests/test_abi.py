@@ -48,7 +48,8 @@ def test_struct_layouts_match_header(tmp_path):
     cc = shutil.which("gcc") or shutil.which("cc")
     if cc is None:
         pytest.skip("no C compiler")
-    fields = {"muse_attn_params": capi.MuseAttnParams, "muse_kv_cache": capi.MuseKvCache}
+    fields = {"muse_attn_params": capi.MuseAttnParams, "muse_kv_cache": capi.MuseKvCache,
+              "muse_block_weights": capi.MuseBlockWeights}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "muse_attn.h"', "int main(void) {"]
     for cname, cls in fields.items():
         lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
