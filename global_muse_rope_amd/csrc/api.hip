@@ -226,7 +226,7 @@ CacheView cache_view(const muse_kv_cache* c) {
 // output (bf16 rows), the GEMM scratch, then the layer's own workspace.
 constexpr size_t kBlockGemmScratch = size_t(64) << 20;
 struct BlockWs {
-  size_t h, proj, o, a, gemm, attn, total;
+  size_t h, proj, o, a, coef, gemm, attn, total;
 };
 BlockWs block_ws_layout(const muse_attn_params* p, const muse_block_weights* w, int32_t B, int32_t T) {
   const size_t R = static_cast<size_t>(B) * T;
@@ -236,7 +236,8 @@ BlockWs block_ws_layout(const muse_attn_params* p, const muse_block_weights* w, 
   l.proj = l.h + align256(R * w->hidden * 2);
   l.o = l.proj + align256(R * (2 * Hq + 2 * Hkv) * D * 2);
   l.a = l.o + align256(R * Hq * D * 2);
-  l.gemm = l.a + align256(R * w->hidden * 2);
+  l.coef = l.a + align256(R * w->hidden * 2);
+  l.gemm = l.coef + align256(static_cast<size_t>(w->hidden) * 8);
   l.attn = l.gemm + kBlockGemmScratch;
   l.total = l.attn + prefill_ws(p, B, T);
   return l;
@@ -725,17 +726,21 @@ int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block
   if (block_gemm(R, w->hidden, Hq * D, o, w->w_o, a, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
     return fail(MUSE_ERR_HIP, "o_proj: %s", msg);
 
+  float2* coef = nullptr;
+  if (w->residual_gate) {
+    coef = reinterpret_cast<float2*>(ws + l.coef);
+    e = launch_block_gate_coef(w->residual_gate, coef, w->hidden, w->residual_gate_temperature, 1e-3f, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "gate coefficient launch: %s", hipGetErrorString(e));
+  }
   BlockResidualArgs ra{};
   ra.x = static_cast<const uint16_t*>(x);
   ra.branch = a;
   ra.post_norm = static_cast<const uint16_t*>(w->post_norm);
-  ra.gate = w->residual_gate;
+  ra.coef = reinterpret_cast<const float*>(coef);
   ra.out = static_cast<uint16_t*>(out);
   ra.rows = R;
   ra.hidden = w->hidden;
   ra.eps = 1e-8f;
-  ra.temperature = w->residual_gate_temperature;
-  ra.alpha_sq_floor = 1e-3f;
   e = launch_block_residual(ra, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "residual launch: %s", hipGetErrorString(e));
   return ok();

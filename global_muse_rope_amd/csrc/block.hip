@@ -10,7 +10,8 @@
 //   Glimmer: out = x + a / sqrt(mean(a^2) + 1e-8) * (1 + w_post);
 //   Spark:   out = alpha * x + beta * a / sqrt(mean(a^2) + 1e-8), with
 //     beta = sigmoid(g / T), alpha = sqrt(max(sigmoid(-g / T) (1 + beta), 1e-3))
-//     (the norm-preserving residual gate, its coefficients in fp32).
+//     (the norm-preserving residual gate, its per-channel coefficients in
+//     fp32, computed once per call).
 #include <hipblaslt/hipblaslt.h>
 
 #include <cstdio>
@@ -99,16 +100,13 @@ __global__ __launch_bounds__(kRowThreads) void block_residual_kernel(BlockResidu
     if (c >= nch) continue;
     float x[8], y[8];
     unpack_bf16x8(*reinterpret_cast<const u32x4*>(xr + 8 * c), x);
-    if (a.gate) {
+    if (a.coef) {
       // Spark: norm-preserving residual gate over the weightless-normed branch
-      const f32x4 g0 = *reinterpret_cast<const f32x4*>(a.gate + 8 * c);
-      const f32x4 g1 = *reinterpret_cast<const f32x4*>(a.gate + 8 * c + 4);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float w = (e < 4 ? g0[e] : g1[e - 4]) / a.temperature;
-        const float beta = sigmoidf_(w);
-        const float alpha = sqrtf(fmaxf(sigmoidf_(-w) * (1.0f + beta), a.alpha_sq_floor));
-        y[e] = alpha * x[e] + beta * (v[i][e] * rs);
+      for (int e = 0; e < 8; e += 2) {
+        const f32x4 ab = *reinterpret_cast<const f32x4*>(a.coef + 2 * (8 * c + e));  // (alpha, beta) x 2
+        y[e] = ab[0] * x[e] + ab[1] * (v[i][e] * rs);
+        y[e + 1] = ab[2] * x[e + 1] + ab[3] * (v[i][e + 1] * rs);
       }
     } else {
       // Glimmer: centered post-norm, then the plain residual add
@@ -122,6 +120,26 @@ __global__ __launch_bounds__(kRowThreads) void block_residual_kernel(BlockResidu
     for (int e = 0; e < 4; ++e) o[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
     *reinterpret_cast<u32x4*>(orow + 8 * c) = o;
   }
+}
+
+// The residual gate's coefficients depend on the channel only: one pass
+// per call turns the parameter g into (alpha, beta) pairs for every row.
+__global__ __launch_bounds__(kRowThreads) void block_gate_coef_kernel(const float* gate, float2* coef, int hidden,
+                                                                      float temperature, float alpha_sq_floor) {
+  const int i = blockIdx.x * kRowThreads + threadIdx.x;
+  if (i >= hidden) return;
+  const float w = gate[i] / temperature;
+  const float beta = sigmoidf_(w);
+  const float alpha = sqrtf(fmaxf(sigmoidf_(-w) * (1.0f + beta), alpha_sq_floor));
+  coef[i] = make_float2(alpha, beta);
+}
+
+hipError_t launch_block_gate_coef(const float* gate, float2* coef, int hidden, float temperature,
+                                  float alpha_sq_floor, hipStream_t st) {
+  const unsigned blocks = static_cast<unsigned>((hidden + kRowThreads - 1) / kRowThreads);
+  hipLaunchKernelGGL(block_gate_coef_kernel, dim3(blocks), dim3(kRowThreads), 0, st, gate, coef, hidden, temperature,
+                     alpha_sq_floor);
+  return hipGetLastError();
 }
 
 hipError_t launch_block_input_norm(const BlockNormArgs& a, hipStream_t st) {

@@ -189,15 +189,18 @@ struct BlockResidualArgs {
   const uint16_t* x;          // residual stream [rows, hidden] bf16
   const uint16_t* branch;     // o_proj output [rows, hidden] bf16
   const uint16_t* post_norm;  // plain add: [hidden] bf16 weight (gain 1 + w)
-  const float* gate;          // residual gate: [hidden] fp32 parameter (null: plain add)
+  const float* coef;          // residual gate: [hidden] (alpha, beta) fp32 pairs (null: plain add)
   uint16_t* out;
   int64_t rows;
   int hidden;
-  float eps, temperature, alpha_sq_floor;
+  float eps;
 };
 
 hipError_t launch_block_input_norm(const BlockNormArgs& a, hipStream_t st);
 hipError_t launch_block_residual(const BlockResidualArgs& a, hipStream_t st);
+// (alpha, beta) of the residual gate for every channel of g
+hipError_t launch_block_gate_coef(const float* gate, float2* coef, int hidden, float temperature,
+                                  float alpha_sq_floor, hipStream_t st);
 // out[rows, n] = act[rows, k] * w[n, k]^T (bf16, fp32 accumulation); returns
 // 0, or non-zero with a message in err
 int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, void* out, void* ws,
