@@ -79,27 +79,32 @@ __global__ __launch_bounds__(kRowThreads) void block_residual_kernel(BlockResidu
   const int64_t row = blockIdx.x;
   const int nch = a.hidden / 8;
   const uint16_t* ar = a.branch + row * a.hidden;
+  const uint16_t* xr = a.x + row * a.hidden;
   float v[kMaxChunksPerThread][8];
+  u32x4 xw[kMaxChunksPerThread];  // the residual stream, fetched while the branch's norm is reduced
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < kMaxChunksPerThread; ++i) {
     const int c = threadIdx.x + i * kRowThreads;
     u32x4 w = {0, 0, 0, 0};
-    if (c < nch) w = *reinterpret_cast<const u32x4*>(ar + 8 * c);
+    xw[i] = w;
+    if (c < nch) {
+      w = *reinterpret_cast<const u32x4*>(ar + 8 * c);
+      xw[i] = *reinterpret_cast<const u32x4*>(xr + 8 * c);
+    }
     unpack_bf16x8(w, v[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
   }
   ss = row_sum(ss, red);
   const float rs = 1.0f / sqrtf(ss / a.hidden + a.eps);
-  const uint16_t* xr = a.x + row * a.hidden;
   uint16_t* orow = a.out + row * a.hidden;
 #pragma unroll
   for (int i = 0; i < kMaxChunksPerThread; ++i) {
     const int c = threadIdx.x + i * kRowThreads;
     if (c >= nch) continue;
     float x[8], y[8];
-    unpack_bf16x8(*reinterpret_cast<const u32x4*>(xr + 8 * c), x);
+    unpack_bf16x8(xw[i], x);
     if (a.coef) {
       // Spark: norm-preserving residual gate over the weightless-normed branch
 #pragma unroll
