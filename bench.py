@@ -172,23 +172,15 @@ def chunk_case(cfg, steps, warmup, events, torch, ma, draft=False):
 
 def block_case(cfg, steps, warmup, events, torch, ma):
     """The attention half of a decoder block with seeded synthetic weights
-    (bf16; the residual gate in fp32) on seeded unit-RMS hidden states."""
-    from synth import normal_bf16_torch_tensor
+    (bf16; the residual gate in fp32) on seeded N(0,1) hidden states."""
+    from synth.device import block_device_setup
     from global_muse_rope_amd import accounting as acc
     L = cfg.layer
-    H = cfg.hidden
-    n = (2 * L.hq + 2 * L.hkv) * L.d
-    gen = torch.Generator(device="cuda").manual_seed(cfg.seed)
-
-    def rnd(shape, scale, dtype=torch.bfloat16):
-        return (torch.randn(shape, generator=gen, device="cuda") * scale).to(dtype)
-
-    w = ma.BlockWeights(in_norm=rnd((H,), 0.1), w_qkvg=rnd((n, H), H ** -0.5), w_o=rnd((H, L.hq * L.d),
-                        (L.hq * L.d) ** -0.5),
-                        residual_gate=rnd((H,), 0.5, torch.float32) if cfg.spark else None,
-                        post_norm=None if cfg.spark else rnd((H,), 0.1))
+    s = block_device_setup(cfg)
+    w = ma.BlockWeights(in_norm=s["in_norm"], w_qkvg=s["w_qkvg"], w_o=s["w_o"], residual_gate=s["residual_gate"],
+                        post_norm=s["post_norm"])
     lp = ma.LayerParams.from_layer(L)
-    x = normal_bf16_torch_tensor(cfg.seed, 9, (cfg.batch, cfg.seq, H), "cuda")
+    x = s["x"]
     out = torch.empty_like(x)
     ws = torch.empty(ma.block_prefill_workspace_size(lp, w, cfg.batch, cfg.seq), dtype=torch.uint8, device="cuda")
 
@@ -196,9 +188,9 @@ def block_case(cfg, steps, warmup, events, torch, ma):
         ma.attention_block_prefill(lp, w, x, out=out, workspace=ws)
 
     wall, kern = timed_steps(step, steps, warmup, events, torch)
-    flops = acc.block_flops(L.hq, L.hkv, L.d, H, cfg.batch, cfg.seq, L.window)
+    flops = acc.block_flops(L.hq, L.hkv, L.d, cfg.hidden, cfg.batch, cfg.seq, L.window)
     res = {"ms_per_step": wall, "tflops": flops / (wall * 1e-3) / 1e12, "attn_kernel_ms": kern, "flops": flops}
-    del w, x, out, ws
+    del s, w, x, out, ws
     torch.cuda.empty_cache()
     return res
 

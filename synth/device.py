@@ -20,7 +20,8 @@ import numpy as np
 
 from . import (normal_bf16_torch, normal_bf16_torch_tensor, bf16_bits_to_f64, f32_to_bf16_bits, normal_f32,
                e4m3_codes, e4m3_codes_torch)
-from .workloads import S_Q, S_K, S_V, S_G, S_CACHE_BASE, decode_lengths
+from .workloads import (S_Q, S_K, S_V, S_G, S_CACHE_BASE, S_X, S_IN_NORM, S_W_QKVG, S_W_O, S_POST_NORM, S_RES_GATE,
+                        decode_lengths)
 
 STREAM = {"q": S_Q, "k": S_K, "v": S_V, "g": S_G}
 
@@ -258,3 +259,31 @@ def chunk_host_rows(cfg, name, b, rows, heads=None):
            + np.arange(L.d)[None, None, :])
     return bf16_bits_to_f64(f32_to_bf16_bits(normal_f32(cfg.seed + 5, STREAM[name], idx)))
 
+
+
+def block_device_setup(cfg, device="cuda"):
+    """Inputs of the decoder-block workload: hidden states x [B, T, hidden]
+    (N(0,1) bf16) and seeded weights, each an N(0,1) bf16 draw times a fixed
+    scale (an fp32 product rounded to bf16, nearest-even; the same bits on
+    any device): input and post-attention norm weights 0.1, the stacked
+    q/k/v/gate projection hidden^-1/2, o_proj (Hq D)^-1/2, and the fp32
+    residual-gate parameter 0.5.  Returns a dict of tensors; exactly one of
+    post_norm (Glimmer) and residual_gate (Spark) is set."""
+    import torch
+    L = cfg.layer
+    H = cfg.hidden
+    n = (2 * L.hq + 2 * L.hkv) * L.d
+
+    def scaled(stream, shape, scale, dtype=torch.bfloat16):
+        return (normal_bf16_torch_tensor(cfg.seed, stream, shape, device).float() * scale).to(dtype)
+
+    res = {"x": normal_bf16_torch_tensor(cfg.seed, S_X, (cfg.batch, cfg.seq, H), device),
+           "in_norm": scaled(S_IN_NORM, (H,), 0.1),
+           "w_qkvg": scaled(S_W_QKVG, (n, H), H ** -0.5),
+           "w_o": scaled(S_W_O, (H, L.hq * L.d), (L.hq * L.d) ** -0.5),
+           "post_norm": None, "residual_gate": None}
+    if cfg.spark:
+        res["residual_gate"] = scaled(S_RES_GATE, (H,), 0.5, torch.float32)
+    else:
+        res["post_norm"] = scaled(S_POST_NORM, (H,), 0.1)
+    return res

@@ -20,6 +20,8 @@ SPARK_SCALE = 5.4730064863875
 S_Q, S_K, S_V, S_G = 1, 2, 3, 4
 S_CACHE_BASE = 1 << 20   # + (b * Hkv + h) * 2 + {0: K, 1: V}
 S_LENGTHS = 7
+# decoder-block inputs: hidden states and the synthetic weights
+S_X, S_IN_NORM, S_W_QKVG, S_W_O, S_POST_NORM, S_RES_GATE = 9, 10, 11, 12, 13, 14
 
 
 @dataclass(frozen=True)

@@ -276,3 +276,94 @@ def test_prefill_chunk_fullsize_sampled(cfg):
     print(f"{cfg.name}: {len(rows)} rows x {2 * G} heads, max_abs_err={worst:.3e} (oracle {time.time() - t:.1f} s)",
           flush=True)
     assert worst <= TOL
+
+
+def test_draft_block_fullsize_sampled():
+    """The drafter's 16-token block after 131072 cached positions (16
+    sequences, a 2048-entry ring): every row of two KV-head groups of the
+    first and last sequence against the oracle over the visible context, and
+    the cache left bit-for-bit unchanged."""
+    cfg = wl.GLIMMER_DRAFT_BLOCK
+    L = cfg.layer
+    G = L.group
+    print(f"draft block full size {cfg.name}", flush=True)
+    s = sd.chunk_device_setup(cfg)
+    assert s["kind"] == "ring"
+    cache = ma.KvCache.ring(s["kc"], s["vc"])
+    k_before, v_before = s["kc"].clone(), s["vc"].clone()
+    lp = ma.LayerParams.from_layer(L)
+    ws = torch.empty(ma.draft_block_workspace_size(lp, cfg.batch, cfg.seq, cfg.start), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(s["q"])
+    y = ma.draft_block(lp, s["q"], s["k"], s["v"], s["g"], s["start"], cfg.start, cache, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    assert torch.equal(s["kc"], k_before) and torch.equal(s["vc"], v_before)
+    y = y.float().cpu().numpy()
+    S, T = cfg.start, cfg.seq
+    hs = S - L.window + 1                       # the first row's window starts here
+    rows = np.arange(T)
+    worst = 0.0
+    t = time.time()
+    for b in sorted({0, cfg.batch - 1}):
+        for hk in sorted({0, L.hkv - 1}):
+            heads = np.arange(hk * G, (hk + 1) * G)
+            k_hist = sd.cache_values_host(cfg.seed, b, hk, L.hkv, "k", hs, S, L.d)[:, None, :]
+            v_hist = sd.cache_values_host(cfg.seed, b, hk, L.hkv, "v", hs, S, L.d)[:, None, :]
+            kb = sd.chunk_host_rows(cfg, "k", b, rows, [hk])
+            vb = sd.chunk_host_rows(cfg, "v", b, rows, [hk])
+            q = sd.chunk_host_rows(cfg, "q", b, rows, heads)
+            g = sd.chunk_host_rows(cfg, "g", b, rows, heads)
+            ref = oracle.block_bidirectional(q, kb, vb, g, k_hist, v_hist, hs, S, group_layer(L))
+            worst = max(worst, max_err(y[b][:, heads], ref))
+    print(f"{cfg.name}: 2 sequences x {2 * G} heads x {T} rows, max_abs_err={worst:.3e} "
+          f"(oracle {time.time() - t:.1f} s)", flush=True)
+    assert worst <= TOL
+
+
+def test_attention_block_fullsize_sampled():
+    """The attention half of a Spark decoder block on 4096 tokens (hidden
+    8192, local layer): sampled rows against the fp64 block oracle.  A row
+    of a local layer depends on the hidden states of its own window only, so
+    the oracle runs on the slice of rows that ends at the sampled row and
+    starts at its window's first position (or at 0)."""
+    from oracle import block as OB
+    from synth.device import block_device_setup
+    from test_gpu_block import BLOCK_TOL
+    cfg = wl.SPARK_BLOCK_LOCAL
+    L = cfg.layer
+    W = L.window
+    assert W > 0 and cfg.batch == 1
+    print(f"attention block full size {cfg.name}", flush=True)
+    s = block_device_setup(cfg)
+    w = ma.BlockWeights(in_norm=s["in_norm"], w_qkvg=s["w_qkvg"], w_o=s["w_o"], residual_gate=s["residual_gate"],
+                        post_norm=s["post_norm"])
+    lp = ma.LayerParams.from_layer(L)
+    ws = torch.empty(ma.block_prefill_workspace_size(lp, w, cfg.batch, cfg.seq), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(s["x"])
+    y = ma.attention_block_prefill(lp, w, s["x"], out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    y = y[0].float().cpu().numpy()
+
+    def host(t):
+        return t.double().cpu().numpy() if t is not None else None
+
+    Wt = {"in_norm": host(s["in_norm"]), "w_qkvg": host(s["w_qkvg"]), "w_o": host(s["w_o"]),
+          "post_norm": host(s["post_norm"]), "residual_gate": host(s["residual_gate"])}
+    x = host(s["x"][0])
+    T = cfg.seq
+    # one slice from 0 covers every row whose window starts at 0; later rows
+    # each get the slice of their own window
+    early = [r for r in sample_rows(T, W, n_random=0) if r < W]
+    late = sorted({T - 1, T - 2, W, W + 1, *np.random.default_rng(3).integers(W, T, size=2).tolist()})
+    worst = 0.0
+    t = time.time()
+    ref = OB.attention_block(x[:W], Wt, L, rows=np.array(early))
+    worst = max(worst, max_err(y[early], ref))
+    for r in late:
+        lo = r - W + 1
+        ref = OB.attention_block(x[lo:r + 1], Wt, L, positions=np.arange(lo, r + 1), rows=np.array([W - 1]))
+        worst = max(worst, max_err(y[[r]], ref))
+    print(f"{cfg.name}: {len(early) + len(late)} rows x {cfg.hidden}, max_abs_err={worst:.3e} "
+          f"(oracle {time.time() - t:.1f} s)", flush=True)
+    assert worst <= BLOCK_TOL

@@ -41,3 +41,31 @@ def test_e4m3_codes_numpy_and_torch_agree():
     assert np.array_equal(a, b)
     mag = a & 0x7F
     assert mag.min() >= 0x20 and mag.max() <= 0x47 and 0.4 < (a >> 7).mean() < 0.6
+
+
+def test_block_inputs_are_scaled_draws_with_host_bits():
+    """The decoder-block inputs: each weight is the stream's N(0,1) bf16 draw
+    times its scale, rounded to bf16 (nearest-even) from the fp32 product;
+    the same bits on the CPU form as the numpy form gives."""
+    import torch
+    from synth.device import block_device_setup
+    from synth.workloads import Block, Layer, S_X, S_W_QKVG, S_RES_GATE, S_POST_NORM
+    layer = Layer(hq=4, hkv=2, d=16, window=8, theta=10000.0, scale=3.87)
+    for spark in (True, False):
+        cfg = Block("tiny", layer, 64, spark, 2, 5, seed=3)
+        s = block_device_setup(cfg, device="cpu")
+        assert np.array_equal(s["x"].view(torch.int16).numpy().view(np.uint16),
+                              synth.normal_bf16_bits(3, S_X, (2, 5, 64)))
+        n = (2 * 4 + 2 * 2) * 16
+        raw = synth.bf16_bits_to_f32(synth.normal_bf16_bits(3, S_W_QKVG, (n, 64)))
+        want = synth.f32_to_bf16_bits(raw * np.float32(64 ** -0.5))
+        assert np.array_equal(s["w_qkvg"].view(torch.int16).numpy().view(np.uint16), want)
+        if spark:
+            assert s["post_norm"] is None and s["residual_gate"].dtype == torch.float32
+            g = synth.bf16_bits_to_f32(synth.normal_bf16_bits(3, S_RES_GATE, (64,))) * np.float32(0.5)
+            assert np.array_equal(s["residual_gate"].numpy(), g)
+        else:
+            assert s["residual_gate"] is None
+            p = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(synth.normal_bf16_bits(3, S_POST_NORM, (64,)))
+                                       * np.float32(0.1))
+            assert np.array_equal(s["post_norm"].view(torch.int16).numpy().view(np.uint16), p)
