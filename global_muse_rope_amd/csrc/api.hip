@@ -94,13 +94,16 @@ int64_t prefill_tiles(int32_t T) { return (static_cast<int64_t>(T) + kKeyTile - 
 // Prefill workspace: the K/V tile images (k_hat fp16 + V^T bf16, padded rows)
 // and, on RoPE layers, the (cos, sin) table for B * T positions.
 struct PrefillWs {
-  size_t tile_bytes, rope_bytes, total;
+  size_t tile_bytes, rope_bytes, part_o_bytes, part_l_bytes, total;
+  int nsplit;
 };
 
 PrefillWs prefill_ws_layout(const muse_attn_params* p, int32_t B, int32_t T) {
   PrefillWs w;
   w.tile_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * prefill_tiles(T) * tile_chunks(p->head_dim) * 16);
   w.rope_bytes = p->rope_theta > 0.f ? align256(static_cast<size_t>(B) * T * (p->head_dim / 2) * 8) : 0;
+  w.part_o_bytes = w.part_l_bytes = 0;
+  w.nsplit = 1;
   w.total = w.tile_bytes + w.rope_bytes;
   return w;
 }
@@ -116,12 +119,26 @@ int64_t chunk_tiles(const muse_attn_params* p, int32_t T, int32_t max_start) {
   return (hist + T + kKeyTile - 1) / kKeyTile;
 }
 
+// Query blocks of a chunk launch (every sequence and KV head).
+int64_t chunk_qblocks(const muse_attn_params* p, int32_t B, int32_t T) {
+  const int G = p->num_q_heads / p->num_kv_heads;
+  const int bq = prefill_rows_per_block(p->head_dim, G) / G;
+  return (static_cast<int64_t>(T) + bq - 1) / bq * B * p->num_kv_heads;
+}
+
+// Tile images and the RoPE table, then, when the launch has too few query
+// blocks to fill the chip (a short chunk or a drafter's block), the key
+// pieces' partial sums: O fp32 [nsplit][B][T][Hq][D] and sums [..][Hq].
 PrefillWs chunk_ws_layout(const muse_attn_params* p, int32_t B, int32_t T, int32_t max_start) {
   PrefillWs w;
-  w.tile_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * chunk_tiles(p, T, max_start) *
-                          tile_chunks(p->head_dim) * 16);
+  const int64_t n_tiles = chunk_tiles(p, T, max_start);
+  w.tile_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * n_tiles * tile_chunks(p->head_dim) * 16);
   w.rope_bytes = p->rope_theta > 0.f ? align256(static_cast<size_t>(B) * T * (p->head_dim / 2) * 8) : 0;
-  w.total = w.tile_bytes + w.rope_bytes;
+  w.nsplit = prefill_key_split(chunk_qblocks(p, B, T), n_tiles);
+  const size_t rows = static_cast<size_t>(B) * T * p->num_q_heads;
+  w.part_o_bytes = w.nsplit > 1 ? align256(w.nsplit * rows * p->head_dim * 4) : 0;
+  w.part_l_bytes = w.nsplit > 1 ? align256(w.nsplit * rows * 4) : 0;
+  w.total = w.tile_bytes + w.rope_bytes + w.part_o_bytes + w.part_l_bytes;
   return w;
 }
 
@@ -535,12 +552,37 @@ int32_t chunk_call(const muse_attn_params* params, int32_t B, int32_t T, const v
   pa.start = start;
   pa.max_start = max_start;
   pa.noncausal = noncausal ? 1 : 0;
+  pa.nsplit = wl.nsplit;
+  char* ws_parts = static_cast<char*>(workspace) + wl.tile_bytes + wl.rope_bytes;
+  pa.part_o = wl.nsplit > 1 ? reinterpret_cast<float*>(ws_parts) : nullptr;
+  pa.part_l = wl.nsplit > 1 ? reinterpret_cast<float*>(ws_parts + wl.part_o_bytes) : nullptr;
   if (g_prof_start) {
     e = hipEventRecord(g_prof_start, st);
     if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   }
   e = launch_prefill(D, G, pa, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  if (wl.nsplit > 1) {
+    PrefillCombineArgs pc{};
+    pc.part_o = pa.part_o;
+    pc.part_l = pa.part_l;
+    pc.nsplit = wl.nsplit;
+    pc.gate = pa.gate;
+    pc.out = pa.out;
+    pc.g_sb = s[6];
+    pc.g_st = s[7];
+    pc.o_sb = s[8];
+    pc.o_st = s[9];
+    pc.B = B;
+    pc.T = T;
+    pc.Hq = Hq;
+    pc.out_norm = params->out_norm;
+    pc.out_eps = params->out_norm_eps;
+    pc.start = start;
+    pc.max_start = max_start;
+    e = launch_prefill_combine(D, pc, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "prefill combine launch: %s", hipGetErrorString(e));
+  }
   if (g_prof_stop) {
     e = hipEventRecord(g_prof_stop, st);
     if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));

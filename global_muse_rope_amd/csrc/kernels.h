@@ -140,6 +140,30 @@ struct PrefillArgs {
   // 1: no causal mask; key slot j is visible to query slot i iff |i - j| < W
   // (every key on a window-0 layer), up to the last key slot
   int noncausal;
+  // key split (nsplit > 1): workgroup x takes query block x / nsplit and the
+  // (x mod nsplit)-th of nsplit contiguous pieces of that block's tile range,
+  // and writes unnormalized partial sums for the combine kernel instead of
+  // outputs: part_o [nsplit][B][T][Hq][D] (sum of p v) and part_l
+  // [nsplit][B][T][Hq] (sum of p); an empty piece writes zeros
+  int nsplit;
+  float* part_o;
+  float* part_l;
+};
+
+// Finishes a key-split prefill: sums the partials of each output row, then
+// 1/sum, the per-head output norm, the sigmoid gate and the bf16 store.
+struct PrefillCombineArgs {
+  const float* part_o;
+  const float* part_l;
+  int nsplit;
+  const uint16_t* gate;
+  uint16_t* out;
+  int64_t g_sb, g_st, o_sb, o_st;
+  int B, T, Hq;
+  int out_norm;
+  float out_eps;
+  const int32_t* start;  // rows of a sequence whose start is out of range are zero
+  int max_start;
 };
 
 struct DecodeArgs {
@@ -212,6 +236,12 @@ hipError_t launch_kv_prep(int d, int B, const KvPrepArgs& a, hipStream_t st);
 hipError_t launch_chunk_append(int d, int B, const ChunkAppendArgs& a, hipStream_t st);
 hipError_t launch_prefill(int d, int g, const PrefillArgs& a, hipStream_t st);
 int prefill_rows_per_block(int d, int g);
+// Key pieces per query block for a launch of n_blocks query blocks whose
+// blocks span at most max_tiles key tiles: 1 when the blocks alone fill the
+// chip, else enough pieces for about 512 workgroups, each of at least two
+// tiles (at most 16 pieces).  Depends on the shape only.
+int prefill_key_split(int64_t n_blocks, int64_t max_tiles);
+hipError_t launch_prefill_combine(int d, const PrefillCombineArgs& a, hipStream_t st);
 int prefill_qblock_group();
 // ev0/ev1 (may be null): recorded around the split kernel.
 hipError_t launch_decode(int d, int g, const DecodeArgs& a, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);

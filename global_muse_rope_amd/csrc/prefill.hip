@@ -33,6 +33,7 @@
 //     of one KV head land on one XCD so they share K/V tiles in its L2.
 //     Local layers (uniform work): each XCD walks one contiguous range of
 //     query blocks, so the 2048-key window's tiles stay in that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -114,9 +115,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   //   first, groups of QC consecutive blocks of one KV head on one XCD.
   const int nlog = a.n_qblocks_pad * a.batch_heads;  // a multiple of 8
   constexpr int QC = kQBlockGroup;
+  //   Key split: one (query block, key piece) per workgroup, pieces of a
+  //   block on consecutive workgroups.
   // (head width 64 already fits two workgroups per CU, which overlap each
   // other's block starts; the persistent loop's registers would cost that)
-  const bool persistent = D == 128 && a.W > 0;
+  const bool split = a.nsplit > 1;
+  const bool persistent = D == 128 && a.W > 0 && !split;
   int lx_first, lx_end, lx_step;
   if (persistent) {
     const int per = nlog >> 3;
@@ -130,7 +134,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     lx_step = 1;
   }
   auto block_of = [&](int lx, int& bh, int& qb) {
-    if (persistent) {
+    if (split) {
+      const int ql = lx / a.nsplit;
+      bh = ql / a.n_qblocks;
+      qb = ql - bh * a.n_qblocks;
+    } else if (persistent) {
       bh = lx / a.n_qblocks_pad;
       qb = lx - bh * a.n_qblocks_pad;
     } else {
@@ -156,6 +164,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int b = bh / a.Hkv;
   const int hk = bh - b * a.Hkv;
   const int t0 = qb * C::BQ;
+  const int piece = split ? lx - (lx / a.nsplit) * a.nsplit : 0;
   // Chunked prefill: query row t is key slot t + qoff of the tile image
   // (0 for a whole-sequence prefill).  Every key index below is a slot.
   int qoff = 0;
@@ -181,8 +190,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int q0 = t0 + qoff;                           // slot of the block's first query
   const int tlast = min(t0 + C::BQ, a.T) - 1 + qoff;  // slot of its last real query
   const int klo = a.W > 0 ? max(0, q0 - a.W + 1) : 0;
-  const int tile_lo = klo / kKeyTile;
-  const int tile_hi = key_hi(tlast) / kKeyTile;
+  int tile_lo = klo / kKeyTile;
+  int tile_hi = key_hi(tlast) / kKeyTile;
   // tiles fully visible to every token of the block: k0 + 63 <= key_hi(q0)
   // and k0 > tlast - W
   int mid_lo = tile_lo;
@@ -193,6 +202,34 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int mid_hi = min((key_hi(q0) + 1) / kKeyTile, tile_hi + 1);
   const int m_lo = min(mid_lo, mid_hi);
   const int m_hi = max(mid_hi, m_lo);
+
+  // partial sums of output row (t, hq) for this key piece
+  const int n_seq = a.batch_heads / a.Hkv;
+  auto part_row = [&](int t, int hq) -> int64_t {
+    return ((static_cast<int64_t>(piece) * n_seq + b) * a.T + t) * (static_cast<int64_t>(a.Hkv) * G) + hq;
+  };
+  if (split) {
+    // this piece of the tile range (the masks above stay those of the block)
+    const int n = tile_hi - tile_lo + 1;
+    const int lo = tile_lo + (piece * n) / a.nsplit;
+    tile_hi = tile_lo + ((piece + 1) * n) / a.nsplit - 1;
+    tile_lo = lo;
+    if (tile_hi < tile_lo) {
+      // an empty piece adds nothing: zero partials for the block's rows
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int r = (w * MB + mb) * 32 + l32;
+        const int t = t0 + r / G;
+        if (t >= a.T) continue;
+        const int64_t pr = part_row(t, hk * G + (r % G));
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int d = 0; d < D / 2; d += 4) *reinterpret_cast<f32x4*>(a.part_o + pr * D + h2 * (D / 2) + d) = z;
+        if (h2 == 0) a.part_l[pr] = 0.f;
+      }
+      continue;  // uniform over the workgroup, before any barrier
+    }
+  }
 
   // per-lane visible range of each row block: key in [lo_t, lo_t + span]
   int lo_t[MB], span[MB];
@@ -491,7 +528,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const float ltot = lsum[mb] + __shfl_xor(lsum[mb], 32, kWave);
-    const float inv = __builtin_amdgcn_rcpf(ltot);
+    if (split) {
+      // a key piece hands on its unnormalized sums
+      const int r = (w * MB + mb) * 32 + l32;
+      const int t = t0 + r / G;
+      if (h2 == 0 && t < a.T) a.part_l[part_row(t, hk * G + (r % G))] = ltot;
+    }
+    const float inv = split ? 1.0f : __builtin_amdgcn_rcpf(ltot);
     float ss = 0.f;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -501,7 +544,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         ss += o[mb][db][i] * o[mb][db][i];
       }
     float rsn = 1.0f;
-    if (a.out_norm) {
+    if (a.out_norm && !split) {
       ss += __shfl_xor(ss, 32, kWave);
       rsn = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.out_eps);
     }
@@ -529,7 +572,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     const int d0 = (k % CPC) * 8;
     const int r = w * MB * 32 + cl;              // block column
     const int t = t0 + r / G;
-    if (t < a.T) {
+    if (t < a.T && split) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(ost + cl * OROW + d0);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(ost + cl * OROW + d0 + 4);
+      float* po = a.part_o + part_row(t, hk * G + (r % G)) * D + d0;
+      *reinterpret_cast<f32x4*>(po) = v0;
+      *reinterpret_cast<f32x4*>(po + 4) = v1;
+    } else if (t < a.T) {
       const int hq = hk * G + (r % G);
       const u32x4 gw = *reinterpret_cast<const u32x4*>(a.gate + b * a.g_sb + static_cast<int64_t>(t) * a.g_st +
                                                        static_cast<int64_t>(hq) * D + d0);
@@ -554,6 +603,62 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // before the next block's tile copies land there
   __syncthreads();
   }  // query blocks of this workgroup
+}
+
+// Key-split finish: CPC = D/8 lanes per output row, 8 dims each.  Sums the
+// pieces' partials in piece order, then the prefill epilogue's arithmetic:
+// 1/sum, the per-head RMS norm over D, y = o * sigmoid(g), bf16.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillCombineArgs a) {
+  constexpr int CPC = D / 8;
+  constexpr int RPB = 256 / CPC;
+  const int64_t R = static_cast<int64_t>(a.B) * a.T * a.Hq;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + threadIdx.x / CPC;
+  if (row >= R) return;  // whole groups of CPC lanes
+  const int d0 = (threadIdx.x % CPC) * 8;
+  const int hq = static_cast<int>(row % a.Hq);
+  const int64_t bt = row / a.Hq;
+  const int t = static_cast<int>(bt % a.T);
+  const int b = static_cast<int>(bt / a.T);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float l = 0.f;
+  for (int s = 0; s < a.nsplit; ++s) {
+    const float* po = a.part_o + (static_cast<int64_t>(s) * R + row) * D + d0;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(po);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(po + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += x0[e];
+      acc[e + 4] += x1[e];
+    }
+    l += a.part_l[static_cast<int64_t>(s) * R + row];
+  }
+  const float inv = __builtin_amdgcn_rcpf(l);
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc[e] *= inv;
+    ss += acc[e] * acc[e];
+  }
+#pragma unroll
+  for (int m = 1; m < CPC; m <<= 1) ss += __shfl_xor(ss, m, kWave);
+  const float rsn = a.out_norm ? __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.out_eps) : 1.0f;
+  const bool zero_out = a.start && !chunk_start_ok(a.start[b], a.max_start);
+  const u32x4 gw = *reinterpret_cast<const u32x4*>(a.gate + b * a.g_sb + static_cast<int64_t>(t) * a.g_st +
+                                                   static_cast<int64_t>(hq) * D + d0);
+  float g[8];
+  unpack_bf16x8(gw, g);
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * g[e]));
+    y[e] = zero_out ? 0.f : acc[e] * rsn * sg;
+  }
+  u32x4 ow;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ow[e] = pack_bf16x2(y[2 * e], y[2 * e + 1]);
+  *reinterpret_cast<u32x4*>(a.out + b * a.o_sb + static_cast<int64_t>(t) * a.o_st + static_cast<int64_t>(hq) * D + d0) =
+      ow;
 }
 
 // ---------------------------------------------------------------------------
@@ -605,7 +710,9 @@ hipError_t launch_dg(const PrefillArgs& a, hipStream_t st) {
   auto kernel = prefill_kernel<D, G, NW, MB>;
   const int nlog = a.n_qblocks_pad * a.batch_heads;  // a multiple of 8
   int grid = nlog;
-  if (D == 128 && a.W > 0) {
+  if (a.nsplit > 1) {
+    grid = a.n_qblocks * a.batch_heads * a.nsplit;
+  } else if (D == 128 && a.W > 0) {
     // local layers run a persistent grid of at most one wave of resident
     // workgroups, a multiple of 8 so every XCD gets the same number
     const int cap = resident_workgroups(kernel, C::THREADS) & ~7;
@@ -633,6 +740,26 @@ int prefill_rows_per_block(int d, int) {
 }
 
 int prefill_qblock_group() { return kQBlockGroup; }
+
+int prefill_key_split(int64_t n_blocks, int64_t max_tiles) {
+  constexpr int64_t kFillBlocks = 256, kTargetWorkgroups = 512, kMaxPieces = 16;
+  if (n_blocks <= 0 || n_blocks >= kFillBlocks) return 1;
+  int64_t s = (kTargetWorkgroups + n_blocks - 1) / n_blocks;
+  s = std::min(s, std::min(kMaxPieces, max_tiles / 2));
+  return static_cast<int>(std::max<int64_t>(s, 1));
+}
+
+hipError_t launch_prefill_combine(int d, const PrefillCombineArgs& a, hipStream_t st) {
+  const int64_t R = static_cast<int64_t>(a.B) * a.T * a.Hq;
+  if (R == 0) return hipSuccess;
+  const int rpb = 256 / (d / 8);
+  const unsigned blocks = static_cast<unsigned>((R + rpb - 1) / rpb);
+  if (d == 64)
+    hipLaunchKernelGGL(prefill_combine_kernel<64>, dim3(blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(prefill_combine_kernel<128>, dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(int d, int g, const PrefillArgs& a, hipStream_t st) {
   return d == 64 ? launch_d<64>(g, a, st) : launch_d<128>(g, a, st);

@@ -215,10 +215,14 @@ def test_prefill_chunk_start_out_of_range():
     run_chunk_case("paged", layer, [50, -1, 30, 99], 40, page_tokens=32, max_start=64, bad=(1, 3))
 
 
-def test_prefill_chunk_zero_start_matches_prefill():
-    """With nothing cached the chunk is a whole-sequence prefill."""
+@pytest.mark.parametrize("T", [200, 4200], ids=["key-split", "one-piece"])
+def test_prefill_chunk_zero_start_matches_prefill(T):
+    """With nothing cached the chunk is a whole-sequence prefill: bit for bit
+    when the chunk launch has enough query blocks to run unsplit (T = 4200),
+    and within one bf16 rounding when its few blocks are split over key
+    pieces (T = 200), whose partial sums add in another order."""
     layer = Layer(window=256, theta=10000.0, **SPARK_SMALL)
-    B, T = 2, 200
+    B = 2
     cache, *_ = make_chunk_cache("ring", layer, [0, 0], T, 32, False)
     bits = {n: synth.normal_bf16_bits(9, sid, shp) for n, sid, shp in
             [("q", 1, (B, T, 16, 64)), ("k", 2, (B, T, 2, 64)), ("v", 3, (B, T, 2, 64)), ("g", 4, (B, T, 16, 64))]}
@@ -228,7 +232,10 @@ def test_prefill_chunk_zero_start_matches_prefill():
                           0, cache)
     y2 = ma.prefill(lp, dv["q"], dv["k"], dv["v"], dv["g"])
     torch.cuda.synchronize()
-    assert torch.equal(y1, y2)
+    if T > 1000:
+        assert torch.equal(y1, y2)
+    else:
+        assert torch.allclose(y1.float(), y2.float(), rtol=2.0 ** -7, atol=1e-6)
 
 
 # ---------------------------------------------------------------------------
