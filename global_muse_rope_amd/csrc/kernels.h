@@ -238,8 +238,8 @@ hipError_t launch_prefill(int d, int g, const PrefillArgs& a, hipStream_t st);
 int prefill_rows_per_block(int d, int g);
 // Key pieces per query block for a launch of n_blocks query blocks whose
 // blocks span at most max_tiles key tiles: 1 when the blocks alone fill the
-// chip, else enough pieces for about 512 workgroups, each of at least two
-// tiles (at most 16 pieces).  Depends on the shape only.
+// chip, else enough pieces for about one workgroup per CU of an MI355X (256),
+// each of at least two tiles (at most 16 pieces).  Depends on the shape only.
 int prefill_key_split(int64_t n_blocks, int64_t max_tiles);
 hipError_t launch_prefill_combine(int d, const PrefillCombineArgs& a, hipStream_t st);
 int prefill_qblock_group();

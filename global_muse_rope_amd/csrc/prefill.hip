@@ -741,8 +741,11 @@ int prefill_rows_per_block(int d, int) {
 
 int prefill_qblock_group() { return kQBlockGroup; }
 
+#ifndef MUSE_PREFILL_SPLIT_TARGET
+#define MUSE_PREFILL_SPLIT_TARGET 256
+#endif
 int prefill_key_split(int64_t n_blocks, int64_t max_tiles) {
-  constexpr int64_t kFillBlocks = 256, kTargetWorkgroups = 512, kMaxPieces = 16;
+  constexpr int64_t kFillBlocks = 256, kTargetWorkgroups = MUSE_PREFILL_SPLIT_TARGET, kMaxPieces = 16;
   if (n_blocks <= 0 || n_blocks >= kFillBlocks) return 1;
   int64_t s = (kTargetWorkgroups + n_blocks - 1) / n_blocks;
   s = std::min(s, std::min(kMaxPieces, max_tiles / 2));
