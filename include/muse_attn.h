@@ -276,12 +276,14 @@ const char* muse_last_error(void);
 
 /* Profiling aid: on the calling thread, make the next muse_attn_prefill,
  * muse_attn_prefill_chunk, muse_attn_draft_block and muse_attn_decode calls
- * record `start` (a
- * hipEvent_t) on their stream just before their main attention kernel (the
- * prefill attention kernel; the decode split kernel) and `stop` just after it, so a caller can time that kernel
- * with hipEventElapsedTime.  Pass NULL, NULL to turn it off.  Nothing is
- * recorded by muse_rope_qknorm.  Returns MUSE_OK, or MUSE_ERR_INVALID_ARG if
- * exactly one of the two is NULL. */
+ * record `start` (a hipEvent_t) on their stream just before their main
+ * attention kernel (the prefill attention kernel; the decode split kernel)
+ * and `stop` just after it, so a caller can time that kernel with
+ * hipEventElapsedTime.  A chunk or drafter call whose few query blocks are
+ * split over key pieces records `stop` after the kernel that combines the
+ * pieces.  Pass NULL, NULL to turn it off.  Nothing is recorded by
+ * muse_rope_qknorm.  Returns MUSE_OK, or MUSE_ERR_INVALID_ARG if exactly one
+ * of the two is NULL. */
 int32_t muse_profile_events(void* start, void* stop);
 
 /* Library version, major * 10000 + minor * 100 + patch. */
