@@ -115,6 +115,81 @@ __device__ __forceinline__ int cache_vstride(const CacheView& c) {
 }
 
 // ---------------------------------------------------------------------------
+// Chunked prefill, a tile whose 64 positions are all visible cached history:
+// the image is a format change of the cache's own rows.  Key rows widen to
+// fp32 (E4M3 codes times their scale) and narrow to fp16; a value image
+// chunk holds keys 0-3 and 8-11 (or 4-7 and 12-15) of a 16-position group,
+// i.e. one half of each of two 8-position runs of the cache's head-dim-major
+// rows, so it is assembled in registers from two cache reads.  The same
+// arithmetic as the general path below; absent pages give zeros.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void kv_prep_history_tile(const KvPrepArgs& a, int b, int hk, int pos0, u32x4* tdst) {
+  using TL = TileLayout<D>;
+  constexpr int BK = kKeyTile;
+  constexpr int KC = D / 8;
+  const int tid = threadIdx.x;
+  const CacheView& cv = a.cache;
+  // keys: image chunk j is row j / (KC + 1), chunk j % (KC + 1) (the last is the pad)
+  for (int j = tid; j < BK * (KC + 1); j += 256) {
+    const int r = j / (KC + 1), c = j - r * (KC + 1);
+    u32x4 out = {0, 0, 0, 0};
+    if (c < KC) {
+      const CacheLoc cl = cache_loc(cv, b, hk, a.Hkv, D, pos0 + r);
+      if (cl.ok) {
+        float f[8];
+        const int64_t off = cl.k + c * 8;
+        if (cv.fp8) {
+          unpack_bf16x8(e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(cv.k) + off)), f);
+          const float sc = cv.k_scale[cl.si];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] *= sc;
+        } else {
+          unpack_bf16x8(*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(cv.k) + off), f);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) out[i] = pack_f16x2(f[2 * i], f[2 * i + 1]);
+      }
+    }
+    tdst[j] = out;
+  }
+  // values: item (d, g16) writes image chunks 2 g16 and 2 g16 + 1 of head-dim row d
+  u32x4* vdst = tdst + TL::KCHUNKS;
+  const int vstride = cache_vstride(cv);
+  for (int it = tid; it < D * (BK / 16); it += 256) {
+    const int d = it / (BK / 16), g16 = it - d * (BK / 16);
+    const CacheLoc cl = cache_loc(cv, b, hk, a.Hkv, D, pos0 + 16 * g16);
+    u32x4 x = {0, 0, 0, 0}, y = {0, 0, 0, 0};  // positions 0-7 and 8-15 of the group, bf16 pairs
+    if (cl.ok) {
+      const int64_t off = cl.v + static_cast<int64_t>(d) * vstride;
+      if (cv.fp8) {
+        const float sc = cv.v_scale[cl.si];
+        const uint8_t* src = static_cast<const uint8_t*>(cv.v) + off;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float f[8];
+          unpack_bf16x8(e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(src + 8 * h)), f);
+          u32x4 w;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = static_cast<uint32_t>(f32_to_bf16_bits(f[2 * i] * sc)) |
+                   (static_cast<uint32_t>(f32_to_bf16_bits(f[2 * i + 1] * sc)) << 16);
+          if (h == 0) x = w;
+          else y = w;
+        }
+      } else {
+        const uint16_t* src = static_cast<const uint16_t*>(cv.v) + off;
+        x = *reinterpret_cast<const u32x4*>(src);
+        y = *reinterpret_cast<const u32x4*>(src + 8);
+      }
+    }
+    vdst[d * TL::VROW + 2 * g16] = u32x4{x[0], x[1], y[0], y[1]};
+    vdst[d * TL::VROW + 2 * g16 + 1] = u32x4{x[2], x[3], y[2], y[3]};
+  }
+  for (int d = tid; d < D; d += 256) vdst[d * TL::VROW + BK / 8] = u32x4{0, 0, 0, 0};
+}
+
+// ---------------------------------------------------------------------------
 // Prefill key/value preparation: one 64-key tile of one (sequence, KV head)
 // per workgroup.  Writes the tile image the attention kernel copies straight
 // into LDS: k_hat as fp16 key rows and V transposed to head-dim rows (bf16),
@@ -149,6 +224,13 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     need_lo = a.W > 0 ? max(0, st - a.W + 1) : 0;
   }
   const int pos0 = kb + tile * BK;  // position of the tile's first row
+  if constexpr (CHUNK) {
+    // a tile of visible history only (uniform over the workgroup)
+    if (pos0 >= need_lo && pos0 + BK <= st) {
+      kv_prep_history_tile<D>(a, b, hk, pos0, a.tiles + (bh * a.n_tiles + tile) * TileLayout<D>::CHUNKS);
+      return;
+    }
+  }
   const int tok = CHUNK ? pos0 + r - st : tile * BK + r;
   const bool hist = CHUNK && pos0 + r >= need_lo && pos0 + r < st;
 
