@@ -15,7 +15,9 @@
 #include <hipblaslt/hipblaslt.h>
 
 #include <cstdio>
+#include <map>
 #include <mutex>
+#include <tuple>
 
 #include "kernels.h"
 
@@ -165,10 +167,52 @@ hipError_t launch_block_residual(const BlockResidualArgs& a, hipStream_t st) {
 // that is D[n, rows] = op_T(W') * act', with W' = w viewed as [k, n] and
 // act' = act viewed as [k, rows].  One handle per device, created on first
 // use (host state only); the caller's workspace is the GEMM's scratch.
+// The first call of a shape on a device times hipBLASLt's top candidates on
+// the call's own operands (a few runs each, then a wait for the stream) and
+// keeps the fastest for later calls; under stream capture it takes the
+// heuristic's first choice without timing.
 // ---------------------------------------------------------------------------
 namespace {
 std::mutex g_lt_mu;
 hipblasLtHandle_t g_lt[64] = {};
+constexpr int kTuneCandidates = 16;
+using GemmKey = std::tuple<int, int64_t, int64_t, int64_t, size_t>;
+std::map<GemmKey, hipblasLtMatmulAlgo_t> g_algo;
+
+// Fastest of the candidates on stream st (one warm-up run, then two timed
+// runs each); -1 if none runs.
+int fastest_candidate(hipblasLtHandle_t h, hipblasLtMatmulDesc_t desc, hipblasLtMatrixLayout_t la,
+                      hipblasLtMatrixLayout_t lb, hipblasLtMatrixLayout_t lc, const void* act, const void* w,
+                      void* out, void* ws, size_t wsb, hipStream_t st, const hipblasLtMatmulHeuristicResult_t* res,
+                      int found) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return found > 0 ? 0 : -1;
+  }
+  const float one = 1.0f, zero = 0.0f;
+  int best = -1;
+  float best_ms = 0.f;
+  for (int i = 0; i < found; ++i) {
+    auto run = [&]() {
+      return hipblasLtMatmul(h, desc, &one, w, la, act, lb, &zero, out, lc, out, lc, &res[i].algo, ws, wsb, st) ==
+             HIPBLAS_STATUS_SUCCESS;
+    };
+    if (!run()) continue;
+    if (hipEventRecord(e0, st) != hipSuccess || !run() || !run() || hipEventRecord(e1, st) != hipSuccess ||
+        hipEventSynchronize(e1) != hipSuccess)
+      continue;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) continue;
+    if (best < 0 || ms < best_ms) {
+      best = i;
+      best_ms = ms;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  return best;
+}
 }  // namespace
 
 int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, void* out, void* ws,
@@ -206,17 +250,41 @@ int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* 
     if (hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb)) !=
         HIPBLAS_STATUS_SUCCESS)
       break;
-    hipblasLtMatmulHeuristicResult_t res[1];
-    int found = 0;
-    if (hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, 1, res, &found) != HIPBLAS_STATUS_SUCCESS ||
-        found < 1) {
-      snprintf(err, errlen, "hipBLASLt found no algorithm for %lld x %lld x %lld", static_cast<long long>(rows),
-               static_cast<long long>(n), static_cast<long long>(k));
-      rc = 2;
-      break;
+    const GemmKey key{dev, rows, n, k, ws_bytes};
+    hipblasLtMatmulAlgo_t algo;
+    bool have = false;
+    {
+      std::lock_guard<std::mutex> lk(g_lt_mu);
+      const auto it = g_algo.find(key);
+      if (it != g_algo.end()) {
+        algo = it->second;
+        have = true;
+      }
+    }
+    if (!have) {
+      hipblasLtMatmulHeuristicResult_t res[kTuneCandidates];
+      int found = 0;
+      if (hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, kTuneCandidates, res, &found) !=
+              HIPBLAS_STATUS_SUCCESS ||
+          found < 1) {
+        snprintf(err, errlen, "hipBLASLt found no algorithm for %lld x %lld x %lld", static_cast<long long>(rows),
+                 static_cast<long long>(n), static_cast<long long>(k));
+        rc = 2;
+        break;
+      }
+      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
+      int pick = 0;
+      if (cap == hipStreamCaptureStatusNone && found > 1) {
+        pick = fastest_candidate(h, desc, la, lb, lc, act, w, out, ws, wsb, st, res, found);
+        if (pick < 0) pick = 0;
+        std::lock_guard<std::mutex> lk(g_lt_mu);
+        g_algo[key] = res[pick].algo;
+      }
+      algo = res[pick].algo;
     }
     const float one = 1.0f, zero = 0.0f;
-    if (hipblasLtMatmul(h, desc, &one, w, la, act, lb, &zero, out, lc, out, lc, &res[0].algo, ws, wsb, st) !=
+    if (hipblasLtMatmul(h, desc, &one, w, la, act, lb, &zero, out, lc, out, lc, &algo, ws, wsb, st) !=
         HIPBLAS_STATUS_SUCCESS) {
       snprintf(err, errlen, "hipblasLtMatmul failed");
       rc = 2;

@@ -256,7 +256,11 @@ typedef struct muse_block_weights {
 /* muse_attn_block_prefill: the block's attention half over B sequences of T
  * tokens.  x, out: [B, T, hidden] bf16, contiguous.  The projections run as
  * hipBLASLt GEMMs on `stream` with the caller's workspace as their scratch
- * (the library keeps one host-side hipBLASLt handle per device).
+ * (the library keeps one host-side hipBLASLt handle per device).  The first
+ * call with a given GEMM shape on a device times hipBLASLt's candidate
+ * algorithms on that call's operands, waiting for the stream, and later
+ * calls reuse the fastest (a call under stream capture takes hipBLASLt's
+ * first choice instead).
  * workspace: at least muse_attn_block_prefill_workspace_size() bytes.
  * T == 0 or B == 0 is a no-op. */
 int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block_weights* weights,
