@@ -400,6 +400,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   auto half_step = [&](const Half& cur, const Half& nxt, f32x16* s_out, bf16x8 (*p_in)[2], f32x16* s_in,
                        bf16x8 (*p_out)[2]) {
     constexpr int NE = 16;  // logits per lane per row block
+    // Head width 128 has exponentials on every other matrix item and packs
+    // them one item late; at 64 every item has some, and packing at once
+    // measured faster.
+    constexpr bool kLagPack = D == 128;
+    float pend0[MB], pend1[MB];
+    int pend_e = -1;
+    auto pack_pair = [&](int mb, int e, float y0, float y1) {
+      bf16x2 pr;
+      pr[0] = static_cast<bf16_t>(y0);
+      pr[1] = static_cast<bf16_t>(y1);
+      uint32_t pw = __builtin_bit_cast(uint32_t, pr);
+      asm volatile("" : "+v"(pw));
+      pr = __builtin_bit_cast(bf16x2, pw);
+      p_out[mb][e >> 3][e & 7] = pr[0];
+      p_out[mb][e >> 3][(e & 7) + 1] = pr[1];
+      lsum[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[mb], false);
+    };
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(s_in[mb]));
 #pragma unroll
@@ -424,6 +441,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
           o[mb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_in[mb][st], o[mb][db], 0, 0, 0);
       }
       fq[j % QD] = j + QD < NI ? frag(cur, j + QD) : frag(nxt, j + QD - NI);
+      // the previous item's exponentials, packed one matrix item after they
+      // were issued, so the transcendental unit's latency does not hold up
+      // this wave's next MFMA
+      if (pend_e >= 0) {
+        for (int mb = 0; mb < MB; ++mb) pack_pair(mb, pend_e, pend0[mb], pend1[mb]);
+        pend_e = -1;
+      }
       // this item's slice of the exponentials (pairs, so each pair's row sum
       // is one packed dot product)
 #pragma unroll
@@ -436,18 +460,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
           // the exponentials from being hoisted; the one on each output stops
           // machine sinking from moving them into the next block, past the
           // matrix-core work they hide under.
-          const float x0 = s_in[mb][e], x1 = s_in[mb][e + 1];
-          bf16x2 pr;
-          pr[0] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(x0));
-          pr[1] = static_cast<bf16_t>(__builtin_amdgcn_exp2f(x1));
-          uint32_t pw = __builtin_bit_cast(uint32_t, pr);
-          asm volatile("" : "+v"(pw));
-          pr = __builtin_bit_cast(bf16x2, pw);
-          p_out[mb][e >> 3][e & 7] = pr[0];
-          p_out[mb][e >> 3][(e & 7) + 1] = pr[1];
-          lsum[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[mb], false);
+          float x0 = __builtin_amdgcn_exp2f(s_in[mb][e]);
+          float x1 = __builtin_amdgcn_exp2f(s_in[mb][e + 1]);
+          if constexpr (kLagPack) {
+            asm volatile("" : "+v"(x0), "+v"(x1));
+            pend0[mb] = x0;
+            pend1[mb] = x1;
+          } else {
+            pack_pair(mb, e, x0, x1);
+          }
         }
+        if constexpr (kLagPack) pend_e = e;
       }
+    }
+    if (pend_e >= 0) {
+      for (int mb = 0; mb < MB; ++mb) pack_pair(mb, pend_e, pend0[mb], pend1[mb]);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
