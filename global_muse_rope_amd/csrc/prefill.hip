@@ -109,8 +109,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   //   Local layer (uniform work per block): a persistent grid; XCD x owns one
   //   contiguous range of logical blocks and its K workgroups walk it with
   //   stride K, so the XCD works on K consecutive query blocks at a time and
-  //   the window's tiles stay in its L2.  Each workgroup warms the L2 with the
-  //   next block's queries while it computes the current one.
+  //   the window's tiles stay in its L2.
   //   Global layer: one block per workgroup, heaviest (latest) query blocks
   //   first, groups of QC consecutive blocks of one KV head on one XCD.
   const int nlog = a.n_qblocks_pad * a.batch_heads;  // a multiple of 8
