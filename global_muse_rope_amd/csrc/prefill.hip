@@ -5,6 +5,7 @@
 // What it computes (Muse Spark Open deep dive):
 //   section 3.2: q_hat = s * q / sqrt(mean(q^2) + eps), logits q_hat . k_hat / sqrt(D);
 //   section 3.4: RoPE on local layers, causal window i - W < j <= i;
+//   section 8.2: a drafter's block sees the two-sided window |i - j| < W;
 //   section 3.1: query head h reads KV head floor(h / G);
 //   section 3.3: Spark per-head output RMS norm, then y = o * sigmoid(g).
 //
@@ -23,16 +24,20 @@
 //     The S^T accumulator layout is exactly the P^T operand layout of the
 //     second MFMA, so P never leaves registers.
 //   * Tiles are copied verbatim from the pre-swizzled workspace into a
-//     four-buffer LDS ring (three tiles resident, the next in flight); only
-//     tiles crossing the causal diagonal or the window start are masked, and
-//     a wave skips edge tiles it cannot see.  Between the edges the loop is
-//     software-pipelined: the logits of the next half-tile go to the matrix
-//     cores while the exponentials of the current one run on the vector ALUs.
+//     four-buffer LDS ring (three tiles resident, the next in flight); a
+//     block visits only the tiles its rows can see, and only the first and
+//     last of them (crossing the diagonal or a window edge) are masked.  The
+//     loop is software-pipelined: the logits of the next half-tile go to the
+//     matrix cores while the exponentials of the current one run on the
+//     vector ALUs.
 //   * Launch order.  Global layers: heaviest query blocks first (causal work
 //     grows with the block index), and groups of 8 consecutive query blocks
 //     of one KV head land on one XCD so they share K/V tiles in its L2.
 //     Local layers (uniform work): each XCD walks one contiguous range of
 //     query blocks, so the 2048-key window's tiles stay in that XCD's L2.
+//     Launches with fewer query blocks than CUs (a short chunk, a drafter's
+//     block) split each block's tile range over several workgroups, and
+//     prefill_combine_kernel adds the pieces.
 #include <algorithm>
 #include <type_traits>
 
