@@ -147,10 +147,13 @@ struct DecodePlan {
   int max_chunks;
 };
 
+#ifndef MUSE_RING_CHUNK
+#define MUSE_RING_CHUNK 256
+#endif
 DecodePlan decode_plan(int32_t max_kv_len, const muse_kv_cache* c) {
   DecodePlan d;
   if (c->kind == MUSE_KV_RING) {
-    d.chunk_tokens = c->capacity >= 256 ? 256 : ((c->capacity + 31) / 32) * 32;
+    d.chunk_tokens = c->capacity >= MUSE_RING_CHUNK ? MUSE_RING_CHUNK : ((c->capacity + 31) / 32) * 32;
     d.max_chunks = (c->capacity + d.chunk_tokens - 1) / d.chunk_tokens;
   } else {
     d.chunk_tokens = kPagedChunk;
