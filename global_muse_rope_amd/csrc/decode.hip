@@ -502,10 +502,30 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 // 3. combine + epilogue: one workgroup per (sequence, KV head); wave w takes
 // heads w, w + 4, ...; lane = dim (two dims per lane when D = 128).
 // ---------------------------------------------------------------------------
+// Combine: one workgroup per (sequence, KV head) merges the chunk partials
+// of its G query heads and adds the new token's own term.  The chunks are
+// spread over NWC waves (chunk c to wave c mod NWC) so their loads overlap:
+// each wave first takes the maximum over its chunks of every head, then,
+// after the workgroup's maximum is known, sums its chunks' rescaled partials;
+// the waves' sums meet in LDS, and wave w finishes heads w, w + NWC, ...
+// (1/sum, output norm, gate).
 template <int D, int G>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+struct CombineShape {
+  static constexpr int NWC = G * D > 1024 ? 8 : 16;  // waves (LDS: NWC * G * D floats)
+};
+
+template <int D, int G>
+__global__ __launch_bounds__((CombineShape<D, G>::NWC * 64)) void decode_combine_kernel(DecodeArgs a) {
+  constexpr int NWC = CombineShape<D, G>::NWC;
   constexpr int PER = D / 64;
+  constexpr int ROW = G * (D + 2);  // floats of one chunk's partial: per head O[D], m, l
+  constexpr int CPI = 64 / G;       // chunks one wave reads per step of the maximum pass
   constexpr float NEG = -1.0e30f;
+  static_assert(64 % G == 0, "the heads tile a wave");
+  __shared__ float s_new[G];
+  __shared__ float s_max[NWC][G];
+  __shared__ float s_l[NWC][G];
+  __shared__ float s_acc[NWC][G][D];
   const int bh = blockIdx.x;
   const int b = bh / a.Hkv;
   const int hk = bh - b * a.Hkv;
@@ -514,38 +534,85 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int L = a.kv_len[b];
   const bool len_ok = decode_len_ok(L, a.max_kv_len);
   const int nch = len_ok ? hist_chunks(hist_range(a, L), a.chunk_tokens) : 0;
-  const float* kn = a.khat + static_cast<int64_t>(bh) * D;
-  const uint16_t* vn = a.v_new + static_cast<int64_t>(bh) * D;
-  for (int hh = w; hh < G; hh += 4) {
-    const int hq = hk * G + hh;
-    const float* qp = a.qhat + (static_cast<int64_t>(b) * a.Hkv * G + hq) * D;
-    // the new token's own logit (log2 units) and value
+  const float* part = a.part + static_cast<int64_t>(bh) * a.max_chunks * ROW;
+
+  // the new token's own logit (log2 units) of heads w, w + NWC, ...
+  for (int g = w; g < G; g += NWC) {
+    const float* qp = a.qhat + (static_cast<int64_t>(b) * a.Hkv * G + hk * G + g) * D;
+    const float* kn = a.khat + static_cast<int64_t>(bh) * D;
     float dot = 0.f;
 #pragma unroll
     for (int e = 0; e < PER; ++e) dot += qp[lane + 64 * e] * kn[lane + 64 * e];
-    const float snew = wave_sum(dot);
-    float mm = snew;
-    const float* part = a.part + static_cast<int64_t>(bh) * a.max_chunks * (G * (D + 2)) + hh * (D + 2);
-    for (int ci = 0; ci < nch; ++ci) mm = fmaxf(mm, part[static_cast<int64_t>(ci) * G * (D + 2) + D]);
-    const float fnew = __builtin_amdgcn_exp2f(snew - mm);
-    float ls = fnew;
-    float acc[PER];
+    dot = wave_sum(dot);
+    if (lane == 0) s_new[g] = dot;
+  }
+  // maximum over this wave's chunks: lane -> (head lane mod G, chunk lane / G)
+  {
+    const int g = lane % G;
+    float m = NEG;
+    for (int c = w * CPI + lane / G; c < nch; c += NWC * CPI)
+      m = fmaxf(m, part[static_cast<int64_t>(c) * ROW + g * (D + 2) + D]);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fnew * bf16_bits_to_f32(vn[lane + 64 * e]);
-    for (int ci = 0; ci < nch; ++ci) {
-      const float* pc = part + static_cast<int64_t>(ci) * G * (D + 2);
-      const float mc = pc[D];
-      const float f = mc > NEG ? __builtin_amdgcn_exp2f(mc - mm) : 0.f;
-      ls += f * pc[D + 1];
+    for (int off = G; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    if (lane < G) s_max[w][lane] = m;
+  }
+  __syncthreads();
+  float mm[G];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] += f * pc[lane + 64 * e];
+  for (int g = 0; g < G; ++g) {
+    float x = s_new[g];
+#pragma unroll
+    for (int i = 0; i < NWC; ++i) x = fmaxf(x, s_max[i][g]);
+    mm[g] = x;
+  }
+  // this wave's chunks, rescaled to the workgroup's maximum
+  float acc[G][PER], ls[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    ls[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[g][e] = 0.f;
+  }
+#pragma unroll 2
+  for (int c = w; c < nch; c += NWC) {
+    const float* pc = part + static_cast<int64_t>(c) * ROW;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float mc = pc[g * (D + 2) + D];
+      const float f = mc > NEG ? __builtin_amdgcn_exp2f(mc - mm[g]) : 0.f;
+      ls[g] += f * pc[g * (D + 2) + D + 1];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[g][e] += f * pc[g * (D + 2) + lane + 64 * e];
     }
-    const float inv = 1.0f / ls;
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) s_acc[w][g][lane + 64 * e] = acc[g][e];
+    if (lane == 0) s_l[w][g] = ls[g];
+  }
+  __syncthreads();
+  // heads w, w + NWC, ...: the new token's term, the waves' sums, then the epilogue
+  const uint16_t* vn = a.v_new + static_cast<int64_t>(bh) * D;
+  for (int g = w; g < G; g += NWC) {
+    const int hq = hk * G + g;
+    const float fnew = __builtin_amdgcn_exp2f(s_new[g] - mm[g]);
+    float l = fnew;
+#pragma unroll
+    for (int i = 0; i < NWC; ++i) l += s_l[i][g];
+    float o[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      o[e] = fnew * bf16_bits_to_f32(vn[lane + 64 * e]);
+#pragma unroll
+      for (int i = 0; i < NWC; ++i) o[e] += s_acc[i][g][lane + 64 * e];
+    }
+    const float inv = 1.0f / l;
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      acc[e] *= inv;
-      ss += acc[e] * acc[e];
+      o[e] *= inv;
+      ss += o[e] * o[e];
     }
     float rsn = 1.0f;
     if (a.out_norm) rsn = 1.0f / sqrtf(wave_sum(ss) * (1.0f / D) + a.out_eps);
@@ -553,8 +620,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     uint16_t* op = a.out + (static_cast<int64_t>(b) * a.Hkv * G + hq) * D;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const float g = bf16_bits_to_f32(gp[lane + 64 * e]);
-      const float y = len_ok ? acc[e] * rsn / (1.0f + __expf(-g)) : 0.f;
+      const float gv = bf16_bits_to_f32(gp[lane + 64 * e]);
+      const float y = len_ok ? o[e] * rsn / (1.0f + __expf(-gv)) : 0.f;
       op[lane + 64 * e] = f32_to_bf16_bits(y);
     }
   }
@@ -582,7 +649,7 @@ hipError_t launch_dg(const DecodeArgs& a, hipStream_t st, hipEvent_t ev0, hipEve
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (ev1 && (e = hipEventRecord(ev1, st)) != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D, G>), dim3(a.B * a.Hkv), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D, G>), dim3(a.B * a.Hkv), dim3(CombineShape<D, G>::NWC * 64), 0, st, a);
   return hipGetLastError();
 }
 
