@@ -185,3 +185,92 @@ def test_rope_qknorm_argument_checks():
     assert f(ctypes.byref(p), 4, FAKE, 100, None, 0, None, FAKE, None, 0, None) == 1      # stride < Hq * D
     assert f(ctypes.byref(p), 0, FAKE, 4096, None, 0, None, FAKE, None, 0, None) == 0     # empty: no-op
     assert f(ctypes.byref(p), -1, FAKE, 4096, None, 0, None, FAKE, None, 0, None) == 1
+
+
+TILE_BYTES = {128: (64 * 17 + 128 * 9) * 16, 64: (64 * 9 + 64 * 9) * 16}  # one 64-key tile image
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("name", ["muse_attn_prefill_chunk", "muse_attn_draft_block"])
+def test_chunk_and_draft_argument_checks(name):
+    capi, lib = _lib()
+    p = params(capi)  # a Glimmer local layer: 32/2 heads x 128, window 2048
+    f, wsf = getattr(lib, name), getattr(lib, name + "_workspace_size")
+    ring = capi.MuseKvCache(capi.MUSE_KV_RING, 2048, FAKE, FAKE, None, 0, 0, 0)
+    need = wsf(ctypes.byref(p), 2, 16, 4096)
+    assert need > 0
+
+    def call(B=2, T=16, max_start=4096, cache=ring, ws=need, start=FAKE, q=FAKE, pp=p):
+        return f(ctypes.byref(pp), B, T, q, FAKE, FAKE, FAKE, None, start, max_start,
+                 ctypes.byref(cache) if cache is not None else None, FAKE, FAKE, ws, None)
+
+    assert call(T=-1) == 1
+    assert call(max_start=-1) == 1
+    assert call(max_start=0x7FFFFFFF) == 2          # positions past the 32-bit range
+    assert call(cache=None) == 1
+    assert call(start=None) == 1
+    assert call(q=FAKE + 2) == 1                    # misaligned tensor
+    assert call(ws=need - 1) == 3
+    assert call(B=0) == 0 and call(T=0) == 0        # empty problems are no-ops
+    assert call(cache=capi.MuseKvCache(capi.MUSE_KV_RING, 1024, FAKE, FAKE, None, 0, 0, 0)) == 1  # capacity != W
+    # a paged cache of 4096 positions on a global layer: a chunk writes positions up to
+    # max_start + T - 1 and needs them all; a drafter's block only reads below max_start
+    pg = params(capi, sliding_window=0, rope_theta=0.0)
+    paged = capi.MuseKvCache(capi.MUSE_KV_PAGED, 0, FAKE, FAKE, FAKE, 128, 32, 10000)
+    need_g = wsf(ctypes.byref(pg), 2, 16, 4096)
+    rc = call(cache=paged, pp=pg, ws=need_g - 1)
+    assert rc == (1 if name == "muse_attn_prefill_chunk" else 3)
+
+
+def test_chunk_workspace_covers_key_pieces():
+    """A launch with fewer query blocks than CUs splits each block over key
+    pieces and needs room for their fp32 partial sums; one with many blocks
+    needs only the tile images and the RoPE table."""
+    capi, lib = _lib()
+    p = params(capi)  # G = 16: one query block covers 16 tokens
+    B, hkv, d, hq = 16, 2, 128, 32
+    tiles = lambda T, hist: B * hkv * ((hist + T + 63) // 64) * TILE_BYTES[d]
+    rope = lambda T: B * T * (d // 2) * 8
+    hist = 2047 + 63                                    # the window's history, rounded down to a tile
+    for name in ("muse_attn_prefill_chunk_workspace_size", "muse_attn_draft_block_workspace_size"):
+        wsf = getattr(lib, name)
+        # 16 tokens: 32 query blocks, split
+        small = wsf(ctypes.byref(p), B, 16, 131072)
+        base = _align(tiles(16, hist)) + _align(rope(16))
+        assert small >= base + 2 * B * 16 * hq * (d + 1) * 4
+        # 4096 tokens: 512 query blocks, not split
+        big = wsf(ctypes.byref(p), B, 4096, 131072)
+        assert big == _align(tiles(4096, hist)) + _align(rope(4096))
+
+
+def test_block_prefill_argument_checks():
+    capi, lib = _lib()
+    p = params(capi, num_q_heads=128, num_kv_heads=16, head_dim=64, qk_scale=5.473, out_norm=1)
+    f, wsf = lib.muse_attn_block_prefill, lib.muse_attn_block_prefill_workspace_size
+
+    def weights(hidden=8192, gate=FAKE, temp=0.3, post=None, w_o=FAKE):
+        return capi.MuseBlockWeights(hidden, FAKE, FAKE, w_o, post, gate, temp)
+
+    w = weights()
+    need = wsf(ctypes.byref(p), ctypes.byref(w), 1, 256)
+    assert need > 0
+
+    def call(wt=w, B=1, T=256, ws=need, x=FAKE):
+        return f(ctypes.byref(p), ctypes.byref(wt) if wt is not None else None, B, T, x, FAKE, FAKE, ws, None)
+
+    assert call(wt=None) == 1
+    assert call(B=-1) == 1
+    assert call(wt=weights(hidden=8190)) == 2           # not a multiple of 8
+    assert call(wt=weights(hidden=16384)) == 2          # wider than the row kernels take
+    assert call(wt=weights(w_o=None)) == 1
+    assert call(wt=weights(temp=0.0)) == 1              # residual gate needs a positive temperature
+    assert call(wt=weights(gate=None)) == 1             # a plain add needs post_norm
+    assert call(B=0) == 0 and call(T=0) == 0
+    assert call(x=None) == 1
+    assert call(ws=need - 1) == 3
+    # the workspace holds the bf16 intermediates (h, the projection, o, a) at least
+    n = (2 * 128 + 2 * 16) * 64
+    assert need >= 256 * (8192 + n + 128 * 64 + 8192) * 2
