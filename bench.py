@@ -405,7 +405,7 @@ def main():
         traffic_summary(*args.traffic_summary, args.commands)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
