@@ -36,6 +36,11 @@ as stored (bf16, already normalized and rotated).  A prefill chunk continuing
 a cached sequence reads its history the same way, and its own tokens sit at
 positions start .. start + T - 1; a drafter's non-causal block sees the same
 history and every block key within the window in both directions.
+
+A flagged second mode (``reference_rounding``) rounds the normalized query,
+its product with s, and the normalized key to bf16 where the pages'
+reference implementation casts them (section 3.2 implementation notes).  It
+is reported beside the plain fp64 oracle and never replaces it.
 """
 from .attention import (  # noqa: F401
     layer_is_global,
@@ -43,6 +48,7 @@ from .attention import (  # noqa: F401
     visible_range,
     visible_mask,
     rms_normalize,
+    to_bf16,
     rope_inv_freq,
     rope_rotate,
     query_prologue,

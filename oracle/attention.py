@@ -85,21 +85,44 @@ def rope_rotate(x, positions, theta: float) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
-def query_prologue(q, positions, layer):
+def to_bf16(x) -> np.ndarray:
+    """The bf16 value nearest to each entry (round to nearest, ties to even),
+    reached through float32 as a float32 tensor cast to bfloat16 is: the
+    float32 bits are rounded at bit 16."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    r = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return (r.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def query_prologue(q, positions, layer, reference_rounding: bool = False):
     """q_hat = s * norm(q), then RoPE at the query's position if theta != 0.
     q [T, Hq, D], positions [T].  Deep dive, section 3.2 steps 2-4: normalize
     each head (fp32 in the reference, fp64 here), multiply only the query by
-    qk_scale_factor, rotate (local layers only)."""
-    qh = rms_normalize(q, layer.qk_eps) * np.float64(layer.scale)
+    qk_scale_factor, rotate (local layers only).
+
+    reference_rounding (a flagged second mode, never the parity reference):
+    round where the pages' reference implementation does (section 3.2
+    implementation notes): the normalized query is cast back to bf16, and the
+    product with qk_scale_factor (a float32 scalar) is bf16 again.  RoPE and
+    everything after stay fp64."""
+    qh = rms_normalize(q, layer.qk_eps)
+    if reference_rounding:
+        qh = to_bf16(to_bf16(qh) * np.float64(np.float32(layer.scale)))
+    else:
+        qh = qh * np.float64(layer.scale)
     if layer.theta != 0:
         qh = rope_rotate(qh, positions, layer.theta)
     return qh
 
 
-def key_prologue(k, positions, layer):
+def key_prologue(k, positions, layer, reference_rounding: bool = False):
     """k_hat = norm(k), then RoPE if theta != 0 (no multiplier on keys).
-    k [T, Hkv, D], positions [T].  V is not touched."""
+    k [T, Hkv, D], positions [T].  V is not touched.  reference_rounding:
+    the normalized key is cast back to bf16 (see query_prologue)."""
     kh = rms_normalize(k, layer.qk_eps)
+    if reference_rounding:
+        kh = to_bf16(kh)
     if layer.theta != 0:
         kh = rope_rotate(kh, positions, layer.theta)
     return kh
@@ -173,12 +196,13 @@ def output_epilogue(o, gate, layer) -> np.ndarray:
 # Whole-layer entry points
 # ---------------------------------------------------------------------------
 
-def prefill(q, k, v, gate, layer, positions=None, rows=None) -> np.ndarray:
+def prefill(q, k, v, gate, layer, positions=None, rows=None, reference_rounding: bool = False) -> np.ndarray:
     """The layer on one sequence: q, gate [T, Hq, D]; k, v [T', Hkv, D].
 
     ``rows`` (token indices) selects the output rows; q and gate then hold
     only those rows, while k and v hold tokens 0 .. max(rows).  Positions
-    default to the token index.  Returns y [n_rows, Hq, D] in float64."""
+    default to the token index.  reference_rounding selects the flagged
+    second mode of the prologues.  Returns y [n_rows, Hq, D] in float64."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -188,8 +212,8 @@ def prefill(q, k, v, gate, layer, positions=None, rows=None) -> np.ndarray:
     if positions is None:
         positions = np.arange(k.shape[0], dtype=np.int64)
     positions = np.asarray(positions, dtype=np.int64)
-    qh = query_prologue(q, positions[rows], layer)
-    kh = key_prologue(k, positions[:k.shape[0]], layer)
+    qh = query_prologue(q, positions[rows], layer, reference_rounding)
+    kh = key_prologue(k, positions[:k.shape[0]], layer, reference_rounding)
     o = attend_rows(qh, rows, kh, v, layer)
     return output_epilogue(o, gate, layer)
 

@@ -504,7 +504,7 @@ def test_planted_mistakes_fail_the_library_pin(monkeypatch, mistake):
     elif mistake == "no_query_scale":
         from dataclasses import replace
         orig = A.query_prologue
-        monkeypatch.setattr(A, "query_prologue", lambda q, p, l: orig(q, p, replace(l, scale=1.0)))
+        monkeypatch.setattr(A, "query_prologue", lambda q, p, l, *rest: orig(q, p, replace(l, scale=1.0), *rest))
     rng = np.random.default_rng(10)
     q, k, v, g = _rand_layer_inputs(rng, 37, layer)
     pos = np.arange(37) + 1000
@@ -681,3 +681,55 @@ def _block_one_sided(q, k, v, g, k_hist, v_hist, hs, start, layer):
         for h in range(layer.hq):
             o[t, h] = w[h] @ vals[lo:, h // layer.group, :]
     return oracle.output_epilogue(o, g, layer)
+
+
+# ---------------------------------------------------------------------------
+# The flagged reference-rounding mode (reported beside the oracle, never the
+# parity reference)
+# ---------------------------------------------------------------------------
+
+def test_to_bf16_rounds_to_nearest_even():
+    # 1 + 2^-8 lies halfway between bf16 neighbours 1 and 1 + 2^-7: ties go to the even one (1.0)
+    x = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 3.87, 5.4730064863875, -0.1, 65504.0, 1e-40])
+    y = oracle.to_bf16(x)
+    assert y[0] == 1.0 and y[1] == 1.0 and y[2] == 1.0 + 2.0 ** -6
+    assert y[3] == 3.875 and y[4] == 5.46875            # bf16(3.87) and bf16(5.473...)
+    assert abs(y[5] + 0.1) <= 2.0 ** -12 and y[6] == 65536.0
+    # every result is a bf16 value: its float32 bits end in 16 zero bits
+    assert np.all(y.astype(np.float32).view(np.uint32) & 0xFFFF == 0)
+
+
+@pytest.mark.parametrize("scale,d", [(3.87, 128), (5.4730064863875, 64)])
+def test_reference_rounding_moves_the_aligned_logit_to_the_rounded_multiplier(scale, d):
+    """Aligned all-ones q and k: the plain oracle's logit is s * sqrt(d) * m / (m + 1e-5) with
+    m = 1 (43.7836 on both models, the pages' eps figure); with the reference's casts the
+    normalized entries round to 1 and the product q_hat * s to bf16, so the logit becomes
+    bf16(s) * sqrt(d) (3.875 * sqrt(128) = 43.84; 5.46875 * 8 = 43.75)."""
+    layer = Layer(hq=1, hkv=1, d=d, window=0, theta=0.0, scale=scale)
+    ones = np.ones((1, 1, d))
+    plain = oracle.logits_for_row(oracle.query_prologue(ones, [0], layer)[0],
+                                  oracle.key_prologue(ones, [0], layer), 1)[0, 0]
+    qr = oracle.query_prologue(ones, [0], layer, reference_rounding=True)
+    kr = oracle.key_prologue(ones, [0], layer, reference_rounding=True)
+    rounded = oracle.logits_for_row(qr[0], kr, 1)[0, 0]
+    assert abs(plain - scale * np.sqrt(d) / (1 + 1e-5)) < 1e-12
+    assert abs(rounded - oracle.to_bf16(scale)[()] * np.sqrt(d)) < 1e-12
+    assert abs(rounded - plain) > 1e-2
+
+
+def test_reference_rounding_stays_within_the_bf16_budget():
+    """On N(0,1) inputs the flagged mode moves outputs by the bf16 rounding of q_hat,
+    q_hat * s and k_hat only.  The logit error is about s * 2^-9 per unit, so each
+    softmax weight moves by about 1 % and the largest of a few thousand outputs by a
+    few 1e-2: more than the 2e-2 parity tolerance the GPU path meets with fp16
+    operands, which is why the flagged mode is reported and never the reference."""
+    rng = np.random.default_rng(70)
+    for layer in (Layer(hq=8, hkv=2, d=64, window=16, theta=10000.0, scale=SPARK_SCALE, out_norm=True,
+                        out_eps=1e-6),
+                  Layer(hq=4, hkv=1, d=128, window=0, theta=0.0, scale=GLIMMER_SCALE)):
+        T = 40
+        q, k, v, g = _rand_layer_inputs(rng, T, layer)
+        y = oracle.prefill(q, k, v, g, layer)
+        yr = oracle.prefill(q, k, v, g, layer, reference_rounding=True)
+        diff = np.max(np.abs(y - yr))
+        assert 1e-3 < diff < 0.1
