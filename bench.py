@@ -295,7 +295,19 @@ def cpu_baseline(cfg, gpu_out, budget_s=15.0):
             "sample": f"{done} query rows (all {L.hq} heads) of {cfg.name}, chosen by a seeded permutation "
                       f"plus window-edge rows; {flops / 1e9:.1f} GFLOP in {elapsed:.1f} s of oracle time "
                       f"({wall:.1f} s with input regeneration)",
-            "gpu_max_abs_err_on_sample": worst}
+            "gpu_max_abs_err_on_sample": worst, "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def pmc_pass(torch, ma, workload):
