@@ -136,3 +136,21 @@ def test_planted_block_mistakes_fail_the_library_pin(monkeypatch, mistake):
         monkeypatch.setattr(OB, "residual_gate", lambda x_, f, g, temperature=0.3, alpha_sq_floor=1e-3: x_ + f)
     y = OB.attention_block(x, W, layer)
     assert not np.allclose(y, ref, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("layer,spark,hidden", BLOCK_LAYERS, ids=["spark-like", "glimmer-like"])
+def test_block_decode_equals_last_row_of_prefill_block(layer, spark, hidden):
+    """A one-token decode block over a history holding the sequence's own earlier
+    keys (normalized and rotated, unrounded) and values equals the last row of the
+    prefill block on the whole sequence; a history one key short is rejected."""
+    rng = np.random.default_rng(62)
+    T = 19
+    x = rng.standard_normal((T, hidden))
+    W = block_weights(rng, hidden, layer, spark)
+    _, k, v, _ = OB.input_projections(x, W, layer)
+    kh = oracle.key_prologue(k, np.arange(T), layer)
+    y_dec = OB.attention_block_decode(x[T - 1], W, layer, kh[:T - 1], v[:T - 1], 0, T)
+    y_pre = OB.attention_block(x, W, layer)[T - 1]
+    assert np.allclose(y_dec, y_pre, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        OB.attention_block_decode(x[T - 1], W, layer, kh[:T - 2], v[:T - 2], 0, T)
