@@ -195,6 +195,41 @@ def block_case(cfg, steps, warmup, events, torch, ma):
     return res
 
 
+def block_decode_case(cfg, steps, warmup, events, torch, ma, flush=False):
+    """One new token per sequence of a decode workload through the attention half
+    of a decoder block (hidden 8192, the seeded synthetic weights of the block
+    workload) over that workload's cache."""
+    from synth.device import decode_device_setup, block_device_setup
+    from synth.workloads import SPARK_BLOCK_LOCAL, S_X
+    from synth import normal_bf16_torch_tensor
+    L = cfg.layer
+    s = decode_device_setup(cfg)
+    if s["kind"] == "ring":
+        cache = ma.KvCache.ring(s["kc"], s["vc"])
+    else:
+        cache = ma.KvCache.paged(s["kc"], s["vc"], s["block_table"], s["page_tokens"])
+    w = block_device_setup(SPARK_BLOCK_LOCAL)   # the weights depend on the head shape and width only
+    wb = ma.BlockWeights(in_norm=w["in_norm"], w_qkvg=w["w_qkvg"], w_o=w["w_o"], residual_gate=w["residual_gate"],
+                         post_norm=w["post_norm"])
+    lp = ma.LayerParams.from_layer(L)
+    x = normal_bf16_torch_tensor(cfg.seed, S_X, (cfg.batch, SPARK_BLOCK_LOCAL.hidden), "cuda")
+    out = torch.empty_like(x)
+    ws = torch.empty(ma.block_decode_workspace_size(lp, wb, cfg.batch, s["max_len"], cache), dtype=torch.uint8,
+                     device="cuda")
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if flush else None
+
+    def step():
+        if scrub is not None:
+            scrub.view(torch.int64).sum()   # evict the 256 MB last-level cache (a read: no dirty lines left)
+        ma.attention_block_decode(lp, wb, x, s["kv_len"], s["max_len"], cache, out=out, workspace=ws)
+
+    wall, kern = timed_steps(step, steps, warmup, events, torch)
+    res = {"ms_per_step": wall, "decode_kernel_ms": kern}
+    del s, cache, w, wb, x, out, ws, scrub
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False):
     from synth.device import decode_device_setup
     from global_muse_rope_amd import accounting as acc
@@ -213,7 +248,9 @@ def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False):
 
     def step():
         if scrub is not None:
-            scrub.fill_(1)     # evict the 256 MB last-level cache between steps
+            # evict the 256 MB last-level cache between steps with a 512 MB read: a write
+            # would leave dirty lines whose write-back then competes with the step's reads
+            scrub.view(torch.int64).sum()
         ma.decode(lp, s["q"], s["k"], s["v"], s["g"], s["kv_len"], s["max_len"], s["cache"], out=out, workspace=ws)
 
     wall, kern = timed_steps(step, steps, warmup, events, torch)
@@ -372,9 +409,16 @@ def only_case(name, steps, warmup, torch, ma):
     """Time one workload by itself (for a per-workload kernel trace)."""
     from synth import workloads as wl
     fp8 = name.endswith("_fp8")
-    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE + wl.CHUNK + wl.DRAFT + wl.BLOCKS}[name[:-4] if fp8 else name]
+    through_block = name.endswith("_block")
+    base = name[:-4] if fp8 else name[:-6] if through_block else name
+    cfg = {c.name: c for c in wl.PREFILL + wl.DECODE + wl.CHUNK + wl.DRAFT + wl.BLOCKS}[base]
     events = HipEvents()
-    if cfg in wl.BLOCKS:
+    if through_block and cfg in wl.DECODE:
+        r = block_decode_case(cfg, steps, warmup, events, torch, ma, flush=cfg.layer.window > 0)
+        print(json.dumps({"workload": name, "ms_per_step": round(r["ms_per_step"], 4),
+                          "decode_kernel_ms": round(r["decode_kernel_ms"], 4), "steps": steps, "warmup": warmup}),
+              flush=True)
+    elif cfg in wl.BLOCKS:
         r = block_case(cfg, steps, warmup, events, torch, ma)
         print(json.dumps({"workload": name, "ms_per_step": round(r["ms_per_step"], 4),
                           "step_TFLOP/s": round(r["tflops"], 2), "attn_kernel_ms": round(r["attn_kernel_ms"], 4),
@@ -524,6 +568,15 @@ def main():
             blocks[kcfg.name] = {"ms_per_step": round(r["ms_per_step"], 4), "tflops_step": round(r["tflops"], 2),
                                  "attn_kernel_ms": round(r["attn_kernel_ms"], 4)}
         result["attention_block"] = blocks
+        block_dec = {}
+        for dcfg in wl.DECODE:
+            log(f"decode through the block: {dcfg.name}")
+            r = block_decode_case(dcfg, 5, 1, events, torch, ma, flush=dcfg.layer.window > 0)
+            log(f"  {r['ms_per_step']:.3f} ms per step (decode split kernel {r['decode_kernel_ms']:.3f} ms)")
+            block_dec[dcfg.name] = {"ms_per_step": round(r["ms_per_step"], 4),
+                                    "decode_kernel_ms": round(r["decode_kernel_ms"], 4),
+                                    "cache_flushed": dcfg.layer.window > 0}
+        result["attention_block_decode"] = block_dec
 
     if not args.quick:
         other = {}

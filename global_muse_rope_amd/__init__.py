@@ -339,3 +339,40 @@ def attention_block_prefill(layer: LayerParams, weights: BlockWeights, x, out=No
                                             _stream()))
     return out
 
+
+def block_decode_workspace_size(layer: LayerParams, weights: BlockWeights, batch: int, max_kv_len: int,
+                                cache: KvCache) -> int:
+    p = layer.c()
+    w = weights.c()
+    c = cache.c()
+    return int(_capi.load().muse_attn_block_decode_workspace_size(ctypes.byref(p), ctypes.byref(w), batch,
+                                                                   max_kv_len, ctypes.byref(c)))
+
+
+def attention_block_decode(layer: LayerParams, weights: BlockWeights, x, kv_len, max_kv_len: int, cache: KvCache,
+                           out=None, workspace=None):
+    """One new token per sequence through a decoder block's attention half: x [B, hidden]
+    (bf16, contiguous), kv_len int32 device [B] including the new token.  Appends the new
+    key and value to the cache and returns out [B, hidden] bf16."""
+    torch = _torch()
+    lib = _capi.load()
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous device bf16 tensor [B, hidden]")
+    B, H = (int(s) for s in x.shape)
+    if H != weights.hidden:
+        raise ValueError("x width does not match the weights")
+    if kv_len.dtype != torch.int32 or not kv_len.is_cuda or kv_len.numel() != B:
+        raise ValueError("kv_len must be a device int32 tensor of B entries")
+    if out is None:
+        out = torch.empty_like(x)
+    need = block_decode_workspace_size(layer, weights, B, max_kv_len, cache)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    p = layer.c()
+    w = weights.c()
+    c = cache.c()
+    _capi.check(lib.muse_attn_block_decode(ctypes.byref(p), ctypes.byref(w), B, x.data_ptr(), kv_len.data_ptr(),
+                                           int(max_kv_len), ctypes.byref(c), out.data_ptr(), workspace.data_ptr(),
+                                           workspace.numel() * workspace.element_size(), _stream()))
+    return out
+

@@ -263,11 +263,20 @@ BlockWs block_ws_layout(const muse_attn_params* p, const muse_block_weights* w, 
   return l;
 }
 
+// The decode step through the block: the same buffers for B one-token rows,
+// then the decode workspace instead of the prefill one.
+BlockWs block_decode_ws_layout(const muse_attn_params* p, const muse_block_weights* w, int32_t B,
+                               int32_t max_kv_len, const muse_kv_cache* c) {
+  BlockWs l = block_ws_layout(p, w, B, 1);
+  l.total = l.attn + decode_ws(p, B, max_kv_len, c);
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
 
-int32_t muse_version(void) { return 104; }
+int32_t muse_version(void) { return 105; }
 
 const char* muse_last_error(void) { return g_err; }
 
@@ -613,6 +622,10 @@ int32_t chunk_call(const muse_attn_params* params, int32_t B, int32_t T, const v
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "chunk append launch: %s", hipGetErrorString(e));
   return ok();
 }
+int32_t decode_call(const muse_attn_params* params, int32_t B, const void* q_new, int64_t q_sb, const void* k_new,
+                    const void* v_new, int64_t kv_sb, const void* gate, int64_t g_sb, const int32_t* kv_len,
+                    int32_t max_kv_len, const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes,
+                    void* stream);
 }  // namespace
 
 extern "C" {
@@ -648,6 +661,24 @@ size_t muse_attn_decode_workspace_size(const muse_attn_params* params, int32_t B
 int32_t muse_attn_decode(const muse_attn_params* params, int32_t B, const void* q_new, const void* k_new,
                          const void* v_new, const void* gate, const int32_t* kv_len, int32_t max_kv_len,
                          const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  const int32_t rc = check_params(params);
+  if (rc) return rc;
+  const int64_t qs = static_cast<int64_t>(params->num_q_heads) * params->head_dim;
+  const int64_t ks = static_cast<int64_t>(params->num_kv_heads) * params->head_dim;
+  return decode_call(params, B, q_new, qs, k_new, v_new, ks, gate, qs, kv_len, max_kv_len, cache, out, workspace,
+                     ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+// One decode step; q_new and gate rows of each sequence are q_sb and g_sb
+// elements apart, k_new and v_new rows kv_sb (contiguous for the public
+// entry point, the projection rows for the decoder block).
+int32_t decode_call(const muse_attn_params* params, int32_t B, const void* q_new, int64_t q_sb, const void* k_new,
+                    const void* v_new, int64_t kv_sb, const void* gate, int64_t g_sb, const int32_t* kv_len,
+                    int32_t max_kv_len, const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes,
+                    void* stream) {
   int32_t rc = check_params(params);
   if (rc) return rc;
   if (B < 0) return fail(MUSE_ERR_INVALID_ARG, "B must be >= 0");
@@ -673,6 +704,9 @@ int32_t muse_attn_decode(const muse_attn_params* params, int32_t B, const void* 
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.gate = static_cast<const uint16_t*>(gate);
+  a.q_sb = q_sb;
+  a.kv_sb = kv_sb;
+  a.g_sb = g_sb;
   a.kv_len = kv_len;
   a.out = static_cast<uint16_t*>(out);
   a.kc = static_cast<uint16_t*>(cache->k);
@@ -708,6 +742,9 @@ int32_t muse_attn_decode(const muse_attn_params* params, int32_t B, const void* 
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
+}  // namespace
+
+extern "C" {
 
 size_t muse_attn_block_prefill_workspace_size(const muse_attn_params* params, const muse_block_weights* weights,
                                               int32_t B, int32_t T) {
@@ -784,6 +821,89 @@ int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block
   ra.coef = reinterpret_cast<const float*>(coef);
   ra.out = static_cast<uint16_t*>(out);
   ra.rows = R;
+  ra.hidden = w->hidden;
+  ra.eps = 1e-8f;
+  e = launch_block_residual(ra, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "residual launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t muse_attn_block_decode_workspace_size(const muse_attn_params* params, const muse_block_weights* weights,
+                                             int32_t B, int32_t max_kv_len, const muse_kv_cache* cache) {
+  if (check_params(params) || !weights || !cache || B < 0 || max_kv_len < 1) return 0;
+  return block_decode_ws_layout(params, weights, B, max_kv_len, cache).total;
+}
+
+int32_t muse_attn_block_decode(const muse_attn_params* params, const muse_block_weights* w, int32_t B,
+                               const void* x, const int32_t* kv_len, int32_t max_kv_len, const muse_kv_cache* cache,
+                               void* out, void* workspace, size_t ws_bytes, void* stream) {
+  int32_t rc = check_params(params);
+  if (rc) return rc;
+  if (!w) return fail(MUSE_ERR_INVALID_ARG, "weights is NULL");
+  if (B < 0) return fail(MUSE_ERR_INVALID_ARG, "B must be >= 0");
+  if (max_kv_len < 1) return fail(MUSE_ERR_INVALID_ARG, "max_kv_len must be >= 1");
+  if (w->hidden <= 0 || w->hidden % 8 != 0 || w->hidden > kBlockMaxHidden)
+    return fail(MUSE_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 8 up to %d", w->hidden,
+                kBlockMaxHidden);
+  if (!w->in_norm || !w->w_qkvg || !w->w_o) return fail(MUSE_ERR_INVALID_ARG, "a weight pointer is NULL");
+  if (w->residual_gate ? !(w->residual_gate_temperature > 0.f) : !w->post_norm)
+    return fail(MUSE_ERR_INVALID_ARG, "a plain add needs post_norm; a residual gate a positive temperature");
+  rc = check_cache(params, B, max_kv_len, cache);
+  if (rc) return rc;
+  if (B == 0) return ok();
+  if (!x || !out || !kv_len) return fail(MUSE_ERR_INVALID_ARG, "x, out or kv_len is NULL");
+  const void* ptrs[] = {x, out, w->in_norm, w->w_qkvg, w->w_o, w->post_norm, w->residual_gate};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return fail(MUSE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (!workspace || !aligned16(workspace)) return fail(MUSE_ERR_WORKSPACE, "workspace missing or misaligned");
+  const BlockWs l = block_decode_ws_layout(params, w, B, max_kv_len, cache);
+  if (ws_bytes < l.total) return fail(MUSE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, l.total);
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
+  const int64_t N = (2 * Hq + 2 * Hkv) * D;
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + l.h);
+  uint16_t* proj = reinterpret_cast<uint16_t*>(ws + l.proj);
+  uint16_t* o = reinterpret_cast<uint16_t*>(ws + l.o);
+  uint16_t* a = reinterpret_cast<uint16_t*>(ws + l.a);
+
+  BlockNormArgs na{};
+  na.x = static_cast<const uint16_t*>(x);
+  na.w = static_cast<const uint16_t*>(w->in_norm);
+  na.out = h;
+  na.rows = B;
+  na.hidden = w->hidden;
+  na.eps = 1e-5f;
+  hipError_t e = launch_block_input_norm(na, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "input norm launch: %s", hipGetErrorString(e));
+
+  char msg[256];
+  if (block_gemm(B, N, w->hidden, h, w->w_qkvg, proj, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
+    return fail(MUSE_ERR_HIP, "q/k/v/gate projection: %s", msg);
+
+  // the layer's decode step reads q, k, v and the gate straight from the projection rows
+  rc = decode_call(params, B, proj, N, proj + Hq * D, proj + (Hq + Hkv) * D, N, proj + (Hq + 2 * Hkv) * D, N, kv_len,
+                   max_kv_len, cache, o, ws + l.attn, l.total - l.attn, stream);
+  if (rc) return rc;
+
+  if (block_gemm(B, w->hidden, Hq * D, o, w->w_o, a, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
+    return fail(MUSE_ERR_HIP, "o_proj: %s", msg);
+
+  float2* coef = nullptr;
+  if (w->residual_gate) {
+    coef = reinterpret_cast<float2*>(ws + l.coef);
+    e = launch_block_gate_coef(w->residual_gate, coef, w->hidden, w->residual_gate_temperature, 1e-3f, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "gate coefficient launch: %s", hipGetErrorString(e));
+  }
+  BlockResidualArgs ra{};
+  ra.x = static_cast<const uint16_t*>(x);
+  ra.branch = a;
+  ra.post_norm = static_cast<const uint16_t*>(w->post_norm);
+  ra.coef = reinterpret_cast<const float*>(coef);
+  ra.out = static_cast<uint16_t*>(out);
+  ra.rows = B;
   ra.hidden = w->hidden;
   ra.eps = 1e-8f;
   e = launch_block_residual(ra, st);

@@ -48,8 +48,8 @@ __global__ __launch_bounds__(256) void decode_append_kernel(DecodeArgs a, int hq
   const int h = is_q ? row : row - hq_total;
   float x0 = 0.f, x1 = 0.f;
   if (valid) {
-    const uint16_t* p = is_q ? a.q_new + (static_cast<int64_t>(b) * hq_total + h) * D
-                             : a.k_new + (static_cast<int64_t>(b) * a.Hkv + h) * D;
+    const uint16_t* p = is_q ? a.q_new + b * a.q_sb + static_cast<int64_t>(h) * D
+                             : a.k_new + b * a.kv_sb + static_cast<int64_t>(h) * D;
     x0 = bf16_bits_to_f32(p[j]);
     x1 = bf16_bits_to_f32(p[j + D / 2]);
   }
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void decode_append_kernel(DecodeArgs a, int hq
   ko[j + D / 2] = x1;
   if (!len_ok) return;
   // cache write: k_hat row (token-major) and v column (head-dim-major)
-  const uint16_t* vp = a.v_new + (static_cast<int64_t>(b) * a.Hkv + h) * D;
+  const uint16_t* vp = a.v_new + b * a.kv_sb + static_cast<int64_t>(h) * D;
   int64_t kbase, vbase, vstride;
   if (a.kind == MUSE_KV_RING) {
     const int slot = pos % a.capacity;
@@ -593,7 +593,7 @@ __global__ __launch_bounds__((CombineShape<D, G>::NWC * 64)) void decode_combine
   }
   __syncthreads();
   // heads w, w + NWC, ...: the new token's term, the waves' sums, then the epilogue
-  const uint16_t* vn = a.v_new + static_cast<int64_t>(bh) * D;
+  const uint16_t* vn = a.v_new + b * a.kv_sb + static_cast<int64_t>(hk) * D;
   for (int g = w; g < G; g += NWC) {
     const int hq = hk * G + g;
     const float fnew = __builtin_amdgcn_exp2f(s_new[g] - mm[g]);
@@ -616,7 +616,7 @@ __global__ __launch_bounds__((CombineShape<D, G>::NWC * 64)) void decode_combine
     }
     float rsn = 1.0f;
     if (a.out_norm) rsn = 1.0f / sqrtf(wave_sum(ss) * (1.0f / D) + a.out_eps);
-    const uint16_t* gp = a.gate + (static_cast<int64_t>(b) * a.Hkv * G + hq) * D;
+    const uint16_t* gp = a.gate + b * a.g_sb + static_cast<int64_t>(hq) * D;
     uint16_t* op = a.out + (static_cast<int64_t>(b) * a.Hkv * G + hq) * D;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {

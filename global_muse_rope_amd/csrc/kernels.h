@@ -167,10 +167,11 @@ struct PrefillCombineArgs {
 };
 
 struct DecodeArgs {
-  const uint16_t* q_new;
-  const uint16_t* k_new;
-  const uint16_t* v_new;
-  const uint16_t* gate;
+  const uint16_t* q_new;  // [B, Hq, D] with batch stride q_sb (elements)
+  const uint16_t* k_new;  // [B, Hkv, D] with batch stride kv_sb
+  const uint16_t* v_new;  // [B, Hkv, D] with batch stride kv_sb
+  const uint16_t* gate;   // [B, Hq, D] with batch stride g_sb
+  int64_t q_sb, kv_sb, g_sb;
   const int32_t* kv_len;
   uint16_t* out;
   // cache (bf16 entries, or E4M3 codes when fp8 is set; element offsets

@@ -270,6 +270,26 @@ int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block
 size_t muse_attn_block_prefill_workspace_size(const muse_attn_params* params,
                                               const muse_block_weights* weights, int32_t B, int32_t T);
 
+/* muse_attn_block_decode: one new token per sequence through the block's
+ * attention half (the same steps as muse_attn_block_prefill, deep dive
+ * section 2.1 forward walk), with the layer as one decode step
+ * (muse_attn_decode: the new token at position kv_len[b] - 1, its key and
+ * value appended to `cache` in place, attention over the visible cached
+ * entries plus itself).  x, out: [B, hidden] bf16, contiguous.  kv_len,
+ * max_kv_len and cache as for muse_attn_decode; weights as for
+ * muse_attn_block_prefill.  A sequence whose kv_len is out of range gets
+ * only its residual term (its layer output is zero) and no cache write.
+ * workspace: at least muse_attn_block_decode_workspace_size() bytes.
+ * B == 0 is a no-op. */
+int32_t muse_attn_block_decode(const muse_attn_params* params, const muse_block_weights* weights, int32_t B,
+                               const void* x, const int32_t* kv_len, int32_t max_kv_len,
+                               const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes,
+                               void* stream);
+
+size_t muse_attn_block_decode_workspace_size(const muse_attn_params* params,
+                                             const muse_block_weights* weights, int32_t B, int32_t max_kv_len,
+                                             const muse_kv_cache* cache);
+
 /* Layer schedule: layer i of n_layers is global (full attention, NoPE) iff
  * (n_layers - 1 - i) mod 4 == 0 (deep dive, section 2.2 equation).
  * Returns 1 (global), 0 (local) or -1 for i outside [0, n_layers). */

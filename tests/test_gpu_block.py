@@ -98,3 +98,99 @@ def test_block_prefill_fullsize_spark_sampled():
     err = max_err(y[0, rows].float().cpu().numpy(), ref)
     print(f"block full size spark: rows {rows.tolist()} max_abs_err={err:.3e}", flush=True)
     assert err <= BLOCK_TOL
+
+
+DEC_BLOCK_CASES = [
+    # (kind, layer, hidden, spark, kv lengths, page_tokens)
+    ("ring", Layer(hq=16, hkv=2, d=64, window=256, theta=10000.0, scale=SPARK_SCALE, out_norm=True, out_eps=1e-6),
+     768, True, [1, 2, 255, 256, 1000], 0),
+    ("paged", Layer(hq=16, hkv=2, d=64, window=0, theta=0.0, scale=SPARK_SCALE, out_norm=True, out_eps=1e-6),
+     1024, True, [300, 77, 1, 33], 32),
+    ("paged", Layer(hq=32, hkv=2, d=128, window=0, theta=0.0, scale=GLIMMER_SCALE), 1024, False, [500, 17, 2], 16),
+]
+
+
+@pytest.mark.parametrize("use_fp8", [False, True], ids=["bf16", "e4m3"])
+@pytest.mark.parametrize("case", DEC_BLOCK_CASES, ids=lambda c: f"{c[0]}-hq{c[1].hq}d{c[1].d}w{c[1].window}")
+def test_block_decode_parity(case, use_fp8):
+    """One new token per sequence through the block over a cache of stored entries
+    (bf16, or E4M3 codes with scales): every output against the block oracle's decode
+    step over the stored (dequantized) history, and for bf16 the appended value rows."""
+    from test_gpu_parity import make_cache, make_cache_fp8
+    kind, layer, hidden, spark, lens, pt = case
+    B = len(lens)
+    lens = np.array(lens, dtype=np.int32)
+    W, wb = make_block(layer, hidden, spark, seed=5)
+    if use_fp8:
+        cache, hk, hv, _, _ = make_cache_fp8(kind, layer, B, lens, page_tokens=pt or 32)
+    else:
+        cache, hk, hv = make_cache(kind, layer, B, lens, page_tokens=pt or 32)
+    xb = synth.normal_bf16_bits(7, 9, (B, hidden))
+    lp = ma.LayerParams.from_layer(layer)
+    y = ma.attention_block_decode(lp, wb, to_dev(xb), torch.from_numpy(lens).to(DEV), int(lens.max()), cache)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+    worst = 0.0
+    for b in range(B):
+        L = int(lens[b])
+        ref = OB.attention_block_decode(_f(xb)[b], W, layer, hk[b, :L - 1].astype(np.float64),
+                                        hv[b, :L - 1].astype(np.float64), 0, L)
+        worst = max(worst, max_err(y[b], ref))
+    print(f"block decode {kind} fp8={use_fp8} {layer} hidden={hidden} max_abs_err={worst:.3e}", flush=True)
+    assert worst <= BLOCK_TOL
+    if use_fp8:
+        return
+    # the new value row landed in the cache (bf16 projection of the normed input, so compare with the
+    # oracle's projection within the projection's bf16 rounding)
+    _, _, v_new, _ = OB.input_projections(_f(xb), W, layer)
+    for b in range(B):
+        p = int(lens[b]) - 1
+        if kind == "ring":
+            vst = cache.v[b, :, :, p % layer.window].float().cpu().numpy()
+        else:
+            pg = int(cache.block_table[b, p // pt])
+            vst = cache.v[pg, :, :, p % pt].float().cpu().numpy()
+        assert np.allclose(vst, v_new[b], rtol=2 ** -6, atol=2e-2)
+
+
+def test_block_decode_fullsize_ring():
+    """The Spark local decode workload (16 sequences, a 2048-entry ring, lengths in
+    [131072, 1048576]) through a block of hidden width 8192: every sequence against
+    the block oracle over its stored window."""
+    from synth import device as sd
+    from synth import workloads as wl
+    from synth.device import block_device_setup
+    cfg = wl.SPARK_DECODE_LOCAL
+    L = cfg.layer
+    bcfg = wl.SPARK_BLOCK_LOCAL
+    assert bcfg.layer == L
+    print(f"block decode full size {cfg.name}", flush=True)
+    s = sd.decode_device_setup(cfg)
+    cache = ma.KvCache.ring(s["kc"], s["vc"])
+    w = block_device_setup(bcfg)
+    wb = ma.BlockWeights(in_norm=w["in_norm"], w_qkvg=w["w_qkvg"], w_o=w["w_o"], residual_gate=w["residual_gate"],
+                         post_norm=w["post_norm"])
+    B = cfg.batch
+    x = synth.normal_bf16_torch_tensor(cfg.seed, 9, (B, bcfg.hidden), DEV)
+    lp = ma.LayerParams.from_layer(L)
+    y = ma.attention_block_decode(lp, wb, x, s["kv_len"], s["max_len"], cache)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy()
+
+    def host(t):
+        return t.double().cpu().numpy() if t is not None else None
+
+    Wt = {"in_norm": host(w["in_norm"]), "w_qkvg": host(w["w_qkvg"]), "w_o": host(w["w_o"]),
+          "post_norm": host(w["post_norm"]), "residual_gate": host(w["residual_gate"])}
+    xh = x.double().cpu().numpy()
+    worst = 0.0
+    for b in range(B):
+        Lb = int(s["lengths"][b])
+        p = Lb - 1
+        lo = max(0, p - L.window + 1)
+        kh = np.stack([sd.cache_values_host(cfg.seed, b, h, L.hkv, "k", lo, p, L.d) for h in range(L.hkv)], axis=1)
+        vh = np.stack([sd.cache_values_host(cfg.seed, b, h, L.hkv, "v", lo, p, L.d) for h in range(L.hkv)], axis=1)
+        ref = OB.attention_block_decode(xh[b], Wt, L, kh, vh, lo, Lb)
+        worst = max(worst, max_err(y[b], ref))
+    print(f"{cfg.name} through the block: {B} sequences, max_abs_err={worst:.3e}", flush=True)
+    assert worst <= BLOCK_TOL
