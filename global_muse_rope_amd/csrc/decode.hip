@@ -154,9 +154,9 @@ __device__ __forceinline__ bool hist_valid(const HistRange& r, int idx) {
 // ---------------------------------------------------------------------------
 // 2. split
 // ---------------------------------------------------------------------------
-// 8-entry blocks of one paged chunk (each lies inside one page: pages hold a
-// multiple of 16 positions and chunks start at multiples of 8).
-constexpr int kChunkBlocks = kPagedChunk / 8;
+// 8-entry blocks of the largest paged chunk (each lies inside one page: pages
+// hold a multiple of 16 positions and chunks start at multiples of 8).
+constexpr int kChunkBlocks = kPagedChunkMax / 8;
 // Register buffers of 32-entry sub-chunks per wave (PD - 1 in flight).  bf16
 // keeps two in flight: a cold 2048-entry ring then overlaps more of its load
 // latency (measured 5 % faster; the same on pages).  The E4M3 loop is bound
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
   const bool paged = a.kind != MUSE_KV_RING;
   const int pt = a.page_tokens;
   if (paged) {
-    for (int i = tid; i < kChunkBlocks; i += NW * kWave) {
+    for (int i = tid; i < a.chunk_tokens / 8; i += NW * kWave) {
       const int idx = c0 + 8 * i;
       int64_t ko = -1, vo = -1;
       int si = -1;

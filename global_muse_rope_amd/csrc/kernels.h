@@ -8,8 +8,12 @@ namespace muse {
 
 // Keys per LDS tile of the prefill kernel.
 constexpr int kKeyTile = 64;
-// Cached positions per split of a paged decode cache.
-constexpr int kPagedChunk = 2048;
+// Cached positions per split workgroup of a paged decode cache: the largest
+// of kPagedChunkMax, its half and its quarter for which a launch still has
+// kPagedChunkTarget workgroups or more (the smallest otherwise).
+constexpr int kPagedChunkMax = 8192;
+constexpr int kPagedChunkMin = 2048;
+constexpr int64_t kPagedChunkTarget = 2048;
 
 // ---------------------------------------------------------------------------
 // Prefill tile image: one 64-key tile of one (sequence, KV head), written by

@@ -146,6 +146,30 @@ def test_workspace_sizes():
     assert lib.muse_attn_prefill_workspace_size(ctypes.byref(bad), 1, 1000) == 0
 
 
+def test_decode_workspace_follows_paged_chunk_choice():
+    """Paged decode splits each (sequence, KV head) into chunks of 8192, 4096 or
+    2048 positions: the largest that still gives 2048 workgroups for the batch,
+    KV heads and max_kv_len (2048 when none does).  The workspace holds one fp32
+    partial of G * (D + 2) values per chunk, so its size shows the choice."""
+    capi, lib = _lib()
+    p = params(capi, num_q_heads=128, num_kv_heads=16, head_dim=64, qk_scale=5.473, out_norm=1)
+    paged = capi.MuseKvCache(capi.MUSE_KV_PAGED, 0, FAKE, FAKE, FAKE, 40000, 32, 1 << 22)
+
+    def expect(B, max_len, chunk):
+        a256 = lambda n: (n + 255) // 256 * 256
+        chunks = (max_len + chunk - 1) // chunk + 1
+        return a256(B * 128 * 64 * 4) + a256(B * 16 * 64 * 4) + a256(B * 16 * chunks * 8 * 66 * 4)
+
+    def got(B, max_len):
+        return lib.muse_attn_decode_workspace_size(ctypes.byref(p), B, max_len, ctypes.byref(paged))
+
+    assert got(16, 1 << 20) == expect(16, 1 << 20, 8192)   # 256 * 129 workgroups
+    assert got(16, 30000) == expect(16, 30000, 4096)       # 8192 would give 256 * 5
+    assert got(16, 8000) == expect(16, 8000, 2048)         # none reaches 2048: the smallest
+    assert got(1, 1 << 17) == expect(1, 1 << 17, 2048)
+    assert got(1, 1 << 20) == expect(1, 1 << 20, 8192)     # 16 * 129 = 2064
+
+
 def test_decode_argument_checks():
     capi, lib = _lib()
     p = params(capi, num_q_heads=128, num_kv_heads=16, head_dim=64, qk_scale=5.473, out_norm=1)

@@ -229,6 +229,36 @@ def test_decode_fullsize_fp8_sampled(cfg):
     assert worst <= TOL
 
 
+# 16 sequences of 20,000-30,000 positions over a paged cache: 8192-entry chunks
+# would give only 256 * 5 workgroups, so the launch takes 4096-entry chunks (the
+# full-size workload takes 8192, short test cases 2048).
+MID_PAGED = dataclasses.replace(wl.SPARK_DECODE_GLOBAL, name="spark_decode_global_paged_mid", len_lo=20000,
+                                len_hi=30000)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "e4m3"])
+def test_decode_paged_middle_chunk_size(fp8):
+    cfg = MID_PAGED
+    print(f"decode {cfg.name} fp8={fp8}", flush=True)
+    res = _decode_run(cfg, fp8=fp8)
+    y, lengths = res[0], res[1]
+    assert np.isfinite(y).all()
+    new = sd.new_token_host(cfg)
+    G = cfg.layer.group
+    pairs = [(b, (5 * b) % cfg.layer.hkv) for b in range(cfg.batch)]
+    worst = 0.0
+    t = time.time()
+    for b, hk in pairs:
+        if fp8:
+            ref = oracle_decode_pair_fp8(cfg, new, b, hk, int(lengths[b]), res[2])
+        else:
+            ref = oracle_decode_pair(cfg, new, b, hk, int(lengths[b]))
+        worst = max(worst, max_err(y[b, hk * G:(hk + 1) * G], ref))
+    print(f"{cfg.name}: {len(pairs)} pairs, lengths {int(lengths.min())}-{int(lengths.max())}, "
+          f"max_abs_err={worst:.3e} (oracle {time.time() - t:.1f} s)", flush=True)
+    assert worst <= TOL
+
+
 @pytest.mark.parametrize("cfg", wl.CHUNK, ids=lambda c: c.name)
 def test_prefill_chunk_fullsize_sampled(cfg):
     """A 2048-token chunk after 131072 cached positions: sampled rows of two
