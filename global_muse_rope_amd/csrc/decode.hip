@@ -159,8 +159,9 @@ __device__ __forceinline__ bool hist_valid(const HistRange& r, int idx) {
 constexpr int kChunkBlocks = kPagedChunkMax / 8;
 // Register buffers of 32-entry sub-chunks per wave (PD - 1 in flight).  bf16
 // keeps two in flight: a cold 2048-entry ring then overlaps more of its load
-// latency (measured 5 % faster; the same on pages).  The E4M3 loop is bound
-// by instruction issue, and more buffers measured no faster there.
+// latency (measured 5 % faster; the same on pages), while a fourth buffer
+// measured 11 % slower on the ring.  The E4M3 loop is bound by instruction
+// issue: three or four buffers measured 1.5 % and 4 % slower there.
 #ifndef MUSE_DECODE_DEPTH
 #define MUSE_DECODE_DEPTH 3
 #endif
