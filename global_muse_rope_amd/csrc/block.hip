@@ -275,9 +275,11 @@ int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* 
       hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
       if (hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
       int pick = 0;
-      if (cap == hipStreamCaptureStatusNone && found > 1) {
-        pick = fastest_candidate(h, desc, la, lb, lc, act, w, out, ws, wsb, st, res, found);
-        if (pick < 0) pick = 0;
+      if (cap == hipStreamCaptureStatusNone) {
+        if (found > 1) {
+          pick = fastest_candidate(h, desc, la, lb, lc, act, w, out, ws, wsb, st, res, found);
+          if (pick < 0) pick = 0;
+        }
         std::lock_guard<std::mutex> lk(g_lt_mu);
         g_algo[key] = res[pick].algo;
       }
