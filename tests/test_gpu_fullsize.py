@@ -110,9 +110,9 @@ def test_prefill_fullsize_sampled(cfg):
     assert worst <= TOL
 
 
-def _decode_run(cfg, fp8=False):
+def _decode_run(cfg, fp8=False, lengths=None):
     L = cfg.layer
-    s = sd.decode_device_setup(cfg, fp8=fp8)
+    s = sd.decode_device_setup(cfg, fp8=fp8, lengths=lengths)
     ks, vs = s.get("k_scale"), s.get("v_scale")
     if s["kind"] == "ring":
         cache = ma.KvCache.ring(s["kc"], s["vc"], ks, vs)
@@ -256,6 +256,36 @@ def test_decode_paged_middle_chunk_size(fp8):
         worst = max(worst, max_err(y[b, hk * G:(hk + 1) * G], ref))
     print(f"{cfg.name}: {len(pairs)} pairs, lengths {int(lengths.min())}-{int(lengths.max())}, "
           f"max_abs_err={worst:.3e} (oracle {time.time() - t:.1f} s)", flush=True)
+    assert worst <= TOL
+
+
+# 48 sequences of the Spark global layer with lengths on and around multiples
+# of 8192: the launch takes 8192-entry chunks (768 * 3 workgroups), so every
+# chunk edge case of that size is checked, one KV head per sequence.
+EDGE_LENGTHS = [1, 2, 31, 32, 33, 8191, 8192, 8193, 8194, 16383, 16384, 16385] * 4
+EDGE_PAGED = dataclasses.replace(wl.SPARK_DECODE_GLOBAL, name="spark_decode_global_paged_chunk_edges", batch=48,
+                                 len_lo=1, len_hi=16400)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "e4m3"])
+def test_decode_paged_chunk_edges(fp8):
+    cfg = EDGE_PAGED
+    print(f"decode {cfg.name} fp8={fp8}", flush=True)
+    res = _decode_run(cfg, fp8=fp8, lengths=EDGE_LENGTHS)
+    y, lengths = res[0], res[1]
+    assert list(lengths) == EDGE_LENGTHS
+    assert np.isfinite(y).all()
+    new = sd.new_token_host(cfg)
+    G = cfg.layer.group
+    worst = 0.0
+    for b in range(cfg.batch):
+        hk = (7 * b) % cfg.layer.hkv
+        if fp8:
+            ref = oracle_decode_pair_fp8(cfg, new, b, hk, int(lengths[b]), res[2])
+        else:
+            ref = oracle_decode_pair(cfg, new, b, hk, int(lengths[b]))
+        worst = max(worst, max_err(y[b, hk * G:(hk + 1) * G], ref))
+    print(f"{cfg.name}: {cfg.batch} sequences, max_abs_err={worst:.3e}", flush=True)
     assert worst <= TOL
 
 
