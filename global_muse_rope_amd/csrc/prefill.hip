@@ -94,7 +94,9 @@ struct PrefillCfg {
   static_assert(32 % G == 0 || G == 32, "a 32-row block must hold whole tokens");
 };
 
-template <int D, int G, int NW, int MB>
+// SKIP: waves whose columns all lie past the last query row skip their
+// matrix and vector work (launches whose sequences are shorter than a block).
+template <int D, int G, int NW, int MB, bool SKIP>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D, G, NW, MB>;
   using TL = TileLayout<D>;
@@ -511,7 +513,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int e = 0; e < 16; ++e) sn[mb][e] = 0.f;
-  {
+  // A wave whose columns all lie past the last query row (the short block of
+  // a drafter) only copies its share of each tile and meets the barriers.
+  // Only the SKIP instance tests for it: in the others the branch would cost
+  // the common path about 2 % (register allocation and scheduling).
+  const bool idle = SKIP && t0 + (w * MB * 32) / G >= a.T;
+  if (!idle) {
     const Half h0 = half_at(tile_lo, 0, tile_lo, 0);
     prime(h0);
     half_step(h0, half_at(tile_lo, 1, tile_lo, 1), sc, pp, sn, pc);
@@ -519,6 +526,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) lsum[mb] = 0.f;
   for (int t = tile_lo; t <= tile_hi; ++t) {
+    if (idle) {
+      advance(t);
+      continue;
+    }
     const bool masked = t < m_lo || t >= m_hi;
     const int k0 = t * kKeyTile;
     const int tprev = t > tile_lo ? t - 1 : t;
@@ -539,7 +550,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   float lkeep[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) lkeep[mb] = lsum[mb];
-  {
+  if (!idle) {
     const Half hd = half_at(tile_hi, 1, tile_hi, 1);
     half_step(hd, hd, sn, pp, sc, pc);
   }
@@ -719,11 +730,11 @@ struct LaunchShape {
 };
 
 // Resident workgroups of one kernel on the current device: CUs times the
-// occupancy the kernel's registers and LDS allow (cached per device).
+// occupancy the kernel's registers and LDS allow, cached per device in the
+// caller's array (one per kernel instance).
+constexpr int kMaxDev = 64;
 template <typename K>
-int resident_workgroups(K kernel, int threads) {
-  constexpr int kMaxDev = 64;
-  static int cache[kMaxDev] = {};
+int resident_workgroups(K kernel, int threads, int* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
   if (cache[dev] > 0) return cache[dev];
@@ -738,7 +749,8 @@ template <int D, int G>
 hipError_t launch_dg(const PrefillArgs& a, hipStream_t st) {
   constexpr int NW = LaunchShape<D>::NW, MB = LaunchShape<D>::MB;
   using C = PrefillCfg<D, G, NW, MB>;
-  auto kernel = prefill_kernel<D, G, NW, MB>;
+  // a sequence shorter than one query block leaves whole waves without rows
+  auto kernel = a.T < C::BQ ? prefill_kernel<D, G, NW, MB, true> : prefill_kernel<D, G, NW, MB, false>;
   const int nlog = a.n_qblocks_pad * a.batch_heads;  // a multiple of 8
   int grid = nlog;
   if (a.nsplit > 1) {
@@ -746,7 +758,8 @@ hipError_t launch_dg(const PrefillArgs& a, hipStream_t st) {
   } else if (D == 128 && a.W > 0) {
     // local layers run a persistent grid of at most one wave of resident
     // workgroups, a multiple of 8 so every XCD gets the same number
-    const int cap = resident_workgroups(kernel, C::THREADS) & ~7;
+    static int resident[2][kMaxDev] = {};
+    const int cap = resident_workgroups(kernel, C::THREADS, resident[a.T < C::BQ ? 1 : 0]) & ~7;
     if (cap >= 8 && cap < nlog) grid = cap;
   }
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(C::THREADS), 0, st, a);
