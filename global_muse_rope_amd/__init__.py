@@ -119,6 +119,50 @@ def _check_bf16(name, t, heads, d):
         raise ValueError(f"{name}: heads and dims must be contiguous")
 
 
+def _check_aux(name, t, dtype, numel, device):
+    """An auxiliary tensor (positions, lengths, starts, block table, scales,
+    workspace): its element type, its element count (None: any) and its
+    device are checked before anything reaches the library, which takes a
+    device pointer for it and reads exactly that many entries."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} entries, got {t.numel()}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a device tensor on {device}, got {t.device}")
+
+
+def _check_workspace(workspace, need, device):
+    torch = _torch()
+    _check_aux("workspace", workspace, torch.uint8, None, device)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, the call needs {need}")
+
+
+def _check_cache(cache, device):
+    torch = _torch()
+    for name, t in (("cache.k", cache.k), ("cache.v", cache.v)):
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be a device tensor on {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if cache.kind == MUSE_KV_PAGED:
+        bt = cache.block_table
+        if bt is None or bt.dim() != 2 or not bt.is_contiguous():
+            raise ValueError("a paged cache needs a contiguous [B, max_pages] block_table")
+        _check_aux("cache.block_table", bt, torch.int32, None, device)
+    if cache.dtype == _capi.MUSE_DTYPE_FP8_E4M3:
+        n = int(cache.k.shape[0]) * int(cache.k.shape[1])   # [num_pages or B] x Hkv
+        for name, t in (("cache.k_scale", cache.k_scale), ("cache.v_scale", cache.v_scale)):
+            if t is None:
+                raise ValueError("an E4M3 cache needs k_scale and v_scale")
+            _check_aux(name, t, torch.float32, n, device)
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+
+
 def version() -> int:
     return _capi.load().muse_version()
 
@@ -148,7 +192,10 @@ def rope_qknorm(layer: LayerParams, q=None, k=None, positions=None, out_dtype=No
         _check_bf16("k", k, layer.num_kv_heads, layer.head_dim)
         ko = torch.empty((n, layer.num_kv_heads, layer.head_dim), dtype=out_dtype, device=k.device)
     if positions is not None:
-        positions = positions.to(dtype=torch.int32).contiguous()
+        _check_aux("positions", positions, torch.int32, n, ref.device)
+        positions = positions.contiguous()
+    if q is not None and k is not None and q.device != k.device:
+        raise ValueError("q and k must be on one device")
     p = layer.c()
     _capi.check(lib.muse_rope_qknorm(
         ctypes.byref(p), n,
@@ -181,12 +228,17 @@ def prefill(layer: LayerParams, q, k, v, gate, positions=None, out=None, workspa
     if out is None:
         out = torch.empty((B, T, layer.num_q_heads, layer.head_dim), dtype=torch.bfloat16, device=q.device)
     _check_bf16("out", out, layer.num_q_heads, layer.head_dim)
+    for name, t in (("k", k), ("v", v), ("gate", gate), ("out", out)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on the device of q ({q.device})")
     need = prefill_workspace_size(layer, B, T)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     strides = (ctypes.c_int64 * 10)(*[int(s) for t in (q, k, v, gate, out) for s in (t.stride(0), t.stride(1))])
     if positions is not None:
-        positions = positions.to(dtype=torch.int32).contiguous()
+        _check_aux("positions", positions, torch.int32, B * T, q.device)
+        positions = positions.contiguous()
     p = layer.c()
     _capi.check(lib.muse_attn_prefill(
         ctypes.byref(p), B, T, q.data_ptr(), k.data_ptr(), v.data_ptr(), gate.data_ptr(), strides,
@@ -234,14 +286,18 @@ def _chunk_like(entry, layer, q, k, v, gate, start, max_start, cache, out, works
     for name, t in (("k", k), ("v", v), ("gate", gate)):
         if int(t.shape[0]) != B or int(t.shape[1]) != T:
             raise ValueError(f"{name} batch/sequence shape mismatch")
-    if start.dtype != torch.int32 or not start.is_cuda or start.numel() != B:
-        raise ValueError("start must be a device int32 tensor of B entries")
+    _check_aux("start", start, torch.int32, B, q.device)
     if out is None:
         out = torch.empty((B, T, layer.num_q_heads, layer.head_dim), dtype=torch.bfloat16, device=q.device)
     _check_bf16("out", out, layer.num_q_heads, layer.head_dim)
+    for name, t in (("k", k), ("v", v), ("gate", gate), ("out", out)):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on the device of q ({q.device})")
+    _check_cache(cache, q.device)
     need = prefill_chunk_workspace_size(layer, B, T, max_start)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check_workspace(workspace, need, q.device)
     strides = (ctypes.c_int64 * 10)(*[int(s) for t in (q, k, v, gate, out) for s in (t.stride(0), t.stride(1))])
     p = layer.c()
     c = cache.c()
@@ -271,13 +327,19 @@ def decode(layer: LayerParams, q_new, k_new, v_new, gate, kv_len, max_kv_len: in
         _check_bf16(name, t, h, layer.head_dim)
         if not t.is_contiguous() or int(t.shape[0]) != B:
             raise ValueError(f"{name} must be contiguous [B, H, D]")
-    if kv_len.dtype != torch.int32 or not kv_len.is_cuda or kv_len.numel() != B:
-        raise ValueError("kv_len must be a device int32 tensor of B entries")
+        if t.device != q_new.device:
+            raise ValueError(f"{name} must be on the device of q_new ({q_new.device})")
+    _check_aux("kv_len", kv_len, torch.int32, B, q_new.device)
     if out is None:
         out = torch.empty((B, layer.num_q_heads, layer.head_dim), dtype=torch.bfloat16, device=q_new.device)
+    _check_bf16("out", out, layer.num_q_heads, layer.head_dim)
+    if not out.is_contiguous() or int(out.shape[0]) != B or out.device != q_new.device:
+        raise ValueError("out must be a contiguous [B, Hq, D] tensor on the device of q_new")
+    _check_cache(cache, q_new.device)
     need = decode_workspace_size(layer, B, max_kv_len, cache)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_new.device)
+    _check_workspace(workspace, need, q_new.device)
     p = layer.c()
     c = cache.c()
     _capi.check(lib.muse_attn_decode(

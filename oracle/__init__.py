@@ -46,6 +46,7 @@ from .attention import (  # noqa: F401
     layer_is_global,
     global_layers,
     visible_range,
+    bidirectional_range,
     visible_mask,
     rms_normalize,
     to_bf16,

@@ -35,6 +35,19 @@ def visible_range(i: int, window: int) -> tuple[int, int]:
     return lo, i
 
 
+def bidirectional_range(p: int, window: int, last: int) -> tuple[int, int]:
+    """Inclusive range [lo, hi] of key positions a block-diffusion drafter's
+    query at position p sees (deep dive, section 8.2, step 4: the block
+    attends without a causal mask): |p - j| < W in both directions on a
+    layer with window W > 0, every key on a window-0 layer, and keys exist
+    only up to the block's last position `last`."""
+    if window < 0:
+        raise ValueError("window must be >= 0")
+    if window == 0:
+        return 0, last
+    return max(0, p - window + 1), min(last, p + window - 1)
+
+
 def visible_mask(n: int, window: int) -> np.ndarray:
     """Boolean [n, n] mask, entry (i, j) true iff key j is visible to query i."""
     m = np.zeros((n, n), dtype=bool)
@@ -321,9 +334,7 @@ def block_bidirectional(q, k, v, gate, k_hist, v_hist, hist_start: int, start: i
     g = layer.group
     o = np.empty(np.shape(qh), dtype=np.float64)
     for r, t in enumerate(rows):
-        p = int(start + t)
-        lo = 0 if layer.window == 0 else max(0, p - layer.window + 1)
-        hi = last if layer.window == 0 else min(last, p + layer.window - 1)
+        lo, hi = bidirectional_range(int(start + t), layer.window, last)
         if lo < start and (lo < hist_start or hist_start + k_hist.shape[0] < start):
             raise ValueError("history does not cover the visible range")
         a = lo - hist_start

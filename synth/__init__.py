@@ -96,6 +96,17 @@ def e4m3_codes(seed: int, stream_id: int, idx) -> np.ndarray:
     return (mag | sign).astype(np.uint8)
 
 
+def sign_bf16_bits(seed: int, stream_id: int, idx) -> np.ndarray:
+    """bf16 bit patterns of +1 or -1 for flat indices ``idx``: bit 0 of one
+    64-bit word per index picks the sign.  A row of D such entries has mean
+    square exactly 1, and every value is exact in bf16 and in E4M3."""
+    idx = np.asarray(idx, dtype=np.int64).astype(np.uint64)
+    key = np.uint64(stream_key(seed, stream_id))
+    with np.errstate(over="ignore"):
+        h = _mix64_np(key + idx * np.uint64(GAMMA))
+    return np.where((h & np.uint64(1)) == 1, np.uint16(0xBF80), np.uint16(0x3F80)).astype(np.uint16)
+
+
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 (nearest-even); returns uint16 bit patterns."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -170,6 +181,15 @@ def e4m3_codes_torch(seed: int, stream_id: int, idx):
     mag = torch.remainder(h & 0xFFFF, 40) + 0x20
     sign = (_lsr(h, 16) & 1) << 7
     return (mag | sign).to(torch.uint8)
+
+
+def sign_bf16_torch(seed: int, stream_id: int, idx):
+    """The same signs as ``sign_bf16_bits`` as a bfloat16 tensor (any device)."""
+    import torch
+    key = stream_key(seed, stream_id)
+    h = _mix64_torch(idx.to(torch.int64) * _as_i64(GAMMA) + _as_i64(key))
+    bits = torch.where((h & 1) == 1, torch.full_like(h, 0xBF80 - 65536), torch.full_like(h, 0x3F80))
+    return bits.to(torch.int16).view(torch.bfloat16)
 
 
 def normal_bf16_torch_tensor(seed: int, stream_id: int, shape, device, offset: int = 0):

@@ -4,10 +4,12 @@ forms in ``synth``), and host regeneration of any slice for the oracle.
 Prefill tensors are indexed in the canonical layout [B, T, H, D].  Decode:
 the new token's q, k, v, gate are [B, H, D]; cached entries of (sequence b,
 KV head h) at position p are element p * D + d of stream
-S_CACHE_BASE + 2 * (b * Hkv + h) (+1 for values).  Cached keys are drawn
-like raw projections (mean square 1 per head, as the layer's normalized keys
-have on average) and stored as given; the layer treats cache contents as
-data.  Paged caches place each sequence's pages at positions drawn from a
+S_CACHE_BASE + 2 * (b * Hkv + h) (+1 for values).  A cache holds keys
+after the layer's norm (and RoPE on local layers), so every cached key row
+has mean square 1: cached keys are drawn as random signs, +1 or -1 per
+element, which gives exactly that with no arithmetic of the layer here (a
+rotation keeps the mean square, and a random direction stays random).
+Cached values are N(0,1), like raw projections.  Paged caches place each sequence's pages at positions drawn from a
 seeded permutation of the pool.
 
 FP8 caches hold E4M3 codes drawn directly from the same streams (magnitude
@@ -19,7 +21,7 @@ from __future__ import annotations
 import numpy as np
 
 from . import (normal_bf16_torch, normal_bf16_torch_tensor, bf16_bits_to_f64, f32_to_bf16_bits, normal_f32,
-               e4m3_codes, e4m3_codes_torch)
+               e4m3_codes, e4m3_codes_torch, sign_bf16_torch)
 from .workloads import (S_Q, S_K, S_V, S_G, S_CACHE_BASE, S_X, S_IN_NORM, S_W_QKVG, S_W_O, S_POST_NORM, S_RES_GATE,
                         decode_lengths)
 
@@ -73,10 +75,12 @@ def cache_stream(b, h, hkv, which):
 
 
 def cache_values_torch(seed, b, h, hkv, which, p0, p1, d, device):
-    """bf16 tensor [p1 - p0, d] of cached entries at positions p0 .. p1-1."""
+    """bf16 tensor [p1 - p0, d] of cached entries at positions p0 .. p1-1:
+    keys are signs (unit mean square per row), values N(0,1)."""
     import torch
     idx = torch.arange(p0 * d, p1 * d, dtype=torch.int64, device=device)
-    return normal_bf16_torch(seed, cache_stream(b, h, hkv, which), idx).view(p1 - p0, d)
+    draw = sign_bf16_torch if which == "k" else normal_bf16_torch
+    return draw(seed, cache_stream(b, h, hkv, which), idx).view(p1 - p0, d)
 
 
 def cache_values_host(seed, b, h, hkv, which, p0, p1, d):

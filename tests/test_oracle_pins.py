@@ -66,6 +66,21 @@ def test_window_includes_self():
     assert oracle.visible_range(10 * w, 0) == (0, 10 * w)
 
 
+def test_bidirectional_range_brute_force():
+    """The drafter's two-sided window (deep dive, section 8.2, step 4: no causal
+    mask inside the window) against the set {j <= last : |p - j| < W}, or every
+    key up to last on a window-0 layer, enumerated directly; a position well
+    inside sees 2W - 1 keys, the self key counted once."""
+    for w in (0, 1, 2, 5, 64):
+        for last in (0, 3, 70, 200):
+            for p in range(0, last + 1):
+                want = [j for j in range(0, last + 1) if w == 0 or abs(p - j) < w]
+                lo, hi = oracle.bidirectional_range(p, w, last)
+                assert list(range(lo, hi + 1)) == want, (w, last, p)
+    lo, hi = oracle.bidirectional_range(5000, 2048, 10 ** 6)
+    assert hi - lo + 1 == 2 * 2048 - 1
+
+
 def test_visible_counts_closed_form():
     from global_muse_rope_amd import accounting
     for n, w in [(1, 1), (7, 1), (64, 5), (100, 100), (100, 200), (1024, 256), (1024, 0), (333, 64)]:

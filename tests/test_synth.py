@@ -69,3 +69,23 @@ def test_block_inputs_are_scaled_draws_with_host_bits():
             p = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(synth.normal_bf16_bits(3, S_POST_NORM, (64,)))
                                        * np.float32(0.1))
             assert np.array_equal(s["post_norm"].view(torch.int16).numpy().view(np.uint16), p)
+
+
+def test_sign_draws_agree_and_have_unit_mean_square():
+    import torch
+    idx = np.arange(5, 5 + 64 * 300, dtype=np.int64)
+    a = synth.sign_bf16_bits(0, 77, idx)
+    b = synth.sign_bf16_torch(0, 77, torch.from_numpy(idx)).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(a, b)
+    v = synth.bf16_bits_to_f64(a).reshape(300, 64)
+    assert set(np.unique(v)) == {-1.0, 1.0}
+    assert np.all(np.mean(v * v, axis=1) == 1.0)          # every cached key row: mean square exactly 1
+    assert abs(np.mean(v)) < 0.05
+
+
+def test_cached_keys_are_unit_rms_rows():
+    from synth.device import cache_values_host
+    k = cache_values_host(0, 3, 1, 16, "k", 100, 400, 64)
+    assert np.all(np.mean(k * k, axis=1) == 1.0)
+    v = cache_values_host(0, 3, 1, 16, "v", 100, 400, 64)
+    assert 0.8 < np.mean(v * v) < 1.2
