@@ -349,6 +349,37 @@ def decode(layer: LayerParams, q_new, k_new, v_new, gate, kv_len, max_kv_len: in
     return out
 
 
+def decode_noalloc(layer: LayerParams, q_new, k_new, v_new, gate, kv_len, max_kv_len: int, cache: KvCache,
+                   out=None):
+    """decode() through muse_attn_decode_noalloc: the library's fixed per-device
+    scratch replaces the workspace, so the call itself allocates nothing (pass
+    `out` to allocate nothing on the Python side either).  Calls that overlap on
+    one device race on that scratch."""
+    torch = _torch()
+    lib = _capi.load()
+    B = int(q_new.shape[0])
+    for name, t, h in (("q_new", q_new, layer.num_q_heads), ("k_new", k_new, layer.num_kv_heads),
+                       ("v_new", v_new, layer.num_kv_heads), ("gate", gate, layer.num_q_heads)):
+        _check_bf16(name, t, h, layer.head_dim)
+        if not t.is_contiguous() or int(t.shape[0]) != B:
+            raise ValueError(f"{name} must be contiguous [B, H, D]")
+        if t.device != q_new.device:
+            raise ValueError(f"{name} must be on the device of q_new ({q_new.device})")
+    _check_aux("kv_len", kv_len, torch.int32, B, q_new.device)
+    if out is None:
+        out = torch.empty((B, layer.num_q_heads, layer.head_dim), dtype=torch.bfloat16, device=q_new.device)
+    _check_bf16("out", out, layer.num_q_heads, layer.head_dim)
+    if not out.is_contiguous() or int(out.shape[0]) != B or out.device != q_new.device:
+        raise ValueError("out must be a contiguous [B, Hq, D] tensor on the device of q_new")
+    _check_cache(cache, q_new.device)
+    p = layer.c()
+    c = cache.c()
+    _capi.check(lib.muse_attn_decode_noalloc(
+        ctypes.byref(p), B, q_new.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), gate.data_ptr(),
+        kv_len.data_ptr(), int(max_kv_len), ctypes.byref(c), out.data_ptr(), _stream()))
+    return out
+
+
 @dataclass
 class BlockWeights:
     """Weights of a decoder block's attention half (see muse_block_weights):

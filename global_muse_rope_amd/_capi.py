@@ -85,6 +85,7 @@ SIGNATURES = {
     "muse_attn_draft_block_workspace_size": (_sz, [_P, _i32, _i32, _i32]),
     "muse_attn_decode": (_i32, [_P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _C, _vp, _vp, _sz, _vp]),
     "muse_attn_decode_workspace_size": (_sz, [_P, _i32, _i32, _C]),
+    "muse_attn_decode_noalloc": (_i32, [_P, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _C, _vp, _vp]),
     "muse_attn_block_prefill": (_i32, [_P, _BW, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "muse_attn_block_prefill_workspace_size": (_sz, [_P, _BW, _i32, _i32]),
     "muse_attn_block_decode": (_i32, [_P, _BW, _i32, _vp, _vp, _i32, _C, _vp, _vp, _sz, _vp]),

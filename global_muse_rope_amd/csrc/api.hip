@@ -11,6 +11,16 @@
 
 using namespace muse;
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode entry point (muse_attn_decode_noalloc):
+// one array per device, held from the library's first use on that device
+// until the process ends.  On the host the name is a stand-in, not device
+// memory: host code passes only the device address hipGetSymbolAddress
+// returns for it.  Every value a call reads from it is written earlier in
+// the same call, so nothing is cleared between calls.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MUSE_DECODE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -753,9 +763,57 @@ int32_t decode_call(const muse_attn_params* params, int32_t B, const void* q_new
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }
+
+// The device address of `scratch` on the current device, fetched once per
+// device with that device current.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(MUSE_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return fail(MUSE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MUSE_OK;
+}
 }  // namespace
 
 extern "C" {
+
+int32_t muse_attn_decode_noalloc(const muse_attn_params* params, int32_t B, const void* q_new, const void* k_new,
+                                 const void* v_new, const void* gate, const int32_t* kv_len, int32_t max_kv_len,
+                                 const muse_kv_cache* cache, void* out, void* stream) {
+  int32_t rc = check_params(params);
+  if (rc) return rc;
+  if (B < 0) return fail(MUSE_ERR_INVALID_ARG, "B must be >= 0");
+  if (max_kv_len < 1) return fail(MUSE_ERR_INVALID_ARG, "max_kv_len must be >= 1");
+  rc = check_cache(params, B, max_kv_len, cache);
+  if (rc) return rc;
+  if (B == 0) return ok();
+  const size_t need = decode_ws(params, B, max_kv_len, cache);
+  if (need > MUSE_DECODE_NOALLOC_SCRATCH_BYTES)
+    return fail(MUSE_ERR_WORKSPACE,
+                "muse_attn_decode_noalloc: this call needs %zu bytes of scratch, above its fixed %zu; "
+                "use muse_attn_decode with a workspace",
+                need, static_cast<size_t>(MUSE_DECODE_NOALLOC_SCRATCH_BYTES));
+  rc = check_device();
+  if (rc) return rc;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  const int64_t qs = static_cast<int64_t>(params->num_q_heads) * params->head_dim;
+  const int64_t ks = static_cast<int64_t>(params->num_kv_heads) * params->head_dim;
+  return decode_call(params, B, q_new, qs, k_new, v_new, ks, gate, qs, kv_len, max_kv_len, cache, out, ws,
+                     MUSE_DECODE_NOALLOC_SCRATCH_BYTES, stream);
+}
 
 size_t muse_attn_block_prefill_workspace_size(const muse_attn_params* params, const muse_block_weights* weights,
                                               int32_t B, int32_t T) {

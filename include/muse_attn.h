@@ -231,6 +231,28 @@ int32_t muse_attn_decode(const muse_attn_params* params, int32_t B,
 size_t muse_attn_decode_workspace_size(const muse_attn_params* params, int32_t B,
                                        int32_t max_kv_len, const muse_kv_cache* cache);
 
+/* muse_attn_decode_noalloc: muse_attn_decode without a workspace argument,
+ * for callers that cannot allocate device memory around the call (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, layouts, results and cache update as
+ * muse_attn_decode; the call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine).
+ * Its scratch is a fixed device array inside the library of
+ * MUSE_DECODE_NOALLOC_SCRATCH_BYTES (80 MiB) per device, held from the
+ * library's first use on a device until the process ends.  A call whose
+ * muse_attn_decode_workspace_size() exceeds that returns
+ * MUSE_ERR_WORKSPACE before any launch.  (80 MiB holds the decode of 16
+ * sequences x 16 KV heads of width 64 at lengths up to 2^20, 67 MiB.)
+ * Every call on one device shares that device's array: calls that overlap
+ * on one device (different streams, host threads) race and must be
+ * serialized by the caller. */
+#define MUSE_DECODE_NOALLOC_SCRATCH_BYTES (80u << 20)
+
+int32_t muse_attn_decode_noalloc(const muse_attn_params* params, int32_t B,
+                                 const void* q_new, const void* k_new, const void* v_new,
+                                 const void* gate, const int32_t* kv_len, int32_t max_kv_len,
+                                 const muse_kv_cache* cache, void* out, void* stream);
+
 /* The attention half of one decoder block around the layer (deep dive,
  * section 2.1 forward walk; section 5.1 for Glimmer's sandwich norms, 5.2 for
  * Spark's norm-preserving residual gate, 5.3 for the RMSNorm variants):

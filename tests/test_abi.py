@@ -199,6 +199,24 @@ def test_decode_argument_checks():
     assert call(capi.MuseKvCache(7, 0, FAKE, FAKE, None, 0, 0, 0)) == 1
 
 
+def test_decode_noalloc_rejects_beyond_its_scratch():
+    """The allocation-free decode checks its scratch need against the fixed
+    array before any launch (and before looking for a device)."""
+    capi, lib = _lib()
+    pp = params(capi, num_q_heads=128, num_kv_heads=16, head_dim=64, qk_scale=5.473, out_norm=1, sliding_window=0,
+                rope_theta=0.0)
+    paged = capi.MuseKvCache(capi.MUSE_KV_PAGED, 0, FAKE, FAKE, FAKE, 1 << 15, 32, 10000)
+    need = lib.muse_attn_decode_workspace_size(ctypes.byref(pp), 64, 1 << 20, ctypes.byref(paged))
+    assert need > (80 << 20)
+    rc = lib.muse_attn_decode_noalloc(ctypes.byref(pp), 64, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20,
+                                      ctypes.byref(paged), FAKE, None)
+    assert rc == 3 and b"scratch" in lib.muse_last_error()
+    # the full decode workload (16 sequences up to 2^20 positions) fits
+    assert lib.muse_attn_decode_workspace_size(ctypes.byref(pp), 16, 1 << 20, ctypes.byref(paged)) <= (80 << 20)
+    assert lib.muse_attn_decode_noalloc(ctypes.byref(pp), 16, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None,
+                                        FAKE, None) == 1
+
+
 def test_rope_qknorm_argument_checks():
     capi, lib = _lib()
     p = params(capi)
