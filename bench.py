@@ -7,12 +7,19 @@ head width 128, causal window 2048, RoPE base 10000, multiplier 3.87.
 `value` is that step's algorithmic throughput (4 * Hq * D FLOPs per visible
 (query, key) pair) in TFLOP/s.  The same JSON line carries:
   roofline      - the attention kernel's duration from HIP events recorded
-                  around it on the launch stream, against the bf16/f16 MFMA peak;
+                  around it on the launch stream, against the bf16/f16 MFMA peak,
+                  with the HBM bytes per launch from calibrated rocprofv3
+                  counters when they were taken on the current kernel sources;
   cpu_baseline  - the fp64 oracle on a bounded sample of the same workload;
-  decode        - the Spark decode step over a paged global-layer cache
-                  (16 sequences, lengths uniform in [131072, 1048576]) and a
-                  2048-entry ring, in GB/s of cached K/V read, against HBM peak;
-  prefill_other - the other prefill workloads (one or two timed reps each).
+  one block per other workload, each with its own roofline, oracle baseline
+  and median over timed reps:
+    glimmer_global_prefill_128k - 131072 tokens, global NoPE layer;
+    spark_prefill_256k          - 262144 tokens, one local and one global layer;
+    spark_decode                - 16 sequences, lengths uniform in [131072,
+                                  1048576], over a paged global-layer cache (bf16
+                                  and E4M3) and a 2048-entry ring, in GB/s of
+                                  cached K/V read against HBM peak;
+  and the next rows: chunked prefill, the drafter block, the decoder block.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
 """
@@ -92,8 +99,9 @@ def committed_traffic(name, digest):
     return t.get("hbm_bytes_per_launch")
 
 
-def timed_steps(fn, steps, warmup, events, torch):
-    """Run warmup + steps; returns (wall ms per step, mean attention-kernel ms)."""
+def timed_steps(fn, steps, warmup, events, torch, per_step=None):
+    """Run warmup + steps; returns (wall ms per step, mean attention-kernel ms).
+    per_step (a list) receives each step's attention-kernel ms."""
     import global_muse_rope_amd._capi as capi
     lib = capi.load()
     for _ in range(warmup):
@@ -107,7 +115,10 @@ def timed_steps(fn, steps, warmup, events, torch):
     capi.check(lib.muse_profile_events(None, None))
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    kern = sum(events.elapsed_ms(a, b) for a, b in pairs) / steps
+    each = [events.elapsed_ms(a, b) for a, b in pairs]
+    if per_step is not None:
+        per_step.extend(each)
+    kern = sum(each) / steps
     for a, b in pairs:
         events.destroy(a)
         events.destroy(b)
@@ -126,10 +137,11 @@ def prefill_case(cfg, steps, warmup, events, torch, ma, keep=False):
     def step():
         ma.prefill(lp, x["q"], x["k"], x["v"], x["g"], out=out, workspace=ws)
 
-    wall, kern = timed_steps(step, steps, warmup, events, torch)
+    each = []
+    wall, kern = timed_steps(step, steps, warmup, events, torch, each)
     flops = acc.prefill_flops(L.hq, L.d, cfg.batch, cfg.seq, L.window)
     res = {"ms_per_step": wall, "tflops": flops / (wall * 1e-3) / 1e12, "kernel_ms": kern,
-           "kernel_tflops": flops / (kern * 1e-3) / 1e12, "flops": flops}
+           "kernel_tflops": flops / (kern * 1e-3) / 1e12, "flops": flops, "kernel_ms_each": each}
     if keep:
         res["_tensors"] = (x, out)
     else:
@@ -187,6 +199,8 @@ def block_case(cfg, steps, warmup, events, torch, ma):
     def step():
         ma.attention_block_prefill(lp, w, x, out=out, workspace=ws)
 
+    # pick the projection GEMMs' algorithms once, outside the timed region
+    ma.attention_block_tune(lp, w, cfg.batch * cfg.seq, workspace=ws)
     wall, kern = timed_steps(step, steps, warmup, events, torch)
     flops = acc.block_flops(L.hq, L.hkv, L.d, cfg.hidden, cfg.batch, cfg.seq, L.window)
     res = {"ms_per_step": wall, "tflops": flops / (wall * 1e-3) / 1e12, "attn_kernel_ms": kern, "flops": flops}
@@ -223,6 +237,10 @@ def block_decode_case(cfg, steps, warmup, events, torch, ma, flush=False):
             scrub.view(torch.int64).sum()   # evict the 256 MB last-level cache (a read: no dirty lines left)
         ma.attention_block_decode(lp, wb, x, s["kv_len"], s["max_len"], cache, out=out, workspace=ws)
 
+    tune_ws = torch.empty(ma.block_prefill_workspace_size(lp, wb, 1, cfg.batch), dtype=torch.uint8, device="cuda")
+    ma.attention_block_tune(lp, wb, cfg.batch, workspace=tune_ws)
+    del tune_ws
+
     wall, kern = timed_steps(step, steps, warmup, events, torch)
     res = {"ms_per_step": wall, "decode_kernel_ms": kern}
     del s, cache, w, wb, x, out, ws, scrub
@@ -230,7 +248,7 @@ def block_decode_case(cfg, steps, warmup, events, torch, ma, flush=False):
     return res
 
 
-def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False):
+def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False, keep_out=False):
     from synth.device import decode_device_setup
     from global_muse_rope_amd import accounting as acc
     L = cfg.layer
@@ -253,14 +271,18 @@ def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False):
             scrub.view(torch.int64).sum()
         ma.decode(lp, s["q"], s["k"], s["v"], s["g"], s["kv_len"], s["max_len"], s["cache"], out=out, workspace=ws)
 
-    wall, kern = timed_steps(step, steps, warmup, events, torch)
+    each = []
+    wall, kern = timed_steps(step, steps, warmup, events, torch, each)
     eb = 1 if fp8 else 2
     kv_bytes = acc.decode_kv_bytes(L.hkv, L.d, s["lengths"], L.window, eb)
     if fp8:
         kv_bytes += acc.decode_scale_bytes(L.hkv, s["lengths"], L.window, s["page_tokens"])
     io = acc.decode_io_bytes(L.hq, L.hkv, L.d, cfg.batch, eb)
-    res = {"kernel_ms": kern, "kv_bytes": kv_bytes, "gbs": (kv_bytes + io) / (kern * 1e-3) / 1e9,
-           "ms_per_step": wall, "lengths_sum": int(sum(s["lengths"]))}
+    res = {"kernel_ms": kern, "kv_bytes": kv_bytes, "io_bytes": io,
+           "gbs": (kv_bytes + io) / (kern * 1e-3) / 1e9, "ms_per_step": wall,
+           "lengths_sum": int(sum(s["lengths"])), "kernel_ms_each": each, "lengths": s["lengths"]}
+    if keep_out:
+        res["_out"] = out.float().cpu().numpy()
     del s, ws, out, scrub
     torch.cuda.empty_cache()
     return res
@@ -290,32 +312,39 @@ def copy_bandwidth(torch, events, nbytes=2 << 30, reps=5):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def cpu_baseline(cfg, gpu_out, budget_s=15.0):
-    """The fp64 oracle, as it stands, on a bounded sample of rows of the same
-    workload; returns its throughput in TFLOP/s and the GPU/oracle max-abs
-    difference on those rows."""
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        return 1
+
+
+def cpu_baseline(cfg, gpu_out, budget_s=15.0, row_limit=None, kv=None):
+    """The fp64 oracle, as it stands, on a bounded sample of query rows of the
+    same workload: rows below row_limit (default: every row), in a seeded
+    order after the window-edge rows.  Returns its throughput in TFLOP/s, the
+    full-workload oracle time extrapolated per visible pair, and the
+    GPU/oracle max-abs difference on those rows.  kv: host (k, v) of tokens
+    0 .. row_limit - 1, if already regenerated."""
     import numpy as np
     import oracle
     from global_muse_rope_amd import accounting as acc
     from synth.device import host_tokens, host_rows
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
     L = cfg.layer
     T = cfg.seq
-    k = host_tokens(cfg, "k", 0, 0, T)   # [T, Hkv, D] float64
-    v = host_tokens(cfg, "v", 0, 0, T)
+    lim = min(T, row_limit or T)
+    if kv is None:
+        kv = (host_tokens(cfg, "k", 0, 0, lim), host_tokens(cfg, "v", 0, 0, lim))   # [lim, Hkv, D] float64
+    k, v = kv
     rng = np.random.default_rng(1)
-    order = np.concatenate([[0, 1, L.window - 2, L.window - 1, L.window, T - 1],
-                            rng.permutation(T)]).astype(np.int64)
-    gpu = gpu_out.float().cpu().numpy()[0] if gpu_out is not None else None
+    edge = [r for r in [0, 1, L.window - 2, L.window - 1, L.window, lim - 1] if 0 <= r < lim]
+    order = np.concatenate([edge, rng.permutation(lim)]).astype(np.int64)
     t_start = time.perf_counter()
-    done, flops, worst = 0, 0, 0.0
+    done, flops, pairs, worst = 0, 0, 0, 0.0
     elapsed = 0.0
     while done < len(order) and elapsed < budget_s:
-        rows = order[done:done + 128]
+        rows = order[done:done + 64]
         q = host_rows(cfg, "q", 0, rows)
         g = host_rows(cfg, "g", 0, rows)
         t0 = time.perf_counter()
@@ -323,15 +352,66 @@ def cpu_baseline(cfg, gpu_out, budget_s=15.0):
         elapsed += time.perf_counter() - t0
         for r in rows:
             lo, hi = oracle.visible_range(int(r), L.window)
-            flops += acc.flops_per_pair(L.hq, L.d) * (hi - lo + 1)
-        if gpu is not None:
-            worst = max(worst, float(np.max(np.abs(gpu[rows] - y))))
+            pairs += hi - lo + 1
+        if gpu_out is not None:
+            gy = gpu_out[0, torch_index(rows)].float().cpu().numpy()
+            worst = max(worst, float(np.max(np.abs(gy - y))))
         done += len(rows)
+    flops = acc.flops_per_pair(L.hq, L.d) * pairs
     wall = time.perf_counter() - t_start
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} query rows (all {L.hq} heads) of {cfg.name}, chosen by a seeded permutation "
-                      f"plus window-edge rows; {flops / 1e9:.1f} GFLOP in {elapsed:.1f} s of oracle time "
+    total_pairs = acc.visible_pairs(T, L.window) * cfg.batch
+    where = "" if lim == T else f" among the first {lim} tokens"
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(_threads()), "kind": "oracle",
+            "sample": f"{done} query rows{where} (all {L.hq} heads) of {cfg.name}, window-edge rows then a seeded "
+                      f"permutation; {flops / 1e9:.1f} GFLOP in {elapsed:.1f} s of oracle time "
                       f"({wall:.1f} s with input regeneration)",
+            "extrapolated_full_s": elapsed / pairs * total_pairs,
+            "gpu_max_abs_err_on_sample": worst, "cpu_model": cpu_model()}
+
+
+def torch_index(rows):
+    import torch
+    return torch.as_tensor(rows, dtype=torch.int64, device="cuda")
+
+
+def cpu_baseline_decode(cfg, y_gpu, lengths, budget_s=10.0):
+    """The fp64 oracle on the decode workload: (sequence, KV head) pairs of the
+    shortest sequence, each one decode step over its whole history, streamed
+    from the host regeneration of its cached entries.  Rate: cached K and V
+    bytes the oracle reads per second; plus the GPU/oracle max-abs difference
+    on those pairs."""
+    import numpy as np
+    import oracle
+    from synth import device as sd
+    L = cfg.layer
+    G = L.group
+    b = int(np.argmin(lengths))
+    Lb = int(lengths[b])
+    p = Lb - 1
+    lo, _ = oracle.visible_range(p, L.window)
+    new = sd.new_token_host(cfg)
+    elapsed, nbytes, worst, done = 0.0, 0, 0.0, 0
+    t_start = time.perf_counter()
+    for hk in range(L.hkv):
+        if elapsed >= budget_s:
+            break
+        kh = sd.cache_values_host(cfg.seed, b, hk, L.hkv, "k", lo, p, L.d)[:, None, :]
+        vh = sd.cache_values_host(cfg.seed, b, hk, L.hkv, "v", lo, p, L.d)[:, None, :]
+        hs = slice(hk * G, (hk + 1) * G)
+        lay = type(L)(hq=G, hkv=1, d=L.d, window=L.window, theta=L.theta, scale=L.scale, qk_eps=L.qk_eps,
+                      out_norm=L.out_norm, out_eps=L.out_eps)
+        t0 = time.perf_counter()
+        ref = oracle.decode_one(new["q"][b, hs], new["k"][b, hk:hk + 1], new["v"][b, hk:hk + 1], new["g"][b, hs],
+                                kh, vh, lo, Lb, lay)
+        elapsed += time.perf_counter() - t0
+        nbytes += (p - lo) * 2 * L.d * 2
+        worst = max(worst, float(np.max(np.abs(y_gpu[b, hs] - ref))))
+        done += 1
+    wall = time.perf_counter() - t_start
+    return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": int(_threads()), "kind": "oracle",
+            "sample": f"{done} (sequence, KV head) pairs of sequence {b} ({Lb} positions) of {cfg.name}, each one "
+                      f"decode step over {p - lo} cached entries; {nbytes / 1e9:.2f} GB of bf16 K and V in "
+                      f"{elapsed:.2f} s of oracle time ({wall:.1f} s with cache regeneration)",
             "gpu_max_abs_err_on_sample": worst, "cpu_model": cpu_model()}
 
 
@@ -353,9 +433,10 @@ def pmc_pass(torch, ma, workload):
     device copy as the calibration of the byte counters."""
     from synth import workloads as wl
     cfgs = {c.name: c for c in wl.PREFILL + wl.DECODE}
-    cfg = cfgs[workload]
+    fp8 = workload.endswith("_fp8")
+    cfg = cfgs[workload[:-4] if fp8 else workload]
     if cfg in wl.DECODE:
-        decode_case(cfg, 1, 1, HipEvents(), torch, ma)
+        decode_case(cfg, 1, 1, HipEvents(), torch, ma, flush=cfg.layer.window > 0, fp8=fp8)
     else:
         prefill_case(cfg, 1, 1, HipEvents(), torch, ma)
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
@@ -382,7 +463,7 @@ def traffic_summary(workload, kernel, fetch_csv, write_csv, commands):
     counter reads for the pass's plain 1 GiB copy; written next to the other
     profile summaries with the digest of the kernel sources it was taken on."""
     copy_bytes = float(1 << 30)
-    res = {"workload": workload, "kernel": kernel, "commands": commands}
+    res = {"workload": workload, "kernel": kernel, "commands": [c for c in commands.split(" ;; ") if c]}
     total = 0.0
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path)
@@ -403,6 +484,116 @@ def traffic_summary(workload, kernel, fetch_csv, write_csv, commands):
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res))
+
+
+def _dispatch_durations(trace_csv, kernel):
+    """Dispatch id -> duration (ns) of `kernel` from a rocprofv3 kernel-trace CSV."""
+    import csv
+    out = {}
+    with open(trace_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            if kernel in r["Kernel_Name"]:
+                out[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return out
+
+
+def counter_summary(workload, kernel, run_dirs, commands, cus=256, xcds=8):
+    """Markdown summary of SQ/GRBM counter passes over `kernel` (one rocprofv3
+    output directory per pass, each holding run_counter_collection.csv and
+    run_kernel_trace.csv), per dispatch, averaged over the kernel's
+    dispatches, with derived figures.  GRBM_GUI_ACTIVE is summed over the
+    XCDs (its ratio to the kernel's duration is xcds times the shader clock);
+    SQ_VALU_MFMA_BUSY_CYCLES counts SIMD cycles with a matrix instruction in
+    flight; SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_* count wave
+    quad-cycles."""
+    import csv
+    import statistics
+    vals, durs = {}, []
+    for d in run_dirs:
+        dd = _dispatch_durations(os.path.join(d, "run_kernel_trace.csv"), kernel)
+        per = {}
+        with open(os.path.join(d, "run_counter_collection.csv"), newline="") as f:
+            for r in csv.DictReader(f):
+                if kernel in r["Kernel_Name"]:
+                    per.setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        for disp, cs in per.items():
+            for c, v in cs.items():
+                vals.setdefault(c, []).append(v)
+            if disp in dd and "GRBM_GUI_ACTIVE" in cs:
+                durs.append((dd[disp], cs["GRBM_GUI_ACTIVE"]))
+    mean = {c: statistics.fmean(v) for c, v in vals.items()}
+    lines = [f"# `{kernel}` on `{workload}`: SQ and GRBM counters", "",
+             "Counter passes (one rocprofv3 run each, counters per dispatch, with the kernel trace of the same run "
+             "for the durations), then this summary:", "", "```", *commands, "```", "",
+             "| counter | mean per dispatch | dispatches |", "|---|---|---|"]
+    for c in sorted(mean):
+        lines.append(f"| {c} | {mean[c]:.6g} | {len(vals[c])} |")
+    lines += ["", "Derived (per dispatch):", ""]
+    dur_ns = statistics.fmean(d for d, _ in durs) if durs else None
+    grbm = mean.get("GRBM_GUI_ACTIVE")
+    if dur_ns and durs:
+        clk = statistics.fmean(g / xcds / d for d, g in durs)
+        lines.append(f"- kernel duration in the counter runs: {dur_ns / 1e6:.4f} ms; shader clock "
+                     f"GRBM_GUI_ACTIVE / {xcds} / duration = **{clk:.3f} GHz**")
+    if grbm and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+        busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (grbm / xcds * cus * 4)
+        lines.append(f"- matrix cores busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x {cus} CUs x 4 "
+                     f"SIMDs) = **{100 * busy:.1f} %** of the cycles")
+    if grbm and "SQ_BUSY_CU_CYCLES" in mean:
+        lines.append(f"- CUs busy: SQ_BUSY_CU_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x {cus}) = "
+                     f"{100 * mean['SQ_BUSY_CU_CYCLES'] / (grbm / xcds * cus):.1f} %")
+    wc = mean.get("SQ_WAVE_CYCLES")
+    for c, what in (("SQ_WAIT_ANY", "waiting at s_waitcnt"), ("SQ_WAIT_INST_ANY", "waiting to issue"),
+                    ("SQ_ACTIVE_INST_ANY", "issuing"), ("SQ_ACTIVE_INST_VALU", "issuing vector-ALU work"),
+                    ("SQ_ACTIVE_INST_LDS", "issuing LDS work"), ("SQ_WAIT_INST_LDS", "waiting to issue LDS work")):
+        if wc and c in mean:
+            lines.append(f"- share of wave time {what}: {c} / SQ_WAVE_CYCLES = {100 * mean[c] / wc:.1f} %")
+    mf = mean.get("SQ_INSTS_MFMA")
+    for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+        if mf and c in mean:
+            lines.append(f"- {c} per matrix instruction: {mean[c] / mf:.2f}")
+    if "SQ_INSTS_LDS" in mean and "SQ_LDS_BANK_CONFLICT" in mean:
+        lines.append(f"- LDS bank-conflict cycles per LDS instruction: "
+                     f"{mean['SQ_LDS_BANK_CONFLICT'] / mean['SQ_INSTS_LDS']:.4f}")
+    text = "\n".join(lines) + "\n"
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_sq_counters.md")
+    with open(path, "w") as f:
+        f.write(text)
+    print(text)
+
+
+def trace_summary(workload, kernel, stats_csv, bench_log, commands):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of
+    `bench.py --only WORKLOAD`: the library's kernels and the largest others,
+    with the HIP-event figure the same run printed, written next to the other
+    profile summaries."""
+    import csv
+    with open(stats_csv, newline="") as f:
+        rows = list(csv.DictReader(f))
+    lib = [r for r in rows if "muse::" in r["Name"] or "copyBuffer" in r["Name"]]
+    other = [r for r in rows if r not in lib][:3]
+    lines = [f"# `{kernel}` on `{workload}`: rocprofv3 kernel trace", "", "Command (one MI355X):", "", "```",
+             *commands, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in lib + other:
+        name = r["Name"] if len(r["Name"]) <= 90 else r["Name"][:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f}% |")
+    main = [r for r in rows if kernel in r["Name"]]
+    if main:
+        calls = sum(int(r["Calls"]) for r in main)
+        avg = sum(float(r["TotalDurationNs"]) for r in main) / calls
+        lines += ["", f"`{kernel}` average over the trace: {avg / 1e6:.4f} ms over {calls} launches "
+                      "(warm-up launches included)."]
+    with open(bench_log) as f:
+        js = [ln for ln in f if ln.startswith("{")]
+    if js:
+        lines += ["", "The same run's line (HIP events recorded around the kernel on its launch stream, timed steps "
+                      "only):", "", "```", js[-1].strip(), "```"]
+    path = os.path.join(PROFILES, f"{kernel}_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def only_case(name, steps, warmup, torch, ma):
@@ -442,6 +633,103 @@ def only_case(name, steps, warmup, torch, ma):
               flush=True)
 
 
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def _prefill_roofline(r, cfg):
+    digest = source_digest(PREFILL_SOURCES)
+    med = _median(r["kernel_ms_each"])
+    achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+            "frac_at_median": round(r["flops"] / (med * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+            "traffic": committed_traffic(f"prefill_kernel_{cfg.name}", digest), "kernel": "prefill_kernel",
+            "kernel_ms_median": round(med, 4), "kernel_ms_mean": round(r["kernel_ms"], 4),
+            "flops_per_launch": r["flops"], "source_digest": digest}
+
+
+def prefill_block(cfg, steps, warmup, events, torch, ma, cpu=True, row_limit=16384, kv=None):
+    """One prefill workload timed on its own (median over `steps` reps of the
+    attention kernel), with its roofline and the oracle on a row sample."""
+    log(f"prefill {cfg.name}: warmup {warmup}, reps {steps}")
+    r = prefill_case(cfg, steps, warmup, events, torch, ma, keep=True)
+    x, out = r.pop("_tensors")
+    block = {"workload": cfg.name, "value": round(r["tflops"], 2), "unit": "TFLOP/s",
+             "ms_per_step": round(r["ms_per_step"], 4), "reps": steps, "warmup": warmup,
+             "config": {"batch": cfg.batch, "seq_len": cfg.seq, "q_heads": cfg.layer.hq, "kv_heads": cfg.layer.hkv,
+                        "head_dim": cfg.layer.d, "window": cfg.layer.window, "rope_theta": cfg.layer.theta,
+                        "qk_scale": cfg.layer.scale, "out_norm": cfg.layer.out_norm},
+             "roofline": _prefill_roofline(r, cfg)}
+    log(f"  {r['tflops']:.1f} TFLOP/s step, kernel median {block['roofline']['kernel_ms_median']:.3f} ms "
+        f"({block['roofline']['frac']:.3f} of MFMA peak)")
+    if cpu:
+        log(f"cpu baseline {cfg.name}")
+        block["cpu_baseline"] = cpu_baseline(cfg, out, row_limit=row_limit, kv=kv)
+        log(f"  {block['cpu_baseline']['sample']}")
+    del x, out
+    torch.cuda.empty_cache()
+    return block
+
+
+def spark_prefill_block(events, torch, ma, cpu=True):
+    """The Spark 262144-token workload: one local and one global layer (same
+    seeded inputs), each timed and baselined on its own; `value` is the two
+    layers' FLOPs over their summed step time."""
+    from synth import workloads as wl
+    from synth.device import host_tokens
+    kv = None
+    if cpu:
+        lim = 16384
+        kv = (host_tokens(wl.SPARK_LOCAL, "k", 0, 0, lim), host_tokens(wl.SPARK_LOCAL, "v", 0, 0, lim))
+    loc = prefill_block(wl.SPARK_LOCAL, 10, 3, events, torch, ma, cpu=cpu, kv=kv)
+    glo = prefill_block(wl.SPARK_GLOBAL, 3, 2, events, torch, ma, cpu=cpu, kv=kv)
+    flops = loc["roofline"]["flops_per_launch"] + glo["roofline"]["flops_per_launch"]
+    ms = loc["ms_per_step"] + glo["ms_per_step"]
+    return {"workload": "spark_prefill_256k (one local + one global layer)",
+            "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 3),
+            "local": loc, "global": glo}
+
+
+def decode_block(events, torch, ma, copy_gbs, cpu=True):
+    """The Spark decode step: paged global cache (bf16, and E4M3), 2048-entry
+    ring (last-level cache evicted between steps); median split-kernel time
+    over the reps against HBM peak, and the oracle streaming one sequence."""
+    from synth import workloads as wl
+    from global_muse_rope_amd import accounting as acc
+    dec = {}
+    digest = source_digest(DECODE_SOURCES)
+    for dcfg, steps, flush, fp8 in [(wl.SPARK_DECODE_GLOBAL, 10, False, False),
+                                    (wl.SPARK_DECODE_LOCAL, 20, True, False),
+                                    (wl.SPARK_DECODE_GLOBAL, 10, False, True)]:
+        name = dcfg.name + ("_fp8" if fp8 else "")
+        log(f"decode {name}")
+        base = dcfg.name == wl.SPARK_DECODE_GLOBAL.name and not fp8
+        r = decode_case(dcfg, steps, 3, events, torch, ma, flush=flush, fp8=fp8, keep_out=base and cpu)
+        med = _median(r["kernel_ms_each"])
+        gbs = (r["kv_bytes"] + r["io_bytes"]) / (r["kernel_ms"] * 1e-3) / 1e9
+        gbs_med = (r["kv_bytes"] + r["io_bytes"]) / (med * 1e-3) / 1e9
+        log(f"  {gbs:.0f} GB/s, split kernel mean {r['kernel_ms']:.3f} ms, median {med:.3f} ms")
+        dec[name] = {"value": round(gbs, 1), "unit": "GB/s", "kernel": "decode_split_kernel",
+                     "cache_dtype": "e4m3" if fp8 else "bf16", "reps": steps, "warmup": 3,
+                     "kernel_ms_median": round(med, 4), "kernel_ms_mean": round(r["kernel_ms"], 4),
+                     "ms_per_step": round(r["ms_per_step"], 4), "kv_bytes_per_step": r["kv_bytes"],
+                     "cache_flushed": flush,
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "frac_at_median": round(gbs_med / HBM_PEAK_GBS, 4),
+                                  "frac_of_copy": round(gbs / copy_gbs, 4),
+                                  "traffic": committed_traffic(f"decode_split_kernel_{name}", digest),
+                                  "bytes_per_launch": r["kv_bytes"] + r["io_bytes"], "source_digest": digest}}
+        if base and cpu:
+            log("cpu baseline (oracle) spark decode")
+            dec[name]["cpu_baseline"] = cpu_baseline_decode(dcfg, r["_out"], r["lengths"])
+            log(f"  {dec[name]['cpu_baseline']['sample']}")
+    return dec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -456,9 +744,20 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar=("WORKLOAD", "KERNEL", "FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM-traffic summary of two counter passes (no GPU needed)")
     ap.add_argument("--commands", default="", help="the rocprofv3 commands, recorded in the summary")
+    ap.add_argument("--trace-summary", nargs=4, metavar=("WORKLOAD", "KERNEL", "STATS_CSV", "BENCH_LOG"),
+                    help="summarize a rocprofv3 kernel-trace run of --only WORKLOAD (no GPU needed)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="ARG",
+                    help="WORKLOAD KERNEL RUN_DIR...: summarize SQ/GRBM counter passes (no GPU needed)")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary, args.commands)
+        return
+    if args.counter_summary:
+        wlname, kernel, *dirs = args.counter_summary
+        counter_summary(wlname, kernel, dirs, [c for c in args.commands.split(" ;; ") if c])
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary, [c for c in args.commands.split(" ;; ") if c])
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -519,28 +818,17 @@ def main():
     del x, gpu_out
     torch.cuda.empty_cache()
 
+    if not args.quick:
+        result["glimmer_global_prefill_128k"] = prefill_block(wl.GLIMMER_GLOBAL, 5, 2, events, torch, ma,
+                                                              cpu=not args.no_cpu)
+        result["spark_prefill_256k"] = spark_prefill_block(events, torch, ma, cpu=not args.no_cpu)
+
     if not args.no_decode:
         copy_gbs = copy_bandwidth(torch, events)
         log(f"device copy {copy_gbs:.0f} GB/s (read + write)")
         result["hbm_copy_gbs"] = round(copy_gbs, 1)
-        dec = {}
-        for dcfg, steps, flush, fp8 in [(wl.SPARK_DECODE_GLOBAL, 10, False, False),
-                                        (wl.SPARK_DECODE_LOCAL, 20, True, False),
-                                        (wl.SPARK_DECODE_GLOBAL, 10, False, True)]:
-            name = dcfg.name + ("_fp8" if fp8 else "")
-            log(f"decode {name}")
-            r = decode_case(dcfg, steps, 2, events, torch, ma, flush=flush, fp8=fp8)
-            log(f"  {r['gbs']:.0f} GB/s, split kernel {r['kernel_ms']:.3f} ms")
-            dec[name] = {"value": round(r["gbs"], 1), "unit": "GB/s", "kernel": "decode_split_kernel",
-                         "cache_dtype": "e4m3" if fp8 else "bf16",
-                         "kernel_ms": round(r["kernel_ms"], 4), "ms_per_step": round(r["ms_per_step"], 4),
-                         "kv_bytes_per_step": r["kv_bytes"], "cache_flushed": flush,
-                         "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS,
-                                      "unit": "GB/s", "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
-                                      "frac_of_copy": round(r["gbs"] / copy_gbs, 4)}}
-        result["decode"] = dec
+        result["spark_decode"] = decode_block(events, torch, ma, copy_gbs, cpu=not args.no_cpu)
 
-    if not args.no_decode:
         chunks = {}
         for ccfg in wl.CHUNK:
             log(f"prefill chunk {ccfg.name}")
@@ -577,17 +865,6 @@ def main():
                                     "decode_kernel_ms": round(r["decode_kernel_ms"], 4),
                                     "cache_flushed": dcfg.layer.window > 0}
         result["attention_block_decode"] = block_dec
-
-    if not args.quick:
-        other = {}
-        for pcfg in [wl.GLIMMER_GLOBAL, wl.SPARK_LOCAL, wl.SPARK_GLOBAL]:
-            log(f"prefill {pcfg.name}")
-            r = prefill_case(pcfg, 2, 1, events, torch, ma)
-            log(f"  {r['tflops']:.1f} TFLOP/s step, kernel {r['kernel_tflops']:.1f} TFLOP/s")
-            other[pcfg.name] = {"tflops_step": round(r["tflops"], 2), "ms_per_step": round(r["ms_per_step"], 3),
-                                "kernel_tflops": round(r["kernel_tflops"], 2),
-                                "frac_of_mfma_peak": round(r["kernel_tflops"] / MFMA_PEAK_TFLOPS, 4)}
-        result["prefill_other"] = other
 
     print(json.dumps(result), flush=True)
 

@@ -433,6 +433,22 @@ def attention_block_prefill(layer: LayerParams, weights: BlockWeights, x, out=No
     return out
 
 
+def attention_block_tune(layer: LayerParams, weights: BlockWeights, rows: int, workspace=None):
+    """Time hipBLASLt's candidate algorithms for the block's two projection GEMMs
+    at `rows` token rows and record the fastest for later block calls on this
+    device.  Waits for the stream: call it outside timed or captured regions."""
+    torch = _torch()
+    lib = _capi.load()
+    need = block_prefill_workspace_size(layer, weights, 1, rows)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=weights.w_qkvg.device)
+    _check_workspace(workspace, need, weights.w_qkvg.device)
+    p = layer.c()
+    w = weights.c()
+    _capi.check(lib.muse_attn_block_tune(ctypes.byref(p), ctypes.byref(w), int(rows), workspace.data_ptr(),
+                                         workspace.numel(), _stream()))
+
+
 def block_decode_workspace_size(layer: LayerParams, weights: BlockWeights, batch: int, max_kv_len: int,
                                 cache: KvCache) -> int:
     p = layer.c()

@@ -90,6 +90,7 @@ SIGNATURES = {
     "muse_attn_block_prefill_workspace_size": (_sz, [_P, _BW, _i32, _i32]),
     "muse_attn_block_decode": (_i32, [_P, _BW, _i32, _vp, _vp, _i32, _C, _vp, _vp, _sz, _vp]),
     "muse_attn_block_decode_workspace_size": (_sz, [_P, _BW, _i32, _i32, _C]),
+    "muse_attn_block_tune": (_i32, [_P, _BW, _i32, _vp, _sz, _vp]),
     "muse_layer_is_global": (_i32, [_i32, _i32]),
     "muse_last_error": (ctypes.c_char_p, []),
     "muse_version": (_i32, []),

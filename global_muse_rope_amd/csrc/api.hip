@@ -99,12 +99,25 @@ float q_logit_scale(const muse_attn_params* p) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Compute units of the current device (cached per device), or the MI355X's
+// 256 where no device is visible (a workspace-size query on a host without a
+// GPU); the key split of a chunk launch aims at one workgroup per CU.
+int device_cus() {
+  static int cached[kMaxDevices] = {};
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (cached[dev] > 0) return cached[dev];
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  cached[dev] = n;
+  return n;
+}
+
 int64_t prefill_tiles(int32_t T) { return (static_cast<int64_t>(T) + kKeyTile - 1) / kKeyTile; }
 
 // Prefill workspace: the K/V tile images (k_hat fp16 + V^T bf16, padded rows)
 // and, on RoPE layers, the (cos, sin) table for B * T positions.
 struct PrefillWs {
-  size_t tile_bytes, rope_bytes, part_o_bytes, part_l_bytes, total;
+  size_t tile_bytes, rope_bytes, part_o_bytes, part_l_bytes, tile_ms_bytes, total;
   int nsplit;
 };
 
@@ -112,7 +125,7 @@ PrefillWs prefill_ws_layout(const muse_attn_params* p, int32_t B, int32_t T) {
   PrefillWs w;
   w.tile_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * prefill_tiles(T) * tile_chunks(p->head_dim) * 16);
   w.rope_bytes = p->rope_theta > 0.f ? align256(static_cast<size_t>(B) * T * (p->head_dim / 2) * 8) : 0;
-  w.part_o_bytes = w.part_l_bytes = 0;
+  w.part_o_bytes = w.part_l_bytes = w.tile_ms_bytes = 0;
   w.nsplit = 1;
   w.total = w.tile_bytes + w.rope_bytes;
   return w;
@@ -138,17 +151,19 @@ int64_t chunk_qblocks(const muse_attn_params* p, int32_t B, int32_t T) {
 
 // Tile images and the RoPE table, then, when the launch has too few query
 // blocks to fill the chip (a short chunk or a drafter's block), the key
-// pieces' partial sums: O fp32 [nsplit][B][T][Hq][D] and sums [..][Hq].
+// pieces' partial sums: O fp32 [nsplit][B][T][Hq][D] and sums [..][Hq];
+// last the per-tile largest cached-key mean square, fp32 [B][Hkv][n_tiles].
 PrefillWs chunk_ws_layout(const muse_attn_params* p, int32_t B, int32_t T, int32_t max_start) {
   PrefillWs w;
   const int64_t n_tiles = chunk_tiles(p, T, max_start);
   w.tile_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * n_tiles * tile_chunks(p->head_dim) * 16);
   w.rope_bytes = p->rope_theta > 0.f ? align256(static_cast<size_t>(B) * T * (p->head_dim / 2) * 8) : 0;
-  w.nsplit = prefill_key_split(chunk_qblocks(p, B, T), n_tiles);
+  w.nsplit = prefill_key_split(chunk_qblocks(p, B, T), n_tiles, device_cus());
   const size_t rows = static_cast<size_t>(B) * T * p->num_q_heads;
   w.part_o_bytes = w.nsplit > 1 ? align256(w.nsplit * rows * p->head_dim * 4) : 0;
   w.part_l_bytes = w.nsplit > 1 ? align256(w.nsplit * rows * 4) : 0;
-  w.total = w.tile_bytes + w.rope_bytes + w.part_o_bytes + w.part_l_bytes;
+  w.tile_ms_bytes = align256(static_cast<size_t>(B) * p->num_kv_heads * n_tiles * 4);
+  w.total = w.tile_bytes + w.rope_bytes + w.part_o_bytes + w.part_l_bytes + w.tile_ms_bytes;
   return w;
 }
 
@@ -159,9 +174,7 @@ struct DecodePlan {
 
 // Ring entries per split workgroup: a 2048-entry ring splits in two, which
 // measured fastest on a cold cache (256: 11 % slower, 2048: 9 % slower).
-#ifndef MUSE_RING_CHUNK
-#define MUSE_RING_CHUNK 1024
-#endif
+constexpr int kRingChunk = 1024;
 // Paged chunks: 8192 entries (512 KB of a bf16 cache at head width 64) per
 // workgroup measured 3 % faster than 2048 on 16 sequences of up to 2^20
 // positions, and 8 % faster on an E4M3 cache, mostly from fewer partials and
@@ -170,7 +183,7 @@ struct DecodePlan {
 DecodePlan decode_plan(int32_t B, int32_t Hkv, int32_t max_kv_len, const muse_kv_cache* c) {
   DecodePlan d;
   if (c->kind == MUSE_KV_RING) {
-    d.chunk_tokens = c->capacity >= MUSE_RING_CHUNK ? MUSE_RING_CHUNK : ((c->capacity + 31) / 32) * 32;
+    d.chunk_tokens = c->capacity >= kRingChunk ? kRingChunk : ((c->capacity + 31) / 32) * 32;
     d.max_chunks = (c->capacity + d.chunk_tokens - 1) / d.chunk_tokens;
   } else {
     d.chunk_tokens = kPagedChunkMax;
@@ -554,6 +567,8 @@ int32_t chunk_call(const muse_attn_params* params, int32_t B, int32_t T, const v
   kp.max_start = max_start;
   kp.W = params->sliding_window;
   kp.cache = cv;
+  char* ws_parts = static_cast<char*>(workspace) + wl.tile_bytes + wl.rope_bytes;
+  kp.tile_ms = reinterpret_cast<float*>(ws_parts + wl.part_o_bytes + wl.part_l_bytes);
   e = launch_kv_prep(D, B, kp, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "kv_prep launch: %s", hipGetErrorString(e));
 
@@ -586,7 +601,8 @@ int32_t chunk_call(const muse_attn_params* params, int32_t B, int32_t T, const v
   pa.max_start = max_start;
   pa.noncausal = noncausal ? 1 : 0;
   pa.nsplit = wl.nsplit;
-  char* ws_parts = static_cast<char*>(workspace) + wl.tile_bytes + wl.rope_bytes;
+  pa.tile_ms = kp.tile_ms;
+  pa.qbound = static_cast<float>(static_cast<double>(pa.qscale) * D * (1.0 + 1.0 / 256));
   pa.part_o = wl.nsplit > 1 ? reinterpret_cast<float*>(ws_parts) : nullptr;
   pa.part_l = wl.nsplit > 1 ? reinterpret_cast<float*>(ws_parts + wl.part_o_bytes) : nullptr;
   if (g_prof_start) {
@@ -894,6 +910,40 @@ int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block
   ra.eps = 1e-8f;
   e = launch_block_residual(ra, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "residual launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int32_t muse_attn_block_tune(const muse_attn_params* params, const muse_block_weights* w, int32_t rows,
+                             void* workspace, size_t ws_bytes, void* stream) {
+  int32_t rc = check_params(params);
+  if (rc) return rc;
+  if (!w) return fail(MUSE_ERR_INVALID_ARG, "weights is NULL");
+  if (rows <= 0) return fail(MUSE_ERR_INVALID_ARG, "rows must be > 0");
+  if (w->hidden <= 0 || w->hidden % 8 != 0 || w->hidden > kBlockMaxHidden)
+    return fail(MUSE_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 8 up to %d", w->hidden,
+                kBlockMaxHidden);
+  if (!w->w_qkvg || !w->w_o) return fail(MUSE_ERR_INVALID_ARG, "a weight pointer is NULL");
+  if (!aligned16(w->w_qkvg) || !aligned16(w->w_o)) return fail(MUSE_ERR_INVALID_ARG, "weights must be 16-byte aligned");
+  if (!workspace || !aligned16(workspace)) return fail(MUSE_ERR_WORKSPACE, "workspace missing or misaligned");
+  const BlockWs l = block_ws_layout(params, w, 1, rows);
+  if (ws_bytes < l.total) return fail(MUSE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, l.total);
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const int64_t D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
+  const int64_t N = (2 * Hq + 2 * Hkv) * D;
+  // zero activations: the timed runs read defined values
+  hipError_t e = hipMemsetAsync(ws + l.h, 0, l.proj - l.h, st);
+  if (e == hipSuccess) e = hipMemsetAsync(ws + l.o, 0, l.a - l.o, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
+  char msg[256];
+  if (block_gemm(rows, N, w->hidden, ws + l.h, w->w_qkvg, ws + l.proj, ws + l.gemm, kBlockGemmScratch, st, msg,
+                 sizeof(msg), true))
+    return fail(MUSE_ERR_HIP, "q/k/v/gate projection tuning: %s", msg);
+  if (block_gemm(rows, w->hidden, Hq * D, ws + l.o, w->w_o, ws + l.a, ws + l.gemm, kBlockGemmScratch, st, msg,
+                 sizeof(msg), true))
+    return fail(MUSE_ERR_HIP, "o_proj tuning: %s", msg);
   return ok();
 }
 

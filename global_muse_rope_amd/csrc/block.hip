@@ -166,11 +166,13 @@ hipError_t launch_block_residual(const BlockResidualArgs& a, hipStream_t st) {
 // row-major bf16, fp32 accumulation.  In hipBLASLt's column-major terms
 // that is D[n, rows] = op_T(W') * act', with W' = w viewed as [k, n] and
 // act' = act viewed as [k, rows].  One handle per device, created on first
-// use (host state only); the caller's workspace is the GEMM's scratch.
-// The first call of a shape on a device times hipBLASLt's top candidates on
-// the call's own operands (a few runs each, then a wait for the stream) and
-// keeps the fastest for later calls; under stream capture it takes the
-// heuristic's first choice without timing.
+// use, and a record of the algorithm chosen per (device, shape): host state
+// only; the caller's workspace is the GEMM's scratch.  An ordinary call
+// never waits for the device: it runs the recorded algorithm, or on the
+// first call of a shape the heuristic's first choice (and records it).  A
+// tuning call (`tune`) times the heuristic's top candidates on its own
+// operands instead (a few runs each, then a wait for the stream) and
+// records the fastest for the calls that follow.
 // ---------------------------------------------------------------------------
 namespace {
 std::mutex g_lt_mu;
@@ -216,7 +218,7 @@ int fastest_candidate(hipblasLtHandle_t h, hipblasLtMatmulDesc_t desc, hipblasLt
 }  // namespace
 
 int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, void* out, void* ws,
-               size_t ws_bytes, hipStream_t st, char* err, size_t errlen) {
+               size_t ws_bytes, hipStream_t st, char* err, size_t errlen, bool tune) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     snprintf(err, errlen, "no current device");
@@ -261,10 +263,10 @@ int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* 
         have = true;
       }
     }
-    if (!have) {
+    if (!have || tune) {
       hipblasLtMatmulHeuristicResult_t res[kTuneCandidates];
       int found = 0;
-      if (hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, kTuneCandidates, res, &found) !=
+      if (hipblasLtMatmulAlgoGetHeuristic(h, desc, la, lb, lc, lc, pref, tune ? kTuneCandidates : 1, res, &found) !=
               HIPBLAS_STATUS_SUCCESS ||
           found < 1) {
         snprintf(err, errlen, "hipBLASLt found no algorithm for %lld x %lld x %lld", static_cast<long long>(rows),
@@ -272,17 +274,13 @@ int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* 
         rc = 2;
         break;
       }
-      hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-      if (hipStreamIsCapturing(st, &cap) != hipSuccess) cap = hipStreamCaptureStatusActive;
       int pick = 0;
-      if (cap == hipStreamCaptureStatusNone) {
-        if (found > 1) {
-          pick = fastest_candidate(h, desc, la, lb, lc, act, w, out, ws, wsb, st, res, found);
-          if (pick < 0) pick = 0;
-        }
-        std::lock_guard<std::mutex> lk(g_lt_mu);
-        g_algo[key] = res[pick].algo;
+      if (tune && found > 1) {
+        pick = fastest_candidate(h, desc, la, lb, lc, act, w, out, ws, wsb, st, res, found);
+        if (pick < 0) pick = 0;
       }
+      std::lock_guard<std::mutex> lk(g_lt_mu);
+      g_algo[key] = res[pick].algo;
       algo = res[pick].algo;
     }
     const float one = 1.0f, zero = 0.0f;

@@ -162,14 +162,8 @@ constexpr int kChunkBlocks = kPagedChunkMax / 8;
 // latency (measured 5 % faster; the same on pages), while a fourth buffer
 // measured 11 % slower on the ring.  The E4M3 loop is bound by instruction
 // issue: three or four buffers measured 1.5 % and 4 % slower there.
-#ifndef MUSE_DECODE_DEPTH
-#define MUSE_DECODE_DEPTH 3
-#endif
-#ifndef MUSE_DECODE_DEPTH_FP8
-#define MUSE_DECODE_DEPTH_FP8 2
-#endif
-constexpr int kDecodeDepth = MUSE_DECODE_DEPTH;
-constexpr int kDecodeDepthFp8 = MUSE_DECODE_DEPTH_FP8;
+constexpr int kDecodeDepth = 3;
+constexpr int kDecodeDepthFp8 = 2;
 // The running maximum (log2 units) is raised only when a logit exceeds it by
 // more than this, so unnormalized weights stay below 2^kRescaleSlack and most
 // sub-chunks skip the rescale of the accumulators.

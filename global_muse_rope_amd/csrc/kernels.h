@@ -108,6 +108,10 @@ struct KvPrepArgs {
   const int32_t* start;
   int max_start, W;
   CacheView cache;
+  // chunked prefill: per tile, the largest mean square of its cached key
+  // rows as the attention will read them (0 for a tile without any),
+  // [B * Hkv][n_tiles]; every tile's entry is written
+  float* tile_ms;
 };
 
 // Writes a chunk's normalized (and rotated) keys and its values into the
@@ -152,7 +156,20 @@ struct PrefillArgs {
   int nsplit;
   float* part_o;
   float* part_l;
+  // chunked prefill and drafter blocks (null otherwise): per-tile largest
+  // mean square of the cached key rows ([B * Hkv][n_tiles], kv_prep).  A
+  // block's logits are then bounded by qbound * sqrt(max(1, that maximum))
+  // in log2 units (qbound = qscale * D); where that bound exceeds
+  // kLogitCap, every logit of the block is shifted down by the excess, so
+  // no exponential or sum leaves fp32 range.
+  const float* tile_ms;
+  float qbound;
 };
+
+// Largest exponent (log2 units) the max-free softmax lets a logit reach
+// before a block-wide shift applies: 2^96 times 2^20 keys stays below
+// fp32's range with room for |v| up to 2^11.
+constexpr float kLogitCap = 96.0f;
 
 // Finishes a key-split prefill: sums the partials of each output row, then
 // 1/sum, the per-head output norm, the sigmoid gate and the bf16 store.
@@ -231,9 +248,10 @@ hipError_t launch_block_residual(const BlockResidualArgs& a, hipStream_t st);
 hipError_t launch_block_gate_coef(const float* gate, float2* coef, int hidden, float temperature,
                                   float alpha_sq_floor, hipStream_t st);
 // out[rows, n] = act[rows, k] * w[n, k]^T (bf16, fp32 accumulation); returns
-// 0, or non-zero with a message in err
+// 0, or non-zero with a message in err.  tune: time the top candidate
+// algorithms (waits for the stream) and record the fastest for this shape.
 int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, void* out, void* ws,
-               size_t ws_bytes, hipStream_t st, char* err, size_t errlen);
+               size_t ws_bytes, hipStream_t st, char* err, size_t errlen, bool tune = false);
 
 hipError_t launch_rope_qknorm(int d, int out_dtype, const RopeQkArgs& a, hipStream_t st);
 hipError_t launch_rope_table(int d, const RopeTableArgs& a, hipStream_t st);
@@ -242,10 +260,10 @@ hipError_t launch_chunk_append(int d, int B, const ChunkAppendArgs& a, hipStream
 hipError_t launch_prefill(int d, int g, const PrefillArgs& a, hipStream_t st);
 int prefill_rows_per_block(int d, int g);
 // Key pieces per query block for a launch of n_blocks query blocks whose
-// blocks span at most max_tiles key tiles: 1 when the blocks alone fill the
-// chip, else enough pieces for about one workgroup per CU of an MI355X (256),
-// each of at least two tiles (at most 16 pieces).  Depends on the shape only.
-int prefill_key_split(int64_t n_blocks, int64_t max_tiles);
+// blocks span at most max_tiles key tiles on a device of `cus` compute units:
+// 1 when the blocks alone fill the chip, else enough pieces for about one
+// workgroup per CU, each of at least two tiles (at most 16 pieces).
+int prefill_key_split(int64_t n_blocks, int64_t max_tiles, int cus);
 hipError_t launch_prefill_combine(int d, const PrefillCombineArgs& a, hipStream_t st);
 int prefill_qblock_group();
 // ev0/ev1 (may be null): recorded around the split kernel.

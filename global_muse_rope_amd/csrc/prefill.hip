@@ -18,6 +18,10 @@
 //     log2 units.  exp2 of that range, and sums of 2^20 such terms, stay
 //     inside fp32 and bf16 range, so the softmax needs no running maximum and
 //     no rescaling of the accumulator: p = exp2(logit * log2 e) directly.
+//     Cached history (chunked prefill, drafter blocks) is read as stored,
+//     so its keys need not have unit RMS: the block's bound then scales
+//     with the largest cached-key RMS of its range, and logits are shifted
+//     by a constant per block where that bound passes kLogitCap.
 //   * S^T = K * Q^T with v_mfma_f32_32x32x16_f16 (q_hat, k_hat in fp16: the
 //     normalized operands are bounded by sqrt(D) * s, and fp16 keeps 3 more
 //     mantissa bits than bf16); O^T = V^T * P^T with v_mfma_f32_32x32x16_bf16.
@@ -48,14 +52,8 @@ namespace muse {
 constexpr int kQBlockGroup = 8;
 // LDS fragment queue depth (fragments in flight per wave) per head width.
 // Head width 64 keeps the register count low enough for two workgroups per CU.
-#ifndef MUSE_PREFILL_QD_D128
-#define MUSE_PREFILL_QD_D128 8
-#endif
-#ifndef MUSE_PREFILL_QD_D64
-#define MUSE_PREFILL_QD_D64 2
-#endif
-constexpr int kFragQueueD128 = MUSE_PREFILL_QD_D128;
-constexpr int kFragQueueD64 = MUSE_PREFILL_QD_D64;
+constexpr int kFragQueueD128 = 8;
+constexpr int kFragQueueD64 = 2;
 // s_waitcnt immediate that waits for vmcnt(0) only (expcnt and lgkmcnt at
 // their maxima)
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -70,18 +68,11 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // half-tile.  Written as an instruction of its own the compiler keeps its
 // exact lgkmcnt(7) waits; the statement has no register outputs, and its
 // memory clobber keeps LDS accesses from moving across it.
-#ifndef MUSE_PREFILL_ASM_DMA
-#define MUSE_PREFILL_ASM_DMA 1
-#endif
 __device__ __forceinline__ void dma16_to_lds(const u32x4* src, void* lds_wave_base) {
-#if MUSE_PREFILL_ASM_DMA
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
                : "memory", "m0");
-#else
-  copy16_to_lds(src, lds_wave_base);
-#endif
 }
 
 template <int D, int G, int NW, int MB>
@@ -96,7 +87,15 @@ struct PrefillCfg {
 
 // SKIP: waves whose columns all lie past the last query row skip their
 // matrix and vector work (launches whose sequences are shorter than a block).
-template <int D, int G, int NW, int MB, bool SKIP>
+// HMODE: 0, no cached history (whole-sequence prefill): the logit
+// accumulators start at the constant 0.  Cached history read as stored
+// (chunked prefill, drafter blocks) brings a per-block logit bound read from
+// tile_ms, and each such launch is a pair: HMODE 1 computes the blocks whose
+// bound needs no shift (constant 0 start) and skips the others, HMODE 2 the
+// blocks that need one (the accumulators start at the shift) and skips the
+// rest.  One copy of the tile loop per instance keeps the register count
+// (and occupancy) of the common case.
+template <int D, int G, int NW, int MB, bool SKIP, int HMODE>
 __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D, G, NW, MB>;
   using TL = TileLayout<D>;
@@ -208,6 +207,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const int mid_hi = min((key_hi(q0) + 1) / kKeyTile, tile_hi + 1);
   const int m_lo = min(mid_lo, mid_hi);
   const int m_hi = max(mid_hi, m_lo);
+
+  // Logit shift.  With unit-RMS keys every logit lies within +-qbound
+  // (63.2 log2 units).  Cached history is taken as stored, so its key rows
+  // may have a larger RMS: the block's bound grows with the largest of them
+  // over the block's whole tile range (every key piece of a split block
+  // finds the same value), and where it passes kLogitCap the logit
+  // accumulators start at minus the excess.  Unit-RMS caches give exactly 0.
+  float s_init = 0.f;
+  if constexpr (HMODE != 0) {
+    const float* tm = a.tile_ms + static_cast<int64_t>(bh) * a.n_tiles;
+    float m = 1.0f;
+    for (int i = tile_lo + lane; i <= tile_hi; i += kWave) m = fmaxf(m, tm[i]);
+    m = wave_max(m);
+    s_init = -fmaxf(0.f, a.qbound * sqrtf(m) - kLogitCap);
+    // the same in every lane (and in every wave and key piece of the block):
+    // a scalar, so skipping the block is a uniform branch before any barrier
+    s_init = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_init)));
+    if ((HMODE == 1) != (s_init == 0.f)) continue;  // the other launch of the pair computes this block
+  }
 
   // partial sums of output row (t, hq) for this key piece
   const int n_seq = a.batch_heads / a.Hkv;
@@ -405,6 +423,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   };
   auto half_step = [&](const Half& cur, const Half& nxt, f32x16* s_out, bf16x8 (*p_in)[2], f32x16* s_in,
                        bf16x8 (*p_out)[2]) {
+    constexpr bool SHIFTED = HMODE == 2;
     constexpr int NE = 16;  // logits per lane per row block
     // Head width 128 has exponentials on every other matrix item and packs
     // them one item late; at 64 every item has some, and packing at once
@@ -428,7 +447,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s_out[mb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) s_out[mb][e] = SHIFTED ? s_init : 0.f;
 #pragma unroll
     for (int j = 0; j < NI; ++j) {
       __builtin_amdgcn_sched_barrier(0);
@@ -711,22 +730,10 @@ namespace {
 // wave.  Head width 128: 8 waves x 32 rows (two waves per SIMD, so one wave's
 // exponentials overlap the other's matrix-core work).  Head width 64: the
 // same shape needs half the registers, so two workgroups share a CU.
-#ifndef MUSE_PREFILL_WAVES_D128
-#define MUSE_PREFILL_WAVES_D128 8
-#endif
-#ifndef MUSE_PREFILL_MB_D128
-#define MUSE_PREFILL_MB_D128 1
-#endif
-#ifndef MUSE_PREFILL_WAVES_D64
-#define MUSE_PREFILL_WAVES_D64 8
-#endif
-#ifndef MUSE_PREFILL_MB_D64
-#define MUSE_PREFILL_MB_D64 1
-#endif
 template <int D>
 struct LaunchShape {
-  static constexpr int NW = D == 128 ? MUSE_PREFILL_WAVES_D128 : MUSE_PREFILL_WAVES_D64;
-  static constexpr int MB = D == 128 ? MUSE_PREFILL_MB_D128 : MUSE_PREFILL_MB_D64;
+  static constexpr int NW = 8;
+  static constexpr int MB = 1;
 };
 
 // Resident workgroups of one kernel on the current device: CUs times the
@@ -745,12 +752,11 @@ int resident_workgroups(K kernel, int threads, int* cache) {
   return cache[dev];
 }
 
-template <int D, int G>
-hipError_t launch_dg(const PrefillArgs& a, hipStream_t st) {
+template <int D, int G, bool SKIP, int HMODE>
+hipError_t launch_one(const PrefillArgs& a, hipStream_t st) {
   constexpr int NW = LaunchShape<D>::NW, MB = LaunchShape<D>::MB;
   using C = PrefillCfg<D, G, NW, MB>;
-  // a sequence shorter than one query block leaves whole waves without rows
-  auto kernel = a.T < C::BQ ? prefill_kernel<D, G, NW, MB, true> : prefill_kernel<D, G, NW, MB, false>;
+  auto kernel = prefill_kernel<D, G, NW, MB, SKIP, HMODE>;
   const int nlog = a.n_qblocks_pad * a.batch_heads;  // a multiple of 8
   int grid = nlog;
   if (a.nsplit > 1) {
@@ -758,12 +764,29 @@ hipError_t launch_dg(const PrefillArgs& a, hipStream_t st) {
   } else if (D == 128 && a.W > 0) {
     // local layers run a persistent grid of at most one wave of resident
     // workgroups, a multiple of 8 so every XCD gets the same number
-    static int resident[2][kMaxDev] = {};
-    const int cap = resident_workgroups(kernel, C::THREADS, resident[a.T < C::BQ ? 1 : 0]) & ~7;
+    static int resident[kMaxDev] = {};
+    const int cap = resident_workgroups(kernel, C::THREADS, resident) & ~7;
     if (cap >= 8 && cap < nlog) grid = cap;
   }
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(C::THREADS), 0, st, a);
   return hipGetLastError();
+}
+
+template <int D, int G, bool SKIP>
+hipError_t launch_skip(const PrefillArgs& a, hipStream_t st) {
+  if (!a.tile_ms) return launch_one<D, G, SKIP, 0>(a, st);
+  // cached history: the blocks that need no logit shift, then those that do
+  hipError_t e = launch_one<D, G, SKIP, 1>(a, st);
+  if (e != hipSuccess) return e;
+  return launch_one<D, G, SKIP, 2>(a, st);
+}
+
+template <int D, int G>
+hipError_t launch_dg(const PrefillArgs& a, hipStream_t st) {
+  constexpr int NW = LaunchShape<D>::NW, MB = LaunchShape<D>::MB;
+  using C = PrefillCfg<D, G, NW, MB>;
+  // a sequence shorter than one query block leaves whole waves without rows
+  return a.T < C::BQ ? launch_skip<D, G, true>(a, st) : launch_skip<D, G, false>(a, st);
 }
 
 template <int D>
@@ -785,11 +808,8 @@ int prefill_rows_per_block(int d, int) {
 
 int prefill_qblock_group() { return kQBlockGroup; }
 
-#ifndef MUSE_PREFILL_SPLIT_TARGET
-#define MUSE_PREFILL_SPLIT_TARGET 256
-#endif
-int prefill_key_split(int64_t n_blocks, int64_t max_tiles) {
-  constexpr int64_t kFillBlocks = 256, kTargetWorkgroups = MUSE_PREFILL_SPLIT_TARGET, kMaxPieces = 16;
+int prefill_key_split(int64_t n_blocks, int64_t max_tiles, int cus) {
+  const int64_t kFillBlocks = cus, kTargetWorkgroups = cus, kMaxPieces = 16;
   if (n_blocks <= 0 || n_blocks >= kFillBlocks) return 1;
   int64_t s = (kTargetWorkgroups + n_blocks - 1) / n_blocks;
   s = std::min(s, std::min(kMaxPieces, max_tiles / 2));

@@ -124,35 +124,47 @@ __device__ __forceinline__ int cache_vstride(const CacheView& c) {
 // arithmetic as the general path below; absent pages give zeros.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void kv_prep_history_tile(const KvPrepArgs& a, int b, int hk, int pos0, u32x4* tdst) {
+__device__ __forceinline__ void kv_prep_history_tile(const KvPrepArgs& a, int b, int hk, int pos0, u32x4* tdst,
+                                                     float* kss, int64_t tile_index) {
   using TL = TileLayout<D>;
   constexpr int BK = kKeyTile;
   constexpr int KC = D / 8;
   const int tid = threadIdx.x;
   const CacheView& cv = a.cache;
-  // keys: image chunk j is row j / (KC + 1), chunk j % (KC + 1) (the last is the pad)
-  for (int j = tid; j < BK * (KC + 1); j += 256) {
-    const int r = j / (KC + 1), c = j - r * (KC + 1);
+  // keys: KC consecutive lanes carry the KC data chunks of one row (their
+  // sum of squares is a reduction over the group); the pad chunks are
+  // written separately
+  float mrow = 0.f;
+  for (int j = tid; j < BK * KC; j += 256) {
+    const int r = j / KC, c = j - r * KC;
     u32x4 out = {0, 0, 0, 0};
-    if (c < KC) {
-      const CacheLoc cl = cache_loc(cv, b, hk, a.Hkv, D, pos0 + r);
-      if (cl.ok) {
-        float f[8];
-        const int64_t off = cl.k + c * 8;
-        if (cv.fp8) {
-          unpack_bf16x8(e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(cv.k) + off)), f);
-          const float sc = cv.k_scale[cl.si];
+    float s2 = 0.f;
+    const CacheLoc cl = cache_loc(cv, b, hk, a.Hkv, D, pos0 + r);
+    if (cl.ok) {
+      float f[8];
+      const int64_t off = cl.k + c * 8;
+      if (cv.fp8) {
+        unpack_bf16x8(e4m3x8_to_bf16x8(*reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(cv.k) + off)), f);
+        const float sc = cv.k_scale[cl.si];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] *= sc;
-        } else {
-          unpack_bf16x8(*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(cv.k) + off), f);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = pack_f16x2(f[2 * i], f[2 * i + 1]);
+        for (int e = 0; e < 8; ++e) f[e] *= sc;
+      } else {
+        unpack_bf16x8(*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(cv.k) + off), f);
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s2 += f[e] * f[e];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) out[i] = pack_f16x2(f[2 * i], f[2 * i + 1]);
     }
-    tdst[j] = out;
+    mrow = fmaxf(mrow, group_sum<KC>(s2) * (1.0f / D));
+    tdst[r * (KC + 1) + c] = out;
   }
+  for (int r = tid; r < BK; r += 256) tdst[r * (KC + 1) + KC] = u32x4{0, 0, 0, 0};
+  // the tile's largest key mean square (every row is visible history)
+  mrow = wave_max(mrow);
+  if ((tid & 63) == 0) kss[tid >> 6] = mrow;
+  __syncthreads();
+  if (tid == 0) a.tile_ms[tile_index] = fmaxf(fmaxf(kss[0], kss[1]), fmaxf(kss[2], kss[3]));
   // values: item (d, g16) writes image chunks 2 g16 and 2 g16 + 1 of head-dim row d
   u32x4* vdst = tdst + TL::KCHUNKS;
   const int vstride = cache_vstride(cv);
@@ -204,6 +216,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
   constexpr int BK = kKeyTile;
   constexpr int RUN = D / 8;  // elements per thread in each half of the head
   __shared__ uint16_t vs[BK][D + 8];
+  __shared__ float kss[BK];  // chunked prefill: cached key rows' sums of squares, then per-wave maxima
   // KV heads vary fastest over the grid: the workgroups of one tile's heads
   // run together and read each token's row of all heads in one pass
   const int tile = blockIdx.x / a.Hkv;
@@ -227,7 +240,8 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
   if constexpr (CHUNK) {
     // a tile of visible history only (uniform over the workgroup)
     if (pos0 >= need_lo && pos0 + BK <= st) {
-      kv_prep_history_tile<D>(a, b, hk, pos0, a.tiles + (bh * a.n_tiles + tile) * TileLayout<D>::CHUNKS);
+      kv_prep_history_tile<D>(a, b, hk, pos0, a.tiles + (bh * a.n_tiles + tile) * TileLayout<D>::CHUNKS, kss,
+                              bh * a.n_tiles + tile);
       return;
     }
   }
@@ -315,6 +329,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     hi[e] = x1;
   }
   if constexpr (CHUNK) {
+    float hss = 0.f;
     if (hist) {
       // cached keys are taken as stored (absent pages read as zeros)
 #pragma unroll
@@ -326,9 +341,14 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
         for (int e = 0; e < 8; ++e) {
           lo[c * 8 + e] = hok ? hl[e] * hscale : 0.f;
           hi[c * 8 + e] = hok ? hh[e] * hscale : 0.f;
+          hss += lo[c * 8 + e] * lo[c * 8 + e] + hi[c * 8 + e] * hi[c * 8 + e];
         }
       }
     }
+    // the tile's largest cached-key mean square: the row's four lanes, then
+    // the wave, then (after the barrier below) the four waves
+    const float wm = wave_max(group_sum<4>(hss) * (1.0f / D));
+    if ((tid & 63) == 0) kss[tid >> 6] = wm;
   }
   using TL = TileLayout<D>;
   u32x4* tdst = a.tiles + (bh * a.n_tiles + tile) * TL::CHUNKS;
@@ -351,6 +371,9 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
   if (qq == 0) kdst[D / 8] = u32x4{0, 0, 0, 0};
 
   __syncthreads();
+  if constexpr (CHUNK) {
+    if (tid == 0) a.tile_ms[bh * a.n_tiles + tile] = fmaxf(fmaxf(kss[0], kss[1]), fmaxf(kss[2], kss[3]));
+  }
   constexpr int CHUNKS = D * BK / 8;  // 16-byte chunks of the transposed tile
   if constexpr (CHUNK) {
     // cached values of history positions overwrite their staged rows; the

@@ -174,6 +174,14 @@ size_t muse_attn_prefill_workspace_size(const muse_attn_params* params, int32_t 
  * cache: as for muse_attn_decode (a RING needs capacity == W).
  * workspace: at least muse_attn_prefill_chunk_workspace_size() bytes; it
  *   holds a tile image of every sequence's visible history plus the chunk.
+ * Cached keys are taken as stored and need not have unit RMS.  The softmax
+ *   keeps no running maximum: its logits are bounded per query block by
+ *   s * sqrt(D) * max(1, largest RMS of the block's cached key rows), and
+ *   where that bound passes 96 (log2 units) every logit of the block is
+ *   shifted down by the excess, so sums stay in fp32 range.  Outputs are
+ *   exact (to rounding) for cached-key RMS up to about 2.5; beyond that a
+ *   row whose every logit sits far below the bound can lose its weights to
+ *   underflow.  Cached key elements must lie within fp16 range (|x| < 65504).
  * T == 0 or B == 0 is a no-op. */
 int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32_t T,
                                 const void* q, const void* k, const void* v, const void* gate,
@@ -194,10 +202,10 @@ size_t muse_attn_prefill_chunk_workspace_size(const muse_attn_params* params, in
  * directions), and on a window-0 layer always, keys existing up to the
  * block's last position.  The block is not written into the cache (a
  * drafter drops it before the next block).
- * Arguments as for muse_attn_prefill_chunk, except that the cache only needs
- * positions below start[b] (a PAGED cache: max_start <= max_pages_per_seq *
- * page_tokens) and is left unchanged; a start outside [0, max_start] gives
- * zero output.
+ * Arguments as for muse_attn_prefill_chunk (including its bound on logits
+ * over cached keys), except that the cache only needs positions below
+ * start[b] (a PAGED cache: max_start <= max_pages_per_seq * page_tokens) and
+ * is left unchanged; a start outside [0, max_start] gives zero output.
  * workspace: at least muse_attn_draft_block_workspace_size() bytes. */
 int32_t muse_attn_draft_block(const muse_attn_params* params, int32_t B, int32_t T,
                               const void* q, const void* k, const void* v, const void* gate,
@@ -277,12 +285,13 @@ typedef struct muse_block_weights {
 
 /* muse_attn_block_prefill: the block's attention half over B sequences of T
  * tokens.  x, out: [B, T, hidden] bf16, contiguous.  The projections run as
- * hipBLASLt GEMMs on `stream` with the caller's workspace as their scratch
- * (the library keeps one host-side hipBLASLt handle per device).  The first
- * call with a given GEMM shape on a device times hipBLASLt's candidate
- * algorithms on that call's operands, waiting for the stream, and later
- * calls reuse the fastest (a call under stream capture takes hipBLASLt's
- * first choice instead).
+ * hipBLASLt GEMMs on `stream` with the caller's workspace as their scratch.
+ * Host state: the library keeps one hipBLASLt handle per device (created on
+ * its first block call on that device) and, per device and GEMM shape, the
+ * algorithm it runs: the one muse_attn_block_tune recorded, else hipBLASLt's
+ * first heuristic choice (recorded at the first call of the shape).  Like
+ * every other entry point except muse_attn_block_tune, the call never waits
+ * for the device.
  * workspace: at least muse_attn_block_prefill_workspace_size() bytes.
  * T == 0 or B == 0 is a no-op. */
 int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block_weights* weights,
@@ -311,6 +320,19 @@ int32_t muse_attn_block_decode(const muse_attn_params* params, const muse_block_
 size_t muse_attn_block_decode_workspace_size(const muse_attn_params* params,
                                              const muse_block_weights* weights, int32_t B, int32_t max_kv_len,
                                              const muse_kv_cache* cache);
+
+/* muse_attn_block_tune: optional, explicit tuning of the block's two
+ * projection GEMMs for `rows` token rows (B * T for muse_attn_block_prefill,
+ * B for muse_attn_block_decode) on the current device: times hipBLASLt's top
+ * candidate algorithms on zeroed activations in the workspace and the given
+ * weights, and records the fastest for the block calls that follow.  This
+ * call WAITS for `stream` (it reads the timings back), so it belongs outside
+ * timed or captured regions; the other entry points never wait.  Only
+ * weights->hidden, w_qkvg and w_o are read.
+ * workspace: at least muse_attn_block_prefill_workspace_size(params, weights,
+ * 1, rows) bytes; its contents are clobbered. */
+int32_t muse_attn_block_tune(const muse_attn_params* params, const muse_block_weights* weights, int32_t rows,
+                             void* workspace, size_t ws_bytes, void* stream);
 
 /* Layer schedule: layer i of n_layers is global (full attention, NoPE) iff
  * (n_layers - 1 - i) mod 4 == 0 (deep dive, section 2.2 equation).

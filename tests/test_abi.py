@@ -270,7 +270,8 @@ def test_chunk_and_draft_argument_checks(name):
 def test_chunk_workspace_covers_key_pieces():
     """A launch with fewer query blocks than CUs splits each block over key
     pieces and needs room for their fp32 partial sums; one with many blocks
-    needs only the tile images and the RoPE table."""
+    needs only the tile images, the RoPE table and one fp32 per tile (the
+    tile's largest cached-key mean square)."""
     capi, lib = _lib()
     p = params(capi)  # G = 16: one query block covers 16 tokens
     B, hkv, d, hq = 16, 2, 128, 32
@@ -285,7 +286,8 @@ def test_chunk_workspace_covers_key_pieces():
         assert small >= base + 2 * B * 16 * hq * (d + 1) * 4
         # 4096 tokens: 512 query blocks, not split
         big = wsf(ctypes.byref(p), B, 4096, 131072)
-        assert big == _align(tiles(4096, hist)) + _align(rope(4096))
+        n_tiles = (hist + 4096 + 63) // 64
+        assert big == _align(tiles(4096, hist)) + _align(rope(4096)) + _align(B * hkv * n_tiles * 4)
 
 
 def test_block_prefill_argument_checks():
@@ -316,3 +318,22 @@ def test_block_prefill_argument_checks():
     # the workspace holds the bf16 intermediates (h, the projection, o, a) at least
     n = (2 * 128 + 2 * 16) * 64
     assert need >= 256 * (8192 + n + 128 * 64 + 8192) * 2
+
+
+def test_only_the_tuning_call_waits_for_the_device():
+    """Calls are asynchronous: the only host waits in the library sit in the
+    GEMM candidate timing, and only muse_attn_block_tune asks for it."""
+    import re
+    src = os.path.join(ROOT, "global_muse_rope_amd", "csrc")
+    waits = re.compile(r"hip(Event|Device|Stream)Synchronize|hipMemcpy(?!Async)|hipFree\b|hipMalloc\b")
+    for name in sorted(os.listdir(src)):
+        text = open(os.path.join(src, name)).read()
+        for m in waits.finditer(text):
+            enclosing = text.rfind("int fastest_candidate(", 0, m.start())
+            assert name == "block.hip" and enclosing >= 0 and text.find("\nint block_gemm(", enclosing) > m.start(), \
+                f"{name}: {m.group(0)} outside the candidate timing"
+    api = open(os.path.join(src, "api.hip")).read()
+    tuned = [m.start() for m in re.finditer(r"block_gemm\([^;]*,\s*true\)", api, re.S)]
+    assert tuned, "the tuning entry point asks for candidate timing"
+    for pos in tuned:
+        assert api.rfind("int32_t muse_attn_block_tune(", 0, pos) > api.rfind("int32_t muse_attn_block_decode(", 0, pos)

@@ -24,7 +24,7 @@ def _f(bits):
     return synth.bf16_bits_to_f64(bits)
 
 
-def make_chunk_cache(kind, layer, starts, T, page_tokens, use_fp8, seed=3, max_start=0):
+def make_chunk_cache(kind, layer, starts, T, page_tokens, use_fp8, seed=3, max_start=0, key_gain=None):
     """A cache holding each sequence's history before its chunk: a ring the
     last min(start, W) positions, a paged cache positions 0 .. start - 1 with
     pages mapped up to start + T - 1.  Returns the cache, the stored history
@@ -40,6 +40,10 @@ def make_chunk_cache(kind, layer, starts, T, page_tokens, use_fp8, seed=3, max_s
     else:
         kst = synth.normal_bf16_bits(seed, 40, (B, maxs, hkv, d))
         vst = synth.normal_bf16_bits(seed, 41, (B, maxs, hkv, d))
+        if key_gain is not None:
+            # cached keys of sequence b with RMS about key_gain[b] (stored as bf16)
+            g = np.asarray(key_gain, dtype=np.float32)[:, None, None, None]
+            kst = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(kst) * g)
     edt = np.uint8 if use_fp8 else np.uint16
     rng = np.random.default_rng(seed)
     if kind == "ring":
@@ -92,12 +96,12 @@ def make_chunk_cache(kind, layer, starts, T, page_tokens, use_fp8, seed=3, max_s
     return cache, hk, hv, kc, vc, ks, vs, table
 
 
-def run_chunk_case(kind, layer, starts, T, page_tokens=32, use_fp8=False, max_start=None, bad=()):
+def run_chunk_case(kind, layer, starts, T, page_tokens=32, use_fp8=False, max_start=None, bad=(), key_gain=None):
     B = len(starts)
     d = layer.d
     valid_starts = [s if b not in bad else 0 for b, s in enumerate(starts)]
     cache, hk, hv, kc0, vc0, ks, vs, table = make_chunk_cache(kind, layer, valid_starts, T, page_tokens, use_fp8,
-                                                              max_start=max_start or 0)
+                                                              max_start=max_start or 0, key_gain=key_gain)
     bits = {n: synth.normal_bf16_bits(7, sid, shp) for n, sid, shp in
             [("q", 1, (B, T, layer.hq, d)), ("k", 2, (B, T, layer.hkv, d)), ("v", 3, (B, T, layer.hkv, d)),
              ("g", 4, (B, T, layer.hq, d))]}
@@ -242,10 +246,11 @@ def test_prefill_chunk_zero_start_matches_prefill(T):
 # Non-causal drafter block over a cached context
 # ---------------------------------------------------------------------------
 
-def run_block_case(kind, layer, starts, T, page_tokens=32, use_fp8=False):
+def run_block_case(kind, layer, starts, T, page_tokens=32, use_fp8=False, key_gain=None):
     B = len(starts)
     d = layer.d
-    cache, hk, hv, kc0, vc0, ks, vs, table = make_chunk_cache(kind, layer, starts, T, page_tokens, use_fp8)
+    cache, hk, hv, kc0, vc0, ks, vs, table = make_chunk_cache(kind, layer, starts, T, page_tokens, use_fp8,
+                                                              key_gain=key_gain)
     bits = {n: synth.normal_bf16_bits(8, sid, shp) for n, sid, shp in
             [("q", 1, (B, T, layer.hq, d)), ("k", 2, (B, T, layer.hkv, d)), ("v", 3, (B, T, layer.hkv, d)),
              ("g", 4, (B, T, layer.hq, d))]}
@@ -286,3 +291,24 @@ BLOCK_CASES = [
 def test_draft_block_parity(case, use_fp8):
     kind, layer, starts, T, pt = case
     run_block_case(kind, layer, starts, T, page_tokens=pt or 32, use_fp8=use_fp8)
+
+
+# ---------------------------------------------------------------------------
+# Cached keys above unit RMS
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("draft", [False, True], ids=["chunk", "block"])
+@pytest.mark.parametrize("kind,window", [("ring", 256), ("paged", 0)])
+def test_history_keys_above_unit_rms(kind, window, draft):
+    """The cache is read as stored, so its key rows need not have RMS 1 (a
+    cache written by other code, a mis-set E4M3 scale).  With RMS 1.5, 2 and
+    2.5 the logits reach 95, 126 and 158 in log2 units, beyond what the
+    max-free exponential takes unshifted; the outputs stay finite and within
+    the tolerance of the oracle's max-subtracted softmax."""
+    layer = Layer(window=window, theta=10000.0 if window else 0.0, **SPARK_SMALL)
+    starts = [300, 700, 1000]
+    gain = [1.5, 2.0, 2.5]
+    if draft:
+        run_block_case(kind, layer, starts, 16, page_tokens=32, key_gain=gain)
+    else:
+        run_chunk_case(kind, layer, starts, 100, page_tokens=32, key_gain=gain)

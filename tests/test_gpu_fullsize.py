@@ -147,14 +147,23 @@ def oracle_decode_pair(cfg, new, b, hk, L_b):
                              k_hist, v_hist, lo, L_b, group_layer(lay))
 
 
+def paged_pairs(lengths, hkv):
+    """(sequence, KV head) pairs checked on the paged workload: the two
+    shortest sequences and the two longest (near 2^20 positions: about 122
+    chunks of 8192 entries, 7-8 chunks per combine wave), two or more KV heads
+    of each, the first and last heads among them."""
+    order = np.argsort(lengths)
+    return [(int(order[0]), 0), (int(order[0]), hkv - 1), (int(order[1]), 5),
+            (int(order[-1]), 0), (int(order[-1]), hkv - 1), (int(order[-2]), 3), (int(order[-2]), 10)]
+
+
 def test_decode_fullsize_global_paged_sampled():
     cfg = wl.SPARK_DECODE_GLOBAL
     print(f"decode full size {cfg.name}", flush=True)
     y, lengths = _decode_run(cfg)
     assert np.isfinite(y).all()
     new = sd.new_token_host(cfg)
-    order = np.argsort(lengths)
-    pairs = [(int(order[0]), 0), (int(order[0]), cfg.layer.hkv - 1), (int(order[1]), 5)]
+    pairs = paged_pairs(lengths, cfg.layer.hkv)
     worst = 0.0
     t = time.time()
     for b, hk in pairs:
@@ -213,12 +222,11 @@ def test_decode_fullsize_fp8_sampled(cfg):
     y, lengths, extra = _decode_run(cfg, fp8=True)
     assert np.isfinite(y).all()
     new = sd.new_token_host(cfg)
-    order = np.argsort(lengths)
     G = cfg.layer.group
     if cfg.layer.window:
         pairs = [(b, hk) for b in range(cfg.batch) for hk in range(cfg.layer.hkv)]
     else:
-        pairs = [(int(order[0]), 0), (int(order[0]), cfg.layer.hkv - 1), (int(order[1]), 5)]
+        pairs = paged_pairs(lengths, cfg.layer.hkv)
     worst = 0.0
     t = time.time()
     for b, hk in pairs:
