@@ -276,21 +276,26 @@ CacheView cache_view(const muse_kv_cache* c) {
   return v;
 }
 
-// The block's workspace: h, the q/k/v/gate projection, o and the o_proj
-// output (bf16 rows), the GEMM scratch, then the layer's own workspace.
+// The block's workspace: h as bf16 hi rows then lo rows [2R, hidden]; the
+// projection of both halves in fp32 [2R, N]; the layer's inputs [R, N]
+// (q, k, gate fp16, v bf16); o [R, Hq D] bf16; the o_proj output [R, hidden]
+// fp32; the residual gate's coefficients; the GEMM scratch; then the
+// layer's own workspace.
 constexpr size_t kBlockGemmScratch = size_t(64) << 20;
 struct BlockWs {
-  size_t h, proj, o, a, coef, gemm, attn, total;
+  size_t h, proj, lay, o, a, coef, gemm, attn, total;
 };
 BlockWs block_ws_layout(const muse_attn_params* p, const muse_block_weights* w, int32_t B, int32_t T) {
   const size_t R = static_cast<size_t>(B) * T;
   const size_t D = p->head_dim, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
+  const size_t N = (2 * Hq + 2 * Hkv) * D;
   BlockWs l;
   l.h = 0;
-  l.proj = l.h + align256(R * w->hidden * 2);
-  l.o = l.proj + align256(R * (2 * Hq + 2 * Hkv) * D * 2);
+  l.proj = l.h + align256(2 * R * w->hidden * 2);
+  l.lay = l.proj + align256(2 * R * N * 4);
+  l.o = l.lay + align256(R * N * 2);
   l.a = l.o + align256(R * Hq * D * 2);
-  l.coef = l.a + align256(R * w->hidden * 2);
+  l.coef = l.a + align256(R * w->hidden * 4);
   l.gemm = l.coef + align256(static_cast<size_t>(w->hidden) * 8);
   l.attn = l.gemm + kBlockGemmScratch;
   l.total = l.attn + prefill_ws(p, B, T);
@@ -378,9 +383,14 @@ size_t muse_attn_prefill_workspace_size(const muse_attn_params* params, int32_t 
   return prefill_ws(params, B, T);
 }
 
-int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, const void* q, const void* k,
-                          const void* v, const void* gate, const int64_t* strides, const int32_t* positions,
-                          void* out, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// The whole-sequence prefill; in_f16: q, k and gate arrive in fp16 (the
+// decoder block's projections), else bf16 (the public entry point).
+int32_t prefill_call(const muse_attn_params* params, int32_t B, int32_t T, const void* q, const void* k,
+                     const void* v, const void* gate, const int64_t* strides, const int32_t* positions, void* out,
+                     void* workspace, size_t ws_bytes, void* stream, int in_f16) {
   int32_t rc = check_params(params);
   if (rc) return rc;
   if (B < 0 || T < 0) return fail(MUSE_ERR_INVALID_ARG, "B and T must be >= 0");
@@ -438,6 +448,7 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   kp.n_tiles = static_cast<int>(n_tiles);
   kp.eps = params->qk_norm_eps;
   kp.tiles = tiles;
+  kp.k_f16 = in_f16;
   e = launch_kv_prep(D, B, kp, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "kv_prep launch: %s", hipGetErrorString(e));
 
@@ -448,6 +459,7 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
   PrefillArgs pa{};
   pa.q = static_cast<const uint16_t*>(q);
   pa.gate = static_cast<const uint16_t*>(gate);
+  pa.in_f16 = in_f16;
   pa.out = static_cast<uint16_t*>(out);
   pa.tiles = tiles;
   pa.q_sb = s[0];
@@ -480,6 +492,15 @@ int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, 
     if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
   }
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+int32_t muse_attn_prefill(const muse_attn_params* params, int32_t B, int32_t T, const void* q, const void* k,
+                          const void* v, const void* gate, const int64_t* strides, const int32_t* positions,
+                          void* out, void* workspace, size_t ws_bytes, void* stream) {
+  return prefill_call(params, B, T, q, k, v, gate, strides, positions, out, workspace, ws_bytes, stream, 0);
 }
 
 size_t muse_attn_prefill_chunk_workspace_size(const muse_attn_params* params, int32_t B, int32_t T,
@@ -662,7 +683,7 @@ int32_t chunk_call(const muse_attn_params* params, int32_t B, int32_t T, const v
 int32_t decode_call(const muse_attn_params* params, int32_t B, const void* q_new, int64_t q_sb, const void* k_new,
                     const void* v_new, int64_t kv_sb, const void* gate, int64_t g_sb, const int32_t* kv_len,
                     int32_t max_kv_len, const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes,
-                    void* stream);
+                    void* stream, int in_f16 = 0);
 }  // namespace
 
 extern "C" {
@@ -715,7 +736,7 @@ namespace {
 int32_t decode_call(const muse_attn_params* params, int32_t B, const void* q_new, int64_t q_sb, const void* k_new,
                     const void* v_new, int64_t kv_sb, const void* gate, int64_t g_sb, const int32_t* kv_len,
                     int32_t max_kv_len, const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes,
-                    void* stream) {
+                    void* stream, int in_f16) {
   int32_t rc = check_params(params);
   if (rc) return rc;
   if (B < 0) return fail(MUSE_ERR_INVALID_ARG, "B must be >= 0");
@@ -737,6 +758,7 @@ int32_t decode_call(const muse_attn_params* params, int32_t B, const void* q_new
   if (static_cast<int64_t>(B) * Hkv * plan.max_chunks > 0x7fffffffLL)
     return fail(MUSE_ERR_UNSUPPORTED, "problem too large for one launch");
   DecodeArgs a{};
+  a.in_f16 = in_f16;
   a.q_new = static_cast<const uint16_t*>(q_new);
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
@@ -831,6 +853,77 @@ int32_t muse_attn_decode_noalloc(const muse_attn_params* params, int32_t B, cons
                      MUSE_DECODE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
+}  // extern "C"
+
+namespace {
+// The decoder block around the layer, before it: input norm (h as bf16 hi
+// and lo rows), the q/k/v/gate projection of both halves (fp32), and their
+// sum handed to the layer (q, k, gate fp16; v bf16) in `lay`.
+int32_t block_front(const muse_attn_params* params, const muse_block_weights* w, int64_t R, const void* x,
+                    const BlockWs& l, char* ws, hipStream_t st) {
+  const int64_t D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
+  const int64_t N = (2 * Hq + 2 * Hkv) * D;
+  uint16_t* h = reinterpret_cast<uint16_t*>(ws + l.h);
+  BlockNormArgs na{};
+  na.x = static_cast<const uint16_t*>(x);
+  na.w = static_cast<const uint16_t*>(w->in_norm);
+  na.out = h;
+  na.out_lo = h + R * w->hidden;
+  na.rows = R;
+  na.hidden = w->hidden;
+  na.eps = 1e-5f;
+  hipError_t e = launch_block_input_norm(na, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "input norm launch: %s", hipGetErrorString(e));
+  char msg[256];
+  float* proj = reinterpret_cast<float*>(ws + l.proj);
+  if (block_gemm(2 * R, N, w->hidden, h, w->w_qkvg, proj, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
+    return fail(MUSE_ERR_HIP, "q/k/v/gate projection: %s", msg);
+  BlockProjPrepArgs pp{};
+  pp.proj = proj;
+  pp.out = reinterpret_cast<uint16_t*>(ws + l.lay);
+  pp.rows = R;
+  pp.n = static_cast<int>(N);
+  pp.q_end = static_cast<int>(Hq * D);
+  pp.k_end = static_cast<int>((Hq + Hkv) * D);
+  pp.v_end = static_cast<int>((Hq + 2 * Hkv) * D);
+  e = launch_block_proj_prep(pp, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "projection prep launch: %s", hipGetErrorString(e));
+  return MUSE_OK;
+}
+
+// After the layer: o_proj (fp32 out), then the post-attention norm and the
+// residual (Glimmer's centered norm and add, or Spark's residual gate).
+int32_t block_back(const muse_attn_params* params, const muse_block_weights* w, int64_t R, const void* x,
+                   void* out, const BlockWs& l, char* ws, hipStream_t st) {
+  const int64_t D = params->head_dim, Hq = params->num_q_heads;
+  float* a = reinterpret_cast<float*>(ws + l.a);
+  char msg[256];
+  if (block_gemm(R, w->hidden, Hq * D, ws + l.o, w->w_o, a, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
+    return fail(MUSE_ERR_HIP, "o_proj: %s", msg);
+  float2* coef = nullptr;
+  hipError_t e;
+  if (w->residual_gate) {
+    coef = reinterpret_cast<float2*>(ws + l.coef);
+    e = launch_block_gate_coef(w->residual_gate, coef, w->hidden, w->residual_gate_temperature, 1e-3f, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "gate coefficient launch: %s", hipGetErrorString(e));
+  }
+  BlockResidualArgs ra{};
+  ra.x = static_cast<const uint16_t*>(x);
+  ra.branch = a;
+  ra.post_norm = static_cast<const uint16_t*>(w->post_norm);
+  ra.coef = reinterpret_cast<const float*>(coef);
+  ra.out = static_cast<uint16_t*>(out);
+  ra.rows = R;
+  ra.hidden = w->hidden;
+  ra.eps = 1e-8f;
+  e = launch_block_residual(ra, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "residual launch: %s", hipGetErrorString(e));
+  return MUSE_OK;
+}
+}  // namespace
+
+extern "C" {
+
 size_t muse_attn_block_prefill_workspace_size(const muse_attn_params* params, const muse_block_weights* weights,
                                               int32_t B, int32_t T) {
   if (check_params(params) || !weights || B < 0 || T < 0) return 0;
@@ -865,51 +958,16 @@ int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block
   const int64_t R = static_cast<int64_t>(B) * T;
   const int64_t D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
   const int64_t N = (2 * Hq + 2 * Hkv) * D;
-  uint16_t* h = reinterpret_cast<uint16_t*>(ws + l.h);
-  uint16_t* proj = reinterpret_cast<uint16_t*>(ws + l.proj);
-  uint16_t* o = reinterpret_cast<uint16_t*>(ws + l.o);
-  uint16_t* a = reinterpret_cast<uint16_t*>(ws + l.a);
-
-  BlockNormArgs na{};
-  na.x = static_cast<const uint16_t*>(x);
-  na.w = static_cast<const uint16_t*>(w->in_norm);
-  na.out = h;
-  na.rows = R;
-  na.hidden = w->hidden;
-  na.eps = 1e-5f;
-  hipError_t e = launch_block_input_norm(na, st);
-  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "input norm launch: %s", hipGetErrorString(e));
-
-  char msg[256];
-  if (block_gemm(R, N, w->hidden, h, w->w_qkvg, proj, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
-    return fail(MUSE_ERR_HIP, "q/k/v/gate projection: %s", msg);
-
-  // the layer on strided views of the projection: q, k, v, gate columns
-  const int64_t strides[10] = {T * N, N, T * N, N, T * N, N, T * N, N, T * Hq * D, Hq * D};
-  rc = muse_attn_prefill(params, B, T, proj, proj + Hq * D, proj + (Hq + Hkv) * D, proj + (Hq + 2 * Hkv) * D,
-                         strides, nullptr, o, ws + l.attn, l.total - l.attn, stream);
+  rc = block_front(params, w, R, x, l, ws, st);
   if (rc) return rc;
-
-  if (block_gemm(R, w->hidden, Hq * D, o, w->w_o, a, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
-    return fail(MUSE_ERR_HIP, "o_proj: %s", msg);
-
-  float2* coef = nullptr;
-  if (w->residual_gate) {
-    coef = reinterpret_cast<float2*>(ws + l.coef);
-    e = launch_block_gate_coef(w->residual_gate, coef, w->hidden, w->residual_gate_temperature, 1e-3f, st);
-    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "gate coefficient launch: %s", hipGetErrorString(e));
-  }
-  BlockResidualArgs ra{};
-  ra.x = static_cast<const uint16_t*>(x);
-  ra.branch = a;
-  ra.post_norm = static_cast<const uint16_t*>(w->post_norm);
-  ra.coef = reinterpret_cast<const float*>(coef);
-  ra.out = static_cast<uint16_t*>(out);
-  ra.rows = R;
-  ra.hidden = w->hidden;
-  ra.eps = 1e-8f;
-  e = launch_block_residual(ra, st);
-  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "residual launch: %s", hipGetErrorString(e));
+  // the layer on strided views of its inputs: q, k, v, gate columns
+  const uint16_t* lay = reinterpret_cast<const uint16_t*>(ws + l.lay);
+  const int64_t strides[10] = {T * N, N, T * N, N, T * N, N, T * N, N, T * Hq * D, Hq * D};
+  rc = prefill_call(params, B, T, lay, lay + Hq * D, lay + (Hq + Hkv) * D, lay + (Hq + 2 * Hkv) * D, strides,
+                    nullptr, ws + l.o, ws + l.attn, l.total - l.attn, stream, 1);
+  if (rc) return rc;
+  rc = block_back(params, w, R, x, out, l, ws, st);
+  if (rc) return rc;
   return ok();
 }
 
@@ -933,16 +991,16 @@ int32_t muse_attn_block_tune(const muse_attn_params* params, const muse_block_we
   char* ws = static_cast<char*>(workspace);
   const int64_t D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
   const int64_t N = (2 * Hq + 2 * Hkv) * D;
-  // zero activations: the timed runs read defined values
+  // zero activations (h's two halves, o): the timed runs read defined values
   hipError_t e = hipMemsetAsync(ws + l.h, 0, l.proj - l.h, st);
   if (e == hipSuccess) e = hipMemsetAsync(ws + l.o, 0, l.a - l.o, st);
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipMemsetAsync: %s", hipGetErrorString(e));
   char msg[256];
-  if (block_gemm(rows, N, w->hidden, ws + l.h, w->w_qkvg, ws + l.proj, ws + l.gemm, kBlockGemmScratch, st, msg,
-                 sizeof(msg), true))
+  if (block_gemm(2 * static_cast<int64_t>(rows), N, w->hidden, ws + l.h, w->w_qkvg,
+                 reinterpret_cast<float*>(ws + l.proj), ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg), true))
     return fail(MUSE_ERR_HIP, "q/k/v/gate projection tuning: %s", msg);
-  if (block_gemm(rows, w->hidden, Hq * D, ws + l.o, w->w_o, ws + l.a, ws + l.gemm, kBlockGemmScratch, st, msg,
-                 sizeof(msg), true))
+  if (block_gemm(rows, w->hidden, Hq * D, ws + l.o, w->w_o, reinterpret_cast<float*>(ws + l.a), ws + l.gemm,
+                 kBlockGemmScratch, st, msg, sizeof(msg), true))
     return fail(MUSE_ERR_HIP, "o_proj tuning: %s", msg);
   return ok();
 }
@@ -983,50 +1041,15 @@ int32_t muse_attn_block_decode(const muse_attn_params* params, const muse_block_
   char* ws = static_cast<char*>(workspace);
   const int64_t D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
   const int64_t N = (2 * Hq + 2 * Hkv) * D;
-  uint16_t* h = reinterpret_cast<uint16_t*>(ws + l.h);
-  uint16_t* proj = reinterpret_cast<uint16_t*>(ws + l.proj);
-  uint16_t* o = reinterpret_cast<uint16_t*>(ws + l.o);
-  uint16_t* a = reinterpret_cast<uint16_t*>(ws + l.a);
-
-  BlockNormArgs na{};
-  na.x = static_cast<const uint16_t*>(x);
-  na.w = static_cast<const uint16_t*>(w->in_norm);
-  na.out = h;
-  na.rows = B;
-  na.hidden = w->hidden;
-  na.eps = 1e-5f;
-  hipError_t e = launch_block_input_norm(na, st);
-  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "input norm launch: %s", hipGetErrorString(e));
-
-  char msg[256];
-  if (block_gemm(B, N, w->hidden, h, w->w_qkvg, proj, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
-    return fail(MUSE_ERR_HIP, "q/k/v/gate projection: %s", msg);
-
-  // the layer's decode step reads q, k, v and the gate straight from the projection rows
-  rc = decode_call(params, B, proj, N, proj + Hq * D, proj + (Hq + Hkv) * D, N, proj + (Hq + 2 * Hkv) * D, N, kv_len,
-                   max_kv_len, cache, o, ws + l.attn, l.total - l.attn, stream);
+  rc = block_front(params, w, B, x, l, ws, st);
   if (rc) return rc;
-
-  if (block_gemm(B, w->hidden, Hq * D, o, w->w_o, a, ws + l.gemm, kBlockGemmScratch, st, msg, sizeof(msg)))
-    return fail(MUSE_ERR_HIP, "o_proj: %s", msg);
-
-  float2* coef = nullptr;
-  if (w->residual_gate) {
-    coef = reinterpret_cast<float2*>(ws + l.coef);
-    e = launch_block_gate_coef(w->residual_gate, coef, w->hidden, w->residual_gate_temperature, 1e-3f, st);
-    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "gate coefficient launch: %s", hipGetErrorString(e));
-  }
-  BlockResidualArgs ra{};
-  ra.x = static_cast<const uint16_t*>(x);
-  ra.branch = a;
-  ra.post_norm = static_cast<const uint16_t*>(w->post_norm);
-  ra.coef = reinterpret_cast<const float*>(coef);
-  ra.out = static_cast<uint16_t*>(out);
-  ra.rows = B;
-  ra.hidden = w->hidden;
-  ra.eps = 1e-8f;
-  e = launch_block_residual(ra, st);
-  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "residual launch: %s", hipGetErrorString(e));
+  // the layer's decode step reads q, k, v and the gate straight from the rows of its inputs
+  const uint16_t* lay = reinterpret_cast<const uint16_t*>(ws + l.lay);
+  rc = decode_call(params, B, lay, N, lay + Hq * D, lay + (Hq + Hkv) * D, N, lay + (Hq + 2 * Hkv) * D, N, kv_len,
+                   max_kv_len, cache, ws + l.o, ws + l.attn, l.total - l.attn, stream, 1);
+  if (rc) return rc;
+  rc = block_back(params, w, B, x, out, l, ws, st);
+  if (rc) return rc;
   return ok();
 }
 

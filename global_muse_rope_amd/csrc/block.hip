@@ -6,7 +6,12 @@
 // The two projections are plain GEMMs and go to hipBLASLt; the norms and the
 // residual are row kernels here, one workgroup per token row:
 //   input_layernorm: centered RMSNorm, x / sqrt(mean(x^2) + 1e-5) * (1 + w),
-//     the gain formed and applied in fp32 and rounded once to bf16;
+//     the gain formed and applied in fp32, h kept as a pair of bf16 rows
+//     (h_hi = bf16(h), h_lo = bf16(h - h_hi)) so the projection GEMM (bf16
+//     operands, fp32 out) sees h to about 16 bits;
+//   the projections' fp32 sum of the two halves is handed to the layer with
+//     q, k and the gate in fp16 (v in bf16, the type of the layer's value
+//     product), and o_proj's output stays fp32 into the residual;
 //   Glimmer: out = x + a / sqrt(mean(a^2) + 1e-8) * (1 + w_post);
 //   Spark:   out = alpha * x + beta * a / sqrt(mean(a^2) + 1e-8), with
 //     beta = sigmoid(g / T), alpha = sqrt(max(sigmoid(-g / T) (1 + beta), 1e-3))
@@ -62,17 +67,47 @@ __global__ __launch_bounds__(kRowThreads) void block_input_norm_kernel(BlockNorm
   ss = row_sum(ss, red);
   const float rs = 1.0f / sqrtf(ss / a.hidden + a.eps);
   uint16_t* orow = a.out + row * a.hidden;
+  uint16_t* lrow = a.out_lo + row * a.hidden;
 #pragma unroll
   for (int i = 0; i < kMaxChunksPerThread; ++i) {
     const int c = threadIdx.x + i * kRowThreads;
     if (c >= nch) continue;
     float g[8];
     unpack_bf16x8(*reinterpret_cast<const u32x4*>(a.w + 8 * c), g);
-    u32x4 o;
+    u32x4 o, ol;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = pack_bf16x2(v[i][2 * e] * rs * (1.0f + g[2 * e]), v[i][2 * e + 1] * rs * (1.0f + g[2 * e + 1]));
+    for (int e = 0; e < 4; ++e) {
+      const float h0 = v[i][2 * e] * rs * (1.0f + g[2 * e]), h1 = v[i][2 * e + 1] * rs * (1.0f + g[2 * e + 1]);
+      o[e] = pack_bf16x2(h0, h1);
+      ol[e] = pack_bf16x2(h0 - __uint_as_float(o[e] << 16), h1 - __uint_as_float(o[e] & 0xffff0000u));
+    }
     *reinterpret_cast<u32x4*>(orow + 8 * c) = o;
+    *reinterpret_cast<u32x4*>(lrow + 8 * c) = ol;
+  }
+}
+
+// One workgroup per token row: the projection of h as the sum of its hi and
+// lo halves (fp32), q / k / gate written as fp16 and v as bf16.
+__global__ __launch_bounds__(kRowThreads) void block_proj_prep_kernel(BlockProjPrepArgs a) {
+  const int64_t row = blockIdx.x;
+  const float* hi = a.proj + row * a.n;
+  const float* lo = a.proj + (a.rows + row) * a.n;
+  uint16_t* out = a.out + row * a.n;
+  for (int c = threadIdx.x * 8; c < a.n; c += kRowThreads * 8) {
+    const f32x4 h0 = *reinterpret_cast<const f32x4*>(hi + c), h1 = *reinterpret_cast<const f32x4*>(hi + c + 4);
+    const f32x4 l0 = *reinterpret_cast<const f32x4*>(lo + c), l1 = *reinterpret_cast<const f32x4*>(lo + c + 4);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = h0[e] + l0[e];
+      x[e + 4] = h1[e] + l1[e];
+    }
+    // column ranges are multiples of 8: a chunk lies in one of them
+    const bool v_cols = c >= a.k_end && c < a.v_end;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = v_cols ? pack_bf16x2(x[2 * e], x[2 * e + 1]) : pack_f16x2(x[2 * e], x[2 * e + 1]);
+    *reinterpret_cast<u32x4*>(out + c) = w;
   }
 }
 
@@ -80,7 +115,7 @@ __global__ __launch_bounds__(kRowThreads) void block_residual_kernel(BlockResidu
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
   const int nch = a.hidden / 8;
-  const uint16_t* ar = a.branch + row * a.hidden;
+  const float* ar = a.branch + row * a.hidden;
   const uint16_t* xr = a.x + row * a.hidden;
   float v[kMaxChunksPerThread][8];
   u32x4 xw[kMaxChunksPerThread];  // the residual stream, fetched while the branch's norm is reduced
@@ -88,13 +123,18 @@ __global__ __launch_bounds__(kRowThreads) void block_residual_kernel(BlockResidu
 #pragma unroll
   for (int i = 0; i < kMaxChunksPerThread; ++i) {
     const int c = threadIdx.x + i * kRowThreads;
-    u32x4 w = {0, 0, 0, 0};
-    xw[i] = w;
+    f32x4 w0 = {0.f, 0.f, 0.f, 0.f}, w1 = w0;
+    xw[i] = u32x4{0, 0, 0, 0};
     if (c < nch) {
-      w = *reinterpret_cast<const u32x4*>(ar + 8 * c);
+      w0 = *reinterpret_cast<const f32x4*>(ar + 8 * c);
+      w1 = *reinterpret_cast<const f32x4*>(ar + 8 * c + 4);
       xw[i] = *reinterpret_cast<const u32x4*>(xr + 8 * c);
     }
-    unpack_bf16x8(w, v[i]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[i][e] = w0[e];
+      v[i][e + 4] = w1[e];
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
   }
@@ -155,6 +195,12 @@ hipError_t launch_block_input_norm(const BlockNormArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_block_proj_prep(const BlockProjPrepArgs& a, hipStream_t st) {
+  if (a.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(block_proj_prep_kernel, dim3(static_cast<unsigned>(a.rows)), dim3(kRowThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_residual(const BlockResidualArgs& a, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
   hipLaunchKernelGGL(block_residual_kernel, dim3(static_cast<unsigned>(a.rows)), dim3(kRowThreads), 0, st, a);
@@ -163,7 +209,7 @@ hipError_t launch_block_residual(const BlockResidualArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // GEMM through hipBLASLt: out[rows, n] = act[rows, k] * w[n, k]^T, all
-// row-major bf16, fp32 accumulation.  In hipBLASLt's column-major terms
+// row-major, bf16 operands, fp32 accumulation and fp32 out.  In hipBLASLt's column-major terms
 // that is D[n, rows] = op_T(W') * act', with W' = w viewed as [k, n] and
 // act' = act viewed as [k, rows].  One handle per device, created on first
 // use, and a record of the algorithm chosen per (device, shape): host state
@@ -217,7 +263,7 @@ int fastest_candidate(hipblasLtHandle_t h, hipblasLtMatmulDesc_t desc, hipblasLt
 }
 }  // namespace
 
-int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, void* out, void* ws,
+int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, float* out, void* ws,
                size_t ws_bytes, hipStream_t st, char* err, size_t errlen, bool tune) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
@@ -246,7 +292,7 @@ int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* 
       break;
     if (hipblasLtMatrixLayoutCreate(&la, HIP_R_16BF, k, n, k) != HIPBLAS_STATUS_SUCCESS) break;
     if (hipblasLtMatrixLayoutCreate(&lb, HIP_R_16BF, k, rows, k) != HIPBLAS_STATUS_SUCCESS) break;
-    if (hipblasLtMatrixLayoutCreate(&lc, HIP_R_16BF, n, rows, n) != HIPBLAS_STATUS_SUCCESS) break;
+    if (hipblasLtMatrixLayoutCreate(&lc, HIP_R_32F, n, rows, n) != HIPBLAS_STATUS_SUCCESS) break;
     if (hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS) break;
     const uint64_t wsb = ws_bytes;
     if (hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof(wsb)) !=

@@ -55,6 +55,25 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4& w, float* f) {
   }
 }
 
+// Unpack 8 fp16 held in a 16-byte word into floats.
+__device__ __forceinline__ void unpack_f16x8(const u32x4& w, float* f) {
+  const half8 h = __builtin_bit_cast(half8, w);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = static_cast<float>(h[i]);
+}
+
+// 8 values of a 16-bit input tensor: fp16 if f16, else bf16.
+__device__ __forceinline__ void unpack_16x8(const u32x4& w, float* f, bool f16) {
+  if (f16)
+    unpack_f16x8(w, f);
+  else
+    unpack_bf16x8(w, f);
+}
+
+__device__ __forceinline__ float bits16_to_f32(uint16_t b, bool f16) {
+  return f16 ? static_cast<float>(__builtin_bit_cast(half_t, b)) : bf16_bits_to_f32(b);
+}
+
 // OCP E4M3 code of x (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
 // subnormals, no infinities; 0x7F is NaN): round to nearest, ties to an even
 // mantissa, finite magnitudes beyond 448 saturate to 448, NaN gives 0x7F.

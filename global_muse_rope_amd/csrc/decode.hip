@@ -50,8 +50,8 @@ __global__ __launch_bounds__(256) void decode_append_kernel(DecodeArgs a, int hq
   if (valid) {
     const uint16_t* p = is_q ? a.q_new + b * a.q_sb + static_cast<int64_t>(h) * D
                              : a.k_new + b * a.kv_sb + static_cast<int64_t>(h) * D;
-    x0 = bf16_bits_to_f32(p[j]);
-    x1 = bf16_bits_to_f32(p[j + D / 2]);
+    x0 = bits16_to_f32(p[j], a.in_f16);
+    x1 = bits16_to_f32(p[j + D / 2], a.in_f16);
   }
   const float ss = group_sum<LPR>(x0 * x0 + x1 * x1);
   const float r = (is_q ? a.qscale : 1.0f) / sqrtf(ss * (1.0f / D) + a.qk_eps);
@@ -615,7 +615,7 @@ __global__ __launch_bounds__((CombineShape<D, G>::NWC * 64)) void decode_combine
     uint16_t* op = a.out + (static_cast<int64_t>(b) * a.Hkv * G + hq) * D;
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const float gv = bf16_bits_to_f32(gp[lane + 64 * e]);
+      const float gv = bits16_to_f32(gp[lane + 64 * e], a.in_f16);
       const float y = len_ok ? o[e] * rsn / (1.0f + __expf(-gv)) : 0.f;
       op[lane + 64 * e] = f32_to_bf16_bits(y);
     }

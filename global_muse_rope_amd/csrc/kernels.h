@@ -95,8 +95,9 @@ struct CacheView {
 };
 
 struct KvPrepArgs {
-  const uint16_t* k;
+  const uint16_t* k;  // bf16, or fp16 when k_f16 (v is always bf16)
   const uint16_t* v;
+  int k_f16;
   int64_t k_sb, k_st, v_sb, v_st;
   const float2* rope;  // null on NoPE layers
   int rope_batched;    // table rows indexed by b * T + t (else t)
@@ -128,8 +129,9 @@ struct ChunkAppendArgs {
 };
 
 struct PrefillArgs {
-  const uint16_t* q;
+  const uint16_t* q;     // q and gate: bf16, or fp16 when in_f16
   const uint16_t* gate;
+  int in_f16;
   uint16_t* out;
   const u32x4* tiles;  // [B * Hkv][n_tiles][TileLayout<D>::CHUNKS]
   int64_t q_sb, q_st, g_sb, g_st, o_sb, o_st;
@@ -188,6 +190,7 @@ struct PrefillCombineArgs {
 };
 
 struct DecodeArgs {
+  int in_f16;             // q_new, k_new and gate in fp16 instead of bf16 (v_new is always bf16)
   const uint16_t* q_new;  // [B, Hq, D] with batch stride q_sb (elements)
   const uint16_t* k_new;  // [B, Hkv, D] with batch stride kv_sb
   const uint16_t* v_new;  // [B, Hkv, D] with batch stride kv_sb
@@ -225,15 +228,26 @@ constexpr int kBlockMaxHidden = 8192;
 struct BlockNormArgs {
   const uint16_t* x;  // [rows, hidden] bf16
   const uint16_t* w;  // [hidden] bf16 weight (gain 1 + w)
-  uint16_t* out;      // [rows, hidden] bf16
+  uint16_t* out;      // [rows, hidden] bf16: h rounded to bf16 (h_hi)
+  uint16_t* out_lo;   // [rows, hidden] bf16: h - h_hi rounded to bf16
   int64_t rows;
   int hidden;
   float eps;
 };
 
+// The projections' sum over the hi and lo halves of h, handed to the layer:
+// proj [2 rows, n] fp32 (rows of h_hi W^T, then rows of h_lo W^T) -> out
+// [rows, n] 16-bit: q, k and gate columns in fp16, v columns in bf16.
+struct BlockProjPrepArgs {
+  const float* proj;
+  uint16_t* out;
+  int64_t rows;
+  int n, q_end, k_end, v_end;  // column ranges [0, q_end) q, [q_end, k_end) k, [k_end, v_end) v, then gate
+};
+
 struct BlockResidualArgs {
   const uint16_t* x;          // residual stream [rows, hidden] bf16
-  const uint16_t* branch;     // o_proj output [rows, hidden] bf16
+  const float* branch;        // o_proj output [rows, hidden] fp32
   const uint16_t* post_norm;  // plain add: [hidden] bf16 weight (gain 1 + w)
   const float* coef;          // residual gate: [hidden] (alpha, beta) fp32 pairs (null: plain add)
   uint16_t* out;
@@ -243,14 +257,16 @@ struct BlockResidualArgs {
 };
 
 hipError_t launch_block_input_norm(const BlockNormArgs& a, hipStream_t st);
+hipError_t launch_block_proj_prep(const BlockProjPrepArgs& a, hipStream_t st);
 hipError_t launch_block_residual(const BlockResidualArgs& a, hipStream_t st);
 // (alpha, beta) of the residual gate for every channel of g
 hipError_t launch_block_gate_coef(const float* gate, float2* coef, int hidden, float temperature,
                                   float alpha_sq_floor, hipStream_t st);
-// out[rows, n] = act[rows, k] * w[n, k]^T (bf16, fp32 accumulation); returns
-// 0, or non-zero with a message in err.  tune: time the top candidate
-// algorithms (waits for the stream) and record the fastest for this shape.
-int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, void* out, void* ws,
+// out[rows, n] = act[rows, k] * w[n, k]^T (bf16 operands, fp32 accumulation,
+// fp32 out); returns 0, or non-zero with a message in err.  tune: time the top
+// candidate algorithms (waits for the stream) and record the fastest for this
+// shape.
+int block_gemm(int64_t rows, int64_t n, int64_t k, const void* act, const void* w, float* out, void* ws,
                size_t ws_bytes, hipStream_t st, char* err, size_t errlen, bool tune = false);
 
 hipError_t launch_rope_qknorm(int d, int out_dtype, const RopeQkArgs& a, hipStream_t st);

@@ -309,7 +309,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     for (int ks = 0; ks < C::KS; ++ks) {
       u32x4 wv = {0, 0, 0, 0};
       if (valid) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-      unpack_bf16x8(wv, x[ks]);
+      unpack_16x8(wv, x[ks], a.in_f16);
     }
     float ss = 0.f;
 #pragma unroll
@@ -646,7 +646,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(ost + cl * OROW + d0);
       const f32x4 v1 = *reinterpret_cast<const f32x4*>(ost + cl * OROW + d0 + 4);
       float g[8];
-      unpack_bf16x8(gw, g);
+      unpack_16x8(gw, g, a.in_f16);
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {

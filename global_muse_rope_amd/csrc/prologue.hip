@@ -308,8 +308,8 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
   float lo[RUN], hi[RUN];
 #pragma unroll
   for (int c = 0; c < RUN / 8; ++c) {
-    unpack_bf16x8(kw[0][c], lo + c * 8);
-    unpack_bf16x8(kw[1][c], hi + c * 8);
+    unpack_16x8(kw[0][c], lo + c * 8, a.k_f16);
+    unpack_16x8(kw[1][c], hi + c * 8, a.k_f16);
   }
   float ss = 0.f;
 #pragma unroll

@@ -271,8 +271,12 @@ int32_t muse_attn_decode_noalloc(const muse_attn_params* params, int32_t B,
  *   f   = a / sqrt(mean(a^2) + 1e-8), times (1 + post_norm) with a plain add
  *   out = x + f (residual_gate NULL), or alpha * x + beta * f with
  *         beta = sigmoid(g / T), alpha = sqrt(max(sigmoid(-g / T) (1 + beta), 1e-3))
- * Norm gains are formed and applied in fp32; every intermediate tensor (h,
- * the projections, o, a) is bf16; the GEMMs accumulate in fp32. */
+ * Norm gains are formed and applied in fp32.  h enters the projection GEMM
+ * as a pair of bf16 rows (h_hi = bf16(h), h_lo = bf16(h - h_hi): about 16
+ * bits); the GEMMs take bf16 operands and accumulate and write fp32; the
+ * layer receives q, k and the gate in fp16 and v in bf16 (the type of its
+ * value product), and returns o in bf16; o_proj's output stays fp32 into the
+ * post-norm and residual; the result is rounded once to bf16. */
 typedef struct muse_block_weights {
   int32_t hidden;                  /* model width: 8192 (Spark) or 6656 (Glimmer); a multiple of 8, <= 8192 */
   const void* in_norm;             /* [hidden] bf16: input_layernorm weight w (gain 1 + w) */

@@ -2,15 +2,21 @@
 projections through hipBLASLt, the layer, o_proj, post-norm and residual)
 against the fp64 block oracle, through the C ABI.
 
-Tolerance, derived from the arithmetic: the device rounds the q/k/v/gate
-projections to bf16 (relative error up to 2^-9 per element) before the
-layer, and the weightless QK-norm turns that into a logit error of about
-s / sqrt(D) * sqrt(2 D / 3) * 2^-9 (standard deviation 0.009 for Spark, 0.006
-for Glimmer), i.e. about 1 % in each softmax weight; normed output, gate and
-o_proj carry it to an O(1) branch with a per-element standard deviation near
-0.01, and the largest of 10^5-10^6 outputs lies near 5 sigma.  The other
-roundings (h, o, the o_proj output, the stored result) add a few 2^-9.
-BLOCK_TOL = 6e-2 bounds the max-abs error over a call.
+The bar is the layer's, TOL = 2e-2 max-abs, on the error beyond the block
+output's own bf16 quantum.  The block returns the residual stream, whose
+values reach 5-6 in magnitude; there one bf16 unit in the last place is
+2^-5 = 0.031, so the correctly rounded oracle value itself sits up to 0.016
+from the fp64 result.  Each output y is therefore held to
+|y - ref| <= TOL + ulp_bf16(y) / 2, i.e. within TOL before its final
+rounding (equivalently, max-abs 2e-2 on every output below magnitude 1,
+where half an ulp is at most 2^-9).  On the device every intermediate
+keeps at least fp16 precision except v and o (bf16, the operand type of the
+layer's value product and of o_proj): h goes into the projection GEMM as a
+bf16 hi/lo pair, the GEMMs accumulate and write fp32, q, k and the gate
+reach the layer in fp16, and o_proj's output stays fp32.  An fp64 model of
+exactly those roundings sits 0.6-1.2e-2 beyond half an ulp of the oracle on
+these shapes; storing h, the projections and o_proj's output in bf16 put it
+at 3.4-4.2e-2.
 """
 import numpy as np
 import pytest
@@ -20,11 +26,17 @@ import global_muse_rope_amd as ma
 import synth
 from oracle import block as OB
 from synth.workloads import Layer, GLIMMER_SCALE, SPARK_SCALE
-from gpu_helpers import to_dev, max_err
+from gpu_helpers import TOL, to_dev, max_err
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-BLOCK_TOL = 6e-2
+
+
+def beyond_half_ulp(y, ref):
+    """max over outputs of |y - ref| - ulp_bf16(y) / 2 (y holds bf16 values)."""
+    y = np.asarray(y, dtype=np.float64)
+    half_ulp = np.spacing(np.abs(y).astype(np.float32)).astype(np.float64) * 65536.0 / 2
+    return float(np.max(np.abs(y - ref) - half_ulp))
 
 
 def _f(bits):
@@ -71,12 +83,14 @@ def test_block_prefill_parity(case):
     y = ma.attention_block_prefill(ma.LayerParams.from_layer(layer), bw, to_dev(xb))
     torch.cuda.synchronize()
     y = y.float().cpu().numpy()
-    worst = 0.0
+    worst, plain = -1.0, 0.0
     for b in range(B):
         ref = OB.attention_block(_f(xb)[b], W, layer)
-        worst = max(worst, max_err(y[b], ref))
-    print(f"block {layer} hidden={hidden} B={B} T={T} max_abs_err={worst:.3e}", flush=True)
-    assert worst <= BLOCK_TOL
+        worst = max(worst, beyond_half_ulp(y[b], ref))
+        plain = max(plain, max_err(y[b], ref))
+    print(f"block {layer} hidden={hidden} B={B} T={T} beyond half an ulp {worst:.3e} (max_abs_err {plain:.3e})",
+          flush=True)
+    assert worst <= TOL
 
 
 def test_block_prefill_fullsize_spark_sampled():
@@ -95,9 +109,11 @@ def test_block_prefill_fullsize_spark_sampled():
     rows = np.array([0, 1, 2, 63, 64, 127, 128, 200, 255])
     xh = x[0, :256].float().cpu().numpy().astype(np.float64)
     ref = OB.attention_block(xh, W, layer, rows=rows)
-    err = max_err(y[0, rows].float().cpu().numpy(), ref)
-    print(f"block full size spark: rows {rows.tolist()} max_abs_err={err:.3e}", flush=True)
-    assert err <= BLOCK_TOL
+    yr = y[0, rows].float().cpu().numpy()
+    err = beyond_half_ulp(yr, ref)
+    print(f"block full size spark: rows {rows.tolist()} beyond half an ulp {err:.3e} "
+          f"(max_abs_err {max_err(yr, ref):.3e})", flush=True)
+    assert err <= TOL
 
 
 DEC_BLOCK_CASES = [
@@ -130,18 +146,20 @@ def test_block_decode_parity(case, use_fp8):
     y = ma.attention_block_decode(lp, wb, to_dev(xb), torch.from_numpy(lens).to(DEV), int(lens.max()), cache)
     torch.cuda.synchronize()
     y = y.float().cpu().numpy()
-    worst = 0.0
+    worst, plain = -1.0, 0.0
     for b in range(B):
         L = int(lens[b])
         ref = OB.attention_block_decode(_f(xb)[b], W, layer, hk[b, :L - 1].astype(np.float64),
                                         hv[b, :L - 1].astype(np.float64), 0, L)
-        worst = max(worst, max_err(y[b], ref))
-    print(f"block decode {kind} fp8={use_fp8} {layer} hidden={hidden} max_abs_err={worst:.3e}", flush=True)
-    assert worst <= BLOCK_TOL
+        worst = max(worst, beyond_half_ulp(y[b], ref))
+        plain = max(plain, max_err(y[b], ref))
+    print(f"block decode {kind} fp8={use_fp8} {layer} hidden={hidden} beyond half an ulp {worst:.3e} "
+          f"(max_abs_err {plain:.3e})", flush=True)
+    assert worst <= TOL
     if use_fp8:
         return
-    # the new value row landed in the cache (bf16 projection of the normed input, so compare with the
-    # oracle's projection within the projection's bf16 rounding)
+    # the new value row landed in the cache (the bf16 rounding of the fp32 projection of the normed
+    # input, so compare with the oracle's projection within half a bf16 ulp plus the GEMM's error)
     _, _, v_new, _ = OB.input_projections(_f(xb), W, layer)
     for b in range(B):
         p = int(lens[b]) - 1
@@ -150,7 +168,7 @@ def test_block_decode_parity(case, use_fp8):
         else:
             pg = int(cache.block_table[b, p // pt])
             vst = cache.v[pg, :, :, p % pt].float().cpu().numpy()
-        assert np.allclose(vst, v_new[b], rtol=2 ** -6, atol=2e-2)
+        assert np.allclose(vst, v_new[b], rtol=2 ** -8, atol=1e-3)
 
 
 def test_block_decode_fullsize_ring():
@@ -183,7 +201,7 @@ def test_block_decode_fullsize_ring():
     Wt = {"in_norm": host(w["in_norm"]), "w_qkvg": host(w["w_qkvg"]), "w_o": host(w["w_o"]),
           "post_norm": host(w["post_norm"]), "residual_gate": host(w["residual_gate"])}
     xh = x.double().cpu().numpy()
-    worst = 0.0
+    worst, plain = -1.0, 0.0
     for b in range(B):
         Lb = int(s["lengths"][b])
         p = Lb - 1
@@ -191,6 +209,8 @@ def test_block_decode_fullsize_ring():
         kh = np.stack([sd.cache_values_host(cfg.seed, b, h, L.hkv, "k", lo, p, L.d) for h in range(L.hkv)], axis=1)
         vh = np.stack([sd.cache_values_host(cfg.seed, b, h, L.hkv, "v", lo, p, L.d) for h in range(L.hkv)], axis=1)
         ref = OB.attention_block_decode(xh[b], Wt, L, kh, vh, lo, Lb)
-        worst = max(worst, max_err(y[b], ref))
-    print(f"{cfg.name} through the block: {B} sequences, max_abs_err={worst:.3e}", flush=True)
-    assert worst <= BLOCK_TOL
+        worst = max(worst, beyond_half_ulp(y[b], ref))
+        plain = max(plain, max_err(y[b], ref))
+    print(f"{cfg.name} through the block: {B} sequences, beyond half an ulp {worst:.3e} (max_abs_err {plain:.3e})",
+          flush=True)
+    assert worst <= TOL
