@@ -320,28 +320,47 @@ def _threads():
         return 1
 
 
-def cpu_baseline(cfg, gpu_out, budget_s=15.0, row_limit=None, kv=None):
+def baseline_order(cfg, row_limit=None):
+    """Query rows the oracle baseline takes, in order: the window-edge rows,
+    then a seeded permutation of the rows below row_limit."""
+    import numpy as np
+    lim = min(cfg.seq, row_limit or cfg.seq)
+    W = cfg.layer.window
+    rng = np.random.default_rng(1)
+    edge = [r for r in [0, 1, W - 2, W - 1, W, lim - 1] if 0 <= r < lim]
+    return np.concatenate([edge, rng.permutation(lim)]).astype(np.int64), lim
+
+
+BASELINE_ROWS = 8192   # GPU output rows kept on the host for the oracle baseline
+
+
+def keep_baseline_rows(cfg, out, row_limit=None):
+    """The GPU outputs of the first BASELINE_ROWS rows of the baseline order,
+    copied to the host right after the timed run (bf16, [n, Hq, D])."""
+    order, _ = baseline_order(cfg, row_limit)
+    return out[0, torch_index(order[:BASELINE_ROWS])].cpu()
+
+
+def cpu_baseline(cfg, gpu_rows, budget_s=15.0, row_limit=None, kv=None):
     """The fp64 oracle, as it stands, on a bounded sample of query rows of the
-    same workload: rows below row_limit (default: every row), in a seeded
-    order after the window-edge rows.  Returns its throughput in TFLOP/s, the
+    same workload (baseline_order).  Returns its throughput in TFLOP/s, the
     full-workload oracle time extrapolated per visible pair, and the
-    GPU/oracle max-abs difference on those rows.  kv: host (k, v) of tokens
-    0 .. row_limit - 1, if already regenerated."""
+    GPU/oracle max-abs difference on those rows (gpu_rows: the GPU's outputs
+    of the first rows of that order).  kv: host (k, v) of tokens 0 ..
+    row_limit - 1, if already regenerated."""
     import numpy as np
     import oracle
     from global_muse_rope_amd import accounting as acc
     from synth.device import host_tokens, host_rows
     L = cfg.layer
     T = cfg.seq
-    lim = min(T, row_limit or T)
+    order, lim = baseline_order(cfg, row_limit)
+    order = order[:BASELINE_ROWS]
     if kv is None:
         kv = (host_tokens(cfg, "k", 0, 0, lim), host_tokens(cfg, "v", 0, 0, lim))   # [lim, Hkv, D] float64
     k, v = kv
-    rng = np.random.default_rng(1)
-    edge = [r for r in [0, 1, L.window - 2, L.window - 1, L.window, lim - 1] if 0 <= r < lim]
-    order = np.concatenate([edge, rng.permutation(lim)]).astype(np.int64)
     t_start = time.perf_counter()
-    done, flops, pairs, worst = 0, 0, 0, 0.0
+    done, pairs, worst = 0, 0, 0.0
     elapsed = 0.0
     while done < len(order) and elapsed < budget_s:
         rows = order[done:done + 64]
@@ -353,8 +372,8 @@ def cpu_baseline(cfg, gpu_out, budget_s=15.0, row_limit=None, kv=None):
         for r in rows:
             lo, hi = oracle.visible_range(int(r), L.window)
             pairs += hi - lo + 1
-        if gpu_out is not None:
-            gy = gpu_out[0, torch_index(rows)].float().cpu().numpy()
+        if gpu_rows is not None:
+            gy = gpu_rows[done:done + len(rows)].float().numpy()
             worst = max(worst, float(np.max(np.abs(gy - y))))
         done += len(rows)
     flops = acc.flops_per_pair(L.hq, L.d) * pairs
@@ -666,12 +685,25 @@ def prefill_block(cfg, steps, warmup, events, torch, ma, cpu=True, row_limit=163
     log(f"  {r['tflops']:.1f} TFLOP/s step, kernel median {block['roofline']['kernel_ms_median']:.3f} ms "
         f"({block['roofline']['frac']:.3f} of MFMA peak)")
     if cpu:
-        log(f"cpu baseline {cfg.name}")
-        block["cpu_baseline"] = cpu_baseline(cfg, out, row_limit=row_limit, kv=kv)
-        log(f"  {block['cpu_baseline']['sample']}")
+        # the oracle runs after every GPU timing (its host threads would slow launch-bound steps)
+        rows = keep_baseline_rows(cfg, out, row_limit)
+        PENDING.append((block, "cpu_baseline",
+                        lambda: cpu_baseline(cfg, rows, row_limit=row_limit, kv=kv() if callable(kv) else kv),
+                        cfg.name))
     del x, out
     torch.cuda.empty_cache()
     return block
+
+
+PENDING = []   # (block, key, oracle baseline to run once the GPU timings are done, label)
+
+
+def run_pending():
+    for block, key, fn, label in PENDING:
+        log(f"cpu baseline (oracle) {label}")
+        block[key] = fn()
+        log(f"  {block[key]['sample']}")
+    PENDING.clear()
 
 
 def spark_prefill_block(events, torch, ma, cpu=True):
@@ -680,10 +712,16 @@ def spark_prefill_block(events, torch, ma, cpu=True):
     layers' FLOPs over their summed step time."""
     from synth import workloads as wl
     from synth.device import host_tokens
-    kv = None
-    if cpu:
-        lim = 16384
-        kv = (host_tokens(wl.SPARK_LOCAL, "k", 0, 0, lim), host_tokens(wl.SPARK_LOCAL, "v", 0, 0, lim))
+    # host k, v of the first 16384 tokens, regenerated once when the first
+    # baseline reads them (both layers draw the same seeded inputs)
+    kv_cache = {}
+
+    def kv():
+        if "kv" not in kv_cache:
+            lim = 16384
+            kv_cache["kv"] = (host_tokens(wl.SPARK_LOCAL, "k", 0, 0, lim), host_tokens(wl.SPARK_LOCAL, "v", 0, 0, lim))
+        return kv_cache["kv"]
+
     loc = prefill_block(wl.SPARK_LOCAL, 10, 3, events, torch, ma, cpu=cpu, kv=kv)
     glo = prefill_block(wl.SPARK_GLOBAL, 3, 2, events, torch, ma, cpu=cpu, kv=kv)
     flops = loc["roofline"]["flops_per_launch"] + glo["roofline"]["flops_per_launch"]
@@ -724,9 +762,9 @@ def decode_block(events, torch, ma, copy_gbs, cpu=True):
                                   "traffic": committed_traffic(f"decode_split_kernel_{name}", digest),
                                   "bytes_per_launch": r["kv_bytes"] + r["io_bytes"], "source_digest": digest}}
         if base and cpu:
-            log("cpu baseline (oracle) spark decode")
-            dec[name]["cpu_baseline"] = cpu_baseline_decode(dcfg, r["_out"], r["lengths"])
-            log(f"  {dec[name]['cpu_baseline']['sample']}")
+            y_host, lengths = r["_out"], r["lengths"]
+            PENDING.append((dec[name], "cpu_baseline",
+                            lambda d=dcfg, y=y_host, ln=lengths: cpu_baseline_decode(d, y, ln), name))
     return dec
 
 
@@ -812,9 +850,8 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     if not args.no_cpu:
-        log("cpu baseline (oracle, bounded sample)")
-        result["cpu_baseline"] = cpu_baseline(cfg, gpu_out)
-        log(f"  {result['cpu_baseline']['sample']}")
+        rows = keep_baseline_rows(cfg, gpu_out)
+        PENDING.append((result, "cpu_baseline", lambda: cpu_baseline(cfg, rows), cfg.name))
     del x, gpu_out
     torch.cuda.empty_cache()
 
@@ -866,6 +903,7 @@ def main():
                                     "cache_flushed": dcfg.layer.window > 0}
         result["attention_block_decode"] = block_dec
 
+    run_pending()
     print(json.dumps(result), flush=True)
 
 
