@@ -84,6 +84,7 @@ def source_digest(names):
 
 PREFILL_SOURCES = ["prefill.hip", "kernels.h", "common.h"]
 DECODE_SOURCES = ["decode.hip", "kernels.h", "common.h"]
+DRAFT_SOURCES = ["draft.hip", "draft.h", "kernels.h", "common.h"]
 
 
 def committed_traffic(name, digest):
@@ -100,21 +101,28 @@ def committed_traffic(name, digest):
 
 
 def timed_steps(fn, steps, warmup, events, torch, per_step=None):
-    """Run warmup + steps; returns (wall ms per step, mean attention-kernel ms).
-    per_step (a list) receives each step's attention-kernel ms."""
+    """Run warmup, then `steps` plain steps between two synchronizations (the
+    wall time), then `steps` more with the library's HIP events recorded
+    around its attention kernels on their stream (the kernel times: the
+    per-step event calls are kept out of the wall time).  Returns (wall ms
+    per step, mean attention-kernel ms); per_step (a list) receives each
+    step's attention-kernel ms."""
     import global_muse_rope_amd._capi as capi
     lib = capi.load()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    pairs = [(events.create(), events.create()) for _ in range(steps)]
     t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    pairs = [(events.create(), events.create()) for _ in range(steps)]
     for a, b in pairs:
         capi.check(lib.muse_profile_events(a, b))
         fn()
     capi.check(lib.muse_profile_events(None, None))
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3 / steps
     each = [events.elapsed_ms(a, b) for a, b in pairs]
     if per_step is not None:
         per_step.extend(each)
@@ -164,8 +172,8 @@ def chunk_case(cfg, steps, warmup, events, torch, ma, draft=False):
     else:
         cache = ma.KvCache.paged(s["kc"], s["vc"], s["block_table"], s["page_tokens"])
     out = torch.empty((cfg.batch, cfg.seq, L.hq, L.d), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(ma.prefill_chunk_workspace_size(lp, cfg.batch, cfg.seq, cfg.start), dtype=torch.uint8,
-                     device="cuda")
+    size_fn = ma.draft_block_workspace_size if draft else ma.prefill_chunk_workspace_size
+    ws = torch.empty(size_fn(lp, cfg.batch, cfg.seq, cfg.start), dtype=torch.uint8, device="cuda")
 
     fn = ma.draft_block if draft else ma.prefill_chunk
 
@@ -248,11 +256,11 @@ def block_decode_case(cfg, steps, warmup, events, torch, ma, flush=False):
     return res
 
 
-def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False, keep_out=False):
+def decode_case(cfg, steps, warmup, events, torch, ma, flush=False, fp8=False, keep_out=False, plain_fill=False):
     from synth.device import decode_device_setup
     from global_muse_rope_amd import accounting as acc
     L = cfg.layer
-    s = decode_device_setup(cfg, fp8=fp8)
+    s = decode_device_setup(cfg, fp8=fp8, plain_fill=plain_fill)
     ks, vs = s.get("k_scale"), s.get("v_scale")
     if s["kind"] == "ring":
         s["cache"] = ma.KvCache.ring(s["kc"], s["vc"], ks, vs)
@@ -448,14 +456,18 @@ def cpu_model():
 
 def pmc_pass(torch, ma, workload):
     """A short run for rocprofv3 counter passes: two steps of one workload
-    (prefill or decode; default: the benchmark workload) and one plain 1 GiB
-    device copy as the calibration of the byte counters."""
+    (prefill, decode or drafter block; default: the benchmark workload) and
+    one plain 1 GiB device copy as the calibration of the byte counters."""
     from synth import workloads as wl
-    cfgs = {c.name: c for c in wl.PREFILL + wl.DECODE}
+    cfgs = {c.name: c for c in wl.PREFILL + wl.DECODE + wl.DRAFT}
     fp8 = workload.endswith("_fp8")
     cfg = cfgs[workload[:-4] if fp8 else workload]
-    if cfg in wl.DECODE:
-        decode_case(cfg, 1, 1, HipEvents(), torch, ma, flush=cfg.layer.window > 0, fp8=fp8)
+    if cfg in wl.DRAFT:
+        chunk_case(cfg, 1, 1, HipEvents(), torch, ma, draft=True)
+    elif cfg in wl.DECODE:
+        # the byte counters do not depend on the cached values: one fill per pool (a few launches
+        # instead of the seeded streams' thousands)
+        decode_case(cfg, 1, 1, HipEvents(), torch, ma, flush=cfg.layer.window > 0, fp8=fp8, plain_fill=True)
     else:
         prefill_case(cfg, 1, 1, HipEvents(), torch, ma)
     a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
@@ -497,7 +509,7 @@ def traffic_summary(workload, kernel, fetch_csv, write_csv, commands):
                      "scale": round(factor, 4), "bytes_per_launch": kib * 1024 * factor}
         total += kib * 1024 * factor
     res["hbm_bytes_per_launch"] = total
-    srcs = PREFILL_SOURCES if "prefill" in kernel else DECODE_SOURCES
+    srcs = PREFILL_SOURCES if "prefill" in kernel else DRAFT_SOURCES if "draft" in kernel else DECODE_SOURCES
     res["source_digest"] = source_digest(srcs)
     path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.json")
     with open(path, "w") as f:
@@ -635,7 +647,8 @@ def only_case(name, steps, warmup, torch, ma):
                           "steps": steps, "warmup": warmup}), flush=True)
     elif cfg in wl.CHUNK or cfg in wl.DRAFT:
         r = chunk_case(cfg, steps, warmup, events, torch, ma, draft=cfg in wl.DRAFT)
-        print(json.dumps({"workload": name, "kernel": "prefill_kernel", "kernel_ms": round(r["kernel_ms"], 4),
+        kname = "draft_split_kernel + draft_combine_kernel" if cfg in wl.DRAFT else "prefill_kernel"
+        print(json.dumps({"workload": name, "kernel": kname, "kernel_ms": round(r["kernel_ms"], 4),
                           "kernel_TFLOP/s": round(r["kernel_tflops"], 2), "step_TFLOP/s": round(r["tflops"], 2),
                           "ms_per_step": round(r["ms_per_step"], 4), "steps": steps, "warmup": warmup}),
               flush=True)
@@ -744,7 +757,7 @@ def decode_block(events, torch, ma, copy_gbs, cpu=True):
                                     (wl.SPARK_DECODE_GLOBAL, 10, False, True)]:
         name = dcfg.name + ("_fp8" if fp8 else "")
         log(f"decode {name}")
-        base = dcfg.name == wl.SPARK_DECODE_GLOBAL.name and not fp8
+        base = not fp8   # the oracle baseline on both bf16 caches
         r = decode_case(dcfg, steps, 3, events, torch, ma, flush=flush, fp8=fp8, keep_out=base and cpu)
         med = _median(r["kernel_ms_each"])
         gbs = (r["kv_bytes"] + r["io_bytes"]) / (r["kernel_ms"] * 1e-3) / 1e9
@@ -876,14 +889,25 @@ def main():
                                  "kernel_ms": round(r["kernel_ms"], 4),
                                  "frac_of_mfma_peak": round(r["kernel_tflops"] / MFMA_PEAK_TFLOPS, 4)}
         result["prefill_chunk"] = chunks
+        from global_muse_rope_amd import accounting as acc
         draft = {}
+        ddigest = source_digest(DRAFT_SOURCES)
         for bcfg in wl.DRAFT:
             log(f"draft block {bcfg.name}")
-            r = chunk_case(bcfg, 20, 3, events, torch, ma, draft=True)
-            log(f"  {r['ms_per_step'] * 1e3:.1f} us per step, kernel {r['kernel_tflops']:.1f} TFLOP/s")
+            r = chunk_case(bcfg, 50, 5, events, torch, ma, draft=True)
+            L = bcfg.layer
+            nbytes = acc.draft_bytes(L.hq, L.hkv, L.d, bcfg.batch, bcfg.seq, bcfg.start, L.window)
+            gbs = nbytes / (r["kernel_ms"] * 1e-3) / 1e9
+            log(f"  {r['ms_per_step'] * 1e3:.1f} us per step, kernels {r['kernel_ms'] * 1e3:.1f} us, {gbs:.0f} GB/s")
             draft[bcfg.name] = {"us_per_step": round(r["ms_per_step"] * 1e3, 2),
                                 "kernel_us": round(r["kernel_ms"] * 1e3, 2),
-                                "tflops_step": round(r["tflops"], 2), "kernel_tflops": round(r["kernel_tflops"], 2)}
+                                "tflops_step": round(r["tflops"], 2), "kernel_tflops": round(r["kernel_tflops"], 2),
+                                "steps": 50, "warmup": 5,
+                                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                             "traffic": committed_traffic(f"draft_split_kernel_{bcfg.name}", ddigest),
+                                             "kernel": "draft_split_kernel + draft_combine_kernel",
+                                             "bytes_per_launch": nbytes, "source_digest": ddigest}}
         result["draft_block"] = draft
         blocks = {}
         for kcfg in wl.BLOCKS:

@@ -294,7 +294,8 @@ def _chunk_like(entry, layer, q, k, v, gate, start, max_start, cache, out, works
         if t.device != q.device:
             raise ValueError(f"{name} must be on the device of q ({q.device})")
     _check_cache(cache, q.device)
-    need = prefill_chunk_workspace_size(layer, B, T, max_start)
+    size_fn = draft_block_workspace_size if entry == "muse_attn_draft_block" else prefill_chunk_workspace_size
+    need = size_fn(layer, B, T, max_start)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check_workspace(workspace, need, q.device)

@@ -48,6 +48,16 @@ def kv_bytes_per_token(hkv: int, d: int, elem_bytes: int = 2) -> int:
     return 2 * hkv * d * elem_bytes
 
 
+def draft_bytes(hq: int, hkv: int, d: int, batch: int, seq: int, start: int, window: int,
+                elem_bytes: int = 2) -> int:
+    """HBM bytes a drafter's block moves once: the cached K and V of the
+    context its tokens see (positions max(0, start - W + 1) .. start - 1),
+    the block's q, k, v and gate read and its output written (bf16)."""
+    ctx = start if window == 0 else min(start, window - 1)
+    io = batch * seq * d * 2 * (hq + hkv + hkv + hq + hq)
+    return batch * ctx * kv_bytes_per_token(hkv, d, elem_bytes) + io
+
+
 def decode_visible_history(kv_len: int, window: int) -> int:
     """Cached entries one decode query reads (the new token excluded)."""
     if window == 0:

@@ -15,7 +15,7 @@ SRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmuse_attn.so")
-SOURCES = ["api.hip", "prologue.hip", "prefill.hip", "decode.hip", "block.hip"]
+SOURCES = ["api.hip", "prologue.hip", "prefill.hip", "decode.hip", "block.hip", "draft.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -7,6 +7,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "draft.h"
 #include "kernels.h"
 
 using namespace muse;
@@ -680,6 +681,93 @@ int32_t chunk_call(const muse_attn_params* params, int32_t B, int32_t T, const v
   if (e != hipSuccess) return fail(MUSE_ERR_HIP, "chunk append launch: %s", hipGetErrorString(e));
   return ok();
 }
+// The drafter's block as a few-token decode (blocks with T <= 64 and
+// T * G <= 128 columns per KV head): a split pass over each sequence's
+// cached context that also forms the queries and the block's own-key term,
+// and a combine of the partials with the epilogue.  The cache is read as
+// stored, once per 64 columns.  Workspace: one partial row of D + 4 floats
+// per (sequence, KV head, column group, split workgroup, column).
+size_t draft_ws(const muse_attn_params* p, int32_t B, int32_t T, int32_t max_start) {
+  const int D = p->head_dim, Hq = p->num_q_heads, Hkv = p->num_kv_heads;
+  const DraftPlan pl = draft_plan(B, Hkv, Hq / Hkv, T, p->sliding_window, max_start);
+  return align256(static_cast<size_t>(B) * Hkv * pl.n_cgroups * pl.n_wg * kDraftGroupCols * (D + 4) * 4);
+}
+
+int32_t draft_call(const muse_attn_params* params, int32_t B, int32_t T, const void* q, const void* k,
+                   const void* v, const void* gate, const int64_t* strides, const int32_t* start, int32_t max_start,
+                   const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (B < 0 || T < 0) return fail(MUSE_ERR_INVALID_ARG, "B and T must be >= 0");
+  if (max_start < 0) return fail(MUSE_ERR_INVALID_ARG, "max_start must be >= 0");
+  if (static_cast<int64_t>(max_start) + T > 0x7fffffffLL)
+    return fail(MUSE_ERR_UNSUPPORTED, "max_start + T exceeds the 32-bit position range");
+  int32_t rc = check_cache(params, B, std::max(1, max_start), cache);
+  if (rc) return rc;
+  if (B == 0 || T == 0) return ok();
+  if (!q || !k || !v || !gate || !out || !start) return fail(MUSE_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(gate) || !aligned16(out))
+    return fail(MUSE_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const int D = params->head_dim, Hq = params->num_q_heads, Hkv = params->num_kv_heads;
+  int64_t s[10];
+  rc = layer_strides(params, T, strides, s);
+  if (rc) return rc;
+  if (!workspace || !aligned16(workspace)) return fail(MUSE_ERR_WORKSPACE, "workspace missing or misaligned");
+  const size_t need = draft_ws(params, B, T, max_start);
+  if (ws_bytes < need) return fail(MUSE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, need);
+  const DraftPlan pl = draft_plan(B, Hkv, Hq / Hkv, T, params->sliding_window, max_start);
+  if (static_cast<int64_t>(B) * Hkv * pl.n_cgroups * pl.n_wg > 0x7fffffffLL ||
+      static_cast<int64_t>(B) * T * ((Hq + 3) / 4) > 0x7fffffffLL)
+    return fail(MUSE_ERR_UNSUPPORTED, "problem too large for one launch");
+  rc = check_device();
+  if (rc) return rc;
+  DraftArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.gate = static_cast<const uint16_t*>(gate);
+  a.q_sb = s[0];
+  a.q_st = s[1];
+  a.k_sb = s[2];
+  a.k_st = s[3];
+  a.v_sb = s[4];
+  a.v_st = s[5];
+  a.g_sb = s[6];
+  a.g_st = s[7];
+  a.o_sb = s[8];
+  a.o_st = s[9];
+  a.out = static_cast<uint16_t*>(out);
+  a.start = start;
+  a.max_start = max_start;
+  a.B = B;
+  a.T = T;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.W = params->sliding_window;
+  a.qscale = q_logit_scale(params);
+  a.qk_eps = params->qk_norm_eps;
+  a.out_eps = params->out_norm_eps;
+  a.out_norm = params->out_norm;
+  a.log2_theta = log2_theta(params);
+  a.use_rope = params->rope_theta > 0.f ? 1 : 0;
+  a.cache = cache_view(cache);
+  a.chunk_tokens = pl.chunk_tokens;
+  a.n_cgroups = pl.n_cgroups;
+  a.n_wg = pl.n_wg;
+  a.part = static_cast<float*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (g_prof_start) {
+    e = hipEventRecord(g_prof_start, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  }
+  e = launch_draft(D, a, st);
+  if (e != hipSuccess) return fail(MUSE_ERR_HIP, "draft launch: %s", hipGetErrorString(e));
+  if (g_prof_stop) {
+    e = hipEventRecord(g_prof_stop, st);
+    if (e != hipSuccess) return fail(MUSE_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
 int32_t decode_call(const muse_attn_params* params, int32_t B, const void* q_new, int64_t q_sb, const void* k_new,
                     const void* v_new, int64_t kv_sb, const void* gate, int64_t g_sb, const int32_t* kv_len,
                     int32_t max_kv_len, const muse_kv_cache* cache, void* out, void* workspace, size_t ws_bytes,
@@ -698,6 +786,8 @@ int32_t muse_attn_prefill_chunk(const muse_attn_params* params, int32_t B, int32
 
 size_t muse_attn_draft_block_workspace_size(const muse_attn_params* params, int32_t B, int32_t T,
                                             int32_t max_start) {
+  if (check_params(params) || B < 0 || T < 0 || max_start < 0) return 0;
+  if (draft_split_fits(T, params->num_q_heads / params->num_kv_heads)) return draft_ws(params, B, T, max_start);
   return muse_attn_prefill_chunk_workspace_size(params, B, T, max_start);
 }
 
@@ -705,6 +795,11 @@ int32_t muse_attn_draft_block(const muse_attn_params* params, int32_t B, int32_t
                               const void* v, const void* gate, const int64_t* strides, const int32_t* start,
                               int32_t max_start, const muse_kv_cache* cache, void* out, void* workspace,
                               size_t ws_bytes, void* stream) {
+  const int32_t rc = check_params(params);
+  if (rc) return rc;
+  if (draft_split_fits(T, params->num_q_heads / params->num_kv_heads))
+    return draft_call(params, B, T, q, k, v, gate, strides, start, max_start, cache, out, workspace, ws_bytes,
+                      stream);
   return chunk_call(params, B, T, q, k, v, gate, strides, start, max_start, cache, out, workspace, ws_bytes, stream,
                     true);
 }

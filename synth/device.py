@@ -126,13 +126,16 @@ def new_token_host(cfg):
     return out
 
 
-def decode_device_setup(cfg, device="cuda", lengths=None, fp8=False):
+def decode_device_setup(cfg, device="cuda", lengths=None, fp8=False, plain_fill=False):
     """Ring (window > 0) or paged (global) cache filled for every sequence's
     history, the new-token tensors and kv_len.  Returns a dict of tensors:
     q, k, v, g, kv_len (int32), lengths (numpy), max_len, and the cache
     pieces kind, kc, vc, block_table, page_tokens; with ``fp8`` the pools
     hold E4M3 codes and the dict adds k_scale, v_scale (device) and
-    scales_host (numpy k, v) and table_host (paged)."""
+    scales_host (numpy k, v) and table_host (paged).  ``plain_fill`` fills
+    each pool with one call of torch's own generator instead of the seeded
+    per-sequence streams: the same shapes, lengths and page table, for runs
+    whose figures do not depend on the cached values (byte counters)."""
     import torch
     L = cfg.layer
     d, hkv, B = L.d, L.hkv, cfg.batch
@@ -144,6 +147,11 @@ def decode_device_setup(cfg, device="cuda", lengths=None, fp8=False):
     res["lengths"] = lengths
     res["max_len"] = max_len
     edt = torch.uint8 if fp8 else torch.bfloat16
+
+    def plain(t):
+        if fp8:
+            return t.random_(0, 0x78)   # finite positive E4M3 codes
+        return t.normal_()
 
     def values(b, h, which, p0, p1):
         if fp8:
@@ -160,7 +168,10 @@ def decode_device_setup(cfg, device="cuda", lengths=None, fp8=False):
         W = L.window
         kc = torch.zeros((B, hkv, W, d), dtype=edt, device=device)
         vc = torch.zeros((B, hkv, d, W), dtype=edt, device=device)
-        for b in range(B):
+        if plain_fill:
+            plain(kc)
+            plain(vc)
+        for b in range(B if not plain_fill else 0):
             n = int(lengths[b])
             p0, p1 = max(0, n - 1 - W), n - 1
             if p1 <= p0:
@@ -185,7 +196,10 @@ def decode_device_setup(cfg, device="cuda", lengths=None, fp8=False):
     kc = torch.empty((n_pool, hkv, pt, d), dtype=edt, device=device)
     vc = torch.empty((n_pool, hkv, d, pt), dtype=edt, device=device)
     tdev = torch.from_numpy(table).to(device)
-    for b in range(B):
+    if plain_fill:
+        plain(kc)
+        plain(vc)
+    for b in range(B if not plain_fill else 0):
         n = int(lengths[b])
         idxp = tdev[b, :pages[b]].long()
         for h in range(hkv):

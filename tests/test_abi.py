@@ -290,6 +290,64 @@ def test_chunk_workspace_covers_key_pieces():
         assert big == _align(tiles(4096, hist)) + _align(rope(4096)) + _align(B * hkv * n_tiles * 4)
 
 
+def test_draft_split_workspace():
+    """Blocks of at most 64 tokens with at most 128 (token, head) columns per
+    KV head take the few-token decode path.  Its workspace is one fp32
+    partial row (O, max, sum, padded to D + 4) per (sequence, KV head, group
+    of 64 columns, split workgroup, column).  Each workgroup covers a chunk
+    of the context of a multiple of 64 positions; the last one also takes
+    the block's own keys.  Wider blocks keep the tile-image size."""
+    capi, lib = _lib()
+    wsf = lib.muse_attn_draft_block_workspace_size
+    p = params(capi, num_kv_heads=8)                 # Glimmer assistant: 32 / 8 heads x 128, window 2048
+    B, T, hkv, d = 16, 16, 8, 128
+    row = 64 * (d + 4) * 4                           # 64 columns of one (sequence, KV head, slot)
+    got = wsf(ctypes.byref(p), B, T, 131072)
+    assert got % (B * hkv * row) == 0
+    slots = got // (B * hkv * row)
+    # the context (at most W + 30 positions past the 32-aligned base) in chunks of at least 64
+    assert 1 <= slots <= -(-(2048 + 30) // 64)
+    # no context at all: one workgroup (the block's own keys)
+    assert wsf(ctypes.byref(p), B, T, 0) == B * hkv * row
+    # 128 columns per KV head: two groups
+    p8 = params(capi, num_kv_heads=4)
+    assert wsf(ctypes.byref(p8), B, 16, 0) == 2 * B * 4 * row
+    # a global layer's context grows the partials, never a tile image
+    pg = params(capi, num_kv_heads=8, sliding_window=0, rope_theta=0.0)
+    assert wsf(ctypes.byref(pg), B, T, 1 << 20) > wsf(ctypes.byref(pg), B, T, 1 << 16) > B * hkv * row
+    # 65 tokens, or 160 columns per KV head: the tile path
+    assert wsf(ctypes.byref(p), B, 65, 131072) == lib.muse_attn_prefill_chunk_workspace_size(ctypes.byref(p), B, 65,
+                                                                                               131072)
+    assert wsf(ctypes.byref(p), B, 40, 131072) == lib.muse_attn_prefill_chunk_workspace_size(ctypes.byref(p), B, 40,
+                                                                                               131072)
+
+
+def test_draft_split_argument_checks():
+    """The few-token path keeps the block call's checks."""
+    capi, lib = _lib()
+    p = params(capi, num_kv_heads=8)
+    f, wsf = lib.muse_attn_draft_block, lib.muse_attn_draft_block_workspace_size
+    ring = capi.MuseKvCache(capi.MUSE_KV_RING, 2048, FAKE, FAKE, None, 0, 0, 0)
+    need = wsf(ctypes.byref(p), 2, 16, 4096)
+
+    def call(B=2, T=16, max_start=4096, cache=ring, ws=need, start=FAKE, q=FAKE, pp=p):
+        return f(ctypes.byref(pp), B, T, q, FAKE, FAKE, FAKE, None, start, max_start,
+                 ctypes.byref(cache) if cache is not None else None, FAKE, FAKE, ws, None)
+
+    assert call(T=-1) == 1
+    assert call(max_start=-1) == 1
+    assert call(max_start=0x7FFFFFFF) == 2
+    assert call(cache=None) == 1
+    assert call(start=None) == 1
+    assert call(q=FAKE + 2) == 1
+    assert call(ws=need - 1) == 3
+    assert call(B=0) == 0 and call(T=0) == 0
+    assert call(cache=capi.MuseKvCache(capi.MUSE_KV_RING, 1024, FAKE, FAKE, None, 0, 0, 0)) == 1
+    pg = params(capi, num_kv_heads=8, sliding_window=0, rope_theta=0.0)
+    small = capi.MuseKvCache(capi.MUSE_KV_PAGED, 0, FAKE, FAKE, FAKE, 128, 32, 10000)  # 4096 positions
+    assert call(cache=small, pp=pg, max_start=4097, ws=wsf(ctypes.byref(pg), 2, 16, 4097)) == 1
+
+
 def test_block_prefill_argument_checks():
     capi, lib = _lib()
     p = params(capi, num_q_heads=128, num_kv_heads=16, head_dim=64, qk_scale=5.473, out_norm=1)

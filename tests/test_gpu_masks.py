@@ -10,7 +10,8 @@ bit and compared with the oracle's visible_range (causal chunk) or
 bidirectional_range (drafter block).  Every cache entry the call may not rely
 on (positions outside the window the header requires, a ring's stale slot,
 pages past the chunk start) holds NaN: reading one as a visible entry, or
-meeting one with a zero weight, would show up in the output."""
+meeting one with a zero weight, would show up in the output.  The workspace
+is filled with NaN bytes before each call for the same reason."""
 import numpy as np
 import pytest
 import torch
@@ -96,6 +97,9 @@ def run_marker_case(kind, layer, starts, T, draft, pt=32, fp8=False):
             else:
                 lo[b, t], hi[b, t] = oracle.visible_range(s + t, W)
     fn = ma.draft_block if draft else ma.prefill_chunk
+    size_fn = ma.draft_block_workspace_size if draft else ma.prefill_chunk_workspace_size
+    # the workspace holds NaN bytes: a read of anything the call did not write there shows up too
+    ws = torch.full((max(size_fn(lp, B, T, max_start), 1),), 0xFF, dtype=torch.uint8, device=DEV)
     for m0 in range(0, max_start + T, d):
         kc, vc, v = _build(kind, layer, starts, T, pt, fp8, m0, table, n_pages)
         kcd, vcd = _dev_bits(kc, fp8), _dev_bits(vc, fp8)
@@ -105,7 +109,8 @@ def run_marker_case(kind, layer, starts, T, draft, pt=32, fp8=False):
             cache = ma.KvCache.paged(kcd, vcd, table_dev, pt, ks.view(n_pages, hkv) if fp8 else None,
                                      vs.view(n_pages, hkv) if fp8 else None)
         vd = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(DEV)
-        y = fn(lp, q, k, vd, g, st, max_start, cache)
+        ws.fill_(0xFF)
+        y = fn(lp, q, k, vd, g, st, max_start, cache, workspace=ws)
         torch.cuda.synchronize()
         yf = y.float().cpu().numpy()                                 # [B, T, Hq, D]
         assert np.all(np.isfinite(yf)), f"non-finite output, markers from {m0}"
@@ -147,6 +152,11 @@ BLOCK_CASES = [
     ("paged", _lay(64, 0), [0, 1, 64, 65, 300], 16, 32),
     ("paged", _lay(64, 0, g=8), [0, 63, 130], 150, 16),                               # block wider than a tile
     ("paged", _lay(64, 256), [0, 256, 257, 400], 40, 32),
+    # blocks of at most 64 tokens and 128 (token, head) columns per KV head: the few-token decode path
+    ("ring", _lay(128, 2048, g=4), [0, 2047, 2048, 2049, 4096], 16, 0),
+    ("paged", _lay(64, 256), [0, 31, 256, 257, 400], 32, 32),
+    ("paged", _lay(128, 0, g=2), [0, 17, 128, 640, 3000], 64, 16),
+    ("ring", _lay(64, 64, g=8), [0, 1, 63, 64, 65, 200], 3, 0),
 ]
 
 
@@ -163,3 +173,9 @@ def test_visibility_exact_e4m3(kind, draft):
     NaN codes in every entry the call may not rely on."""
     layer = _lay(64, 256)
     run_marker_case(kind, layer, [0, 255, 256, 300], 40, draft=draft, pt=32, fp8=True)
+
+
+@pytest.mark.parametrize("kind", ["ring", "paged"])
+def test_draft_few_token_visibility_exact_e4m3(kind):
+    """E4M3 caches on the drafter's few-token path (24 tokens x 4 heads per KV head)."""
+    run_marker_case(kind, _lay(64, 256), [0, 255, 256, 300], 24, draft=True, pt=32, fp8=True)
