@@ -23,10 +23,12 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + INCLUDE,
 ]
-# Per-source flags.  The decode kernels keep their MFMA accumulators in
-# ordinary VGPRs: the accumulators are rescaled on a rarely taken branch,
-# and in accumulation registers every pass would copy them out and back.
-SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-source flags.  The decode and drafter kernels keep their MFMA
+# accumulators in ordinary VGPRs: the accumulators are rescaled on a rarely
+# taken branch, and in accumulation registers every pass would copy them out
+# and back.
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+                "draft.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

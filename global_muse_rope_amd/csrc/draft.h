@@ -16,7 +16,7 @@ constexpr int kDraftMaxCols = 128;
 constexpr int kDraftGroupCols = 64;
 // Context chunk of one split workgroup: a multiple of 64 positions (its
 // sub-chunks), at most kDraftChunkMax (its block table lives in LDS).
-constexpr int kDraftChunkMax = 4096;
+constexpr int kDraftChunkMax = 2048;
 // Split workgroups aimed for: two per CU (each holds two 32 KB images of
 // LDS and four waves).
 constexpr int64_t kDraftWorkgroups = 512;

@@ -49,6 +49,21 @@ __device__ __forceinline__ int kperm(int e) {
 }
 constexpr int kVS = 9;   // V dim stride in chunks (eight chunks of eight entries, plus one)
 
+// Head dim staged by V piece row r (r = piece / pieces per dim): the 16
+// lanes of one LDS write take dims d and d + 8 (bf16: 8 pieces per dim) or
+// d, d + 1, d + 8, d + 9 (E4M3: 4 pieces per dim, two chunks each), whose
+// chunks fall in 16 distinct bank groups at the 9-chunk dim stride.
+template <bool FP8>
+__device__ __forceinline__ int vdim(int r) {
+  if constexpr (FP8) {
+    const int g = r >> 2, k = r & 3;
+    return (g >> 2) * 16 + (g & 3) * 2 + (k & 1) + (k >> 1) * 8;
+  } else {
+    const int g = r >> 1;
+    return (g >> 3) * 16 + (r & 1) * 8 + (g & 7);
+  }
+}
+
 // Sixteen E4M3 codes (one 16-byte piece) to two chunks of eight bf16.
 __device__ __forceinline__ void e4m3x16_to_bf16(u32x4 w, u32x4& lo, u32x4& hi) {
   lo = e4m3x8_to_bf16x8(u32x2{w[0], w[1]});
@@ -79,9 +94,11 @@ __global__ __launch_bounds__(256) void draft_split_kernel(DraftArgs a) {
   constexpr int KPT = KP / 256, VPT = VP / 256;
   static_assert(KP % 256 == 0 && VP % 256 == 0, "pieces per thread");
   __shared__ u32x4 sm_img[2][IMG];
-  __shared__ int sm_bsi[kBlkMax];     // per 8-entry block: scale index (page * Hkv + hk, or bh), -1: absent
-  __shared__ int sm_brow[kBlkMax];    // per block: row of its first entry in the page or ring
-  __shared__ float2 sm_bsc[FP8 ? kBlkMax : 1];   // E4M3: (k, v) scales per block
+  // per 8-entry block of the chunk: element offsets of its first K row and
+  // of its first V entry at dim 0 (-1: absent page), and E4M3 (k, v) scales
+  __shared__ int64_t sm_koff[kBlkMax];
+  __shared__ int64_t sm_voff[kBlkMax];
+  __shared__ float2 sm_bsc[FP8 ? kBlkMax : 1];
 
   // chunk-major order: a short last chunk of every sequence is dispatched last
   const int npairs = a.B * a.Hkv * a.n_cgroups;
@@ -122,28 +139,31 @@ __global__ __launch_bounds__(256) void draft_split_kernel(DraftArgs a) {
   const int pt = cv.page_tokens;
   const int vstride = paged ? pt : cv.capacity;
 
-  // per 8-entry block of the chunk: where it lives, or -1 (absent page).
-  // Entries below the first visible position are masked where they are
-  // stored.  A block lies in one page (pages hold a multiple of 16
-  // positions, chunks start at multiples of 32) and, on a ring, in one run
-  // of slots; so does a 16-entry group at a multiple of 16.
-  const int nblk = (p1 - p0 + 7) / 8;
+  // The block table, filled to whole sub-chunks: blocks at or past p1 are
+  // marked absent, so staging loads need no range test.  Entries below the
+  // first visible position are masked where they are stored.  A block lies
+  // in one page (pages hold a multiple of 16 positions, chunks start at
+  // multiples of 32) and, on a ring, in one run of slots; so does a
+  // 16-entry group at a multiple of 16.
+  const int nblk = (p1 - p0 + kSub - 1) / kSub * (kSub / 8);
   for (int i = tid; i < nblk; i += 256) {
     const int pos = p0 + 8 * i;
     int si = -1, row = 0;
-    if (paged) {
-      const int pi = pos / pt;
-      const int page = pi < cv.max_pages ? cv.block_table[static_cast<int64_t>(b) * cv.max_pages + pi] : -1;
-      if (page >= 0 && page < cv.num_pages) {
-        si = page * a.Hkv + hk;
-        row = pos - pi * pt;
+    if (pos < p1) {
+      if (paged) {
+        const int pi = pos / pt;
+        const int page = pi < cv.max_pages ? cv.block_table[static_cast<int64_t>(b) * cv.max_pages + pi] : -1;
+        if (page >= 0 && page < cv.num_pages) {
+          si = page * a.Hkv + hk;
+          row = pos - pi * pt;
+        }
+      } else {
+        si = bh;
+        row = pos % cv.capacity;
       }
-    } else {
-      si = bh;
-      row = pos % cv.capacity;
     }
-    sm_bsi[i] = si;
-    sm_brow[i] = row;
+    sm_koff[i] = si >= 0 ? (static_cast<int64_t>(si) * vstride + row) * D : -1;
+    sm_voff[i] = si >= 0 ? static_cast<int64_t>(si) * D * vstride + row : -1;
     if constexpr (FP8) sm_bsc[i] = si >= 0 ? float2{cv.k_scale[si], cv.v_scale[si]} : float2{0.f, 0.f};
   }
 
@@ -223,27 +243,22 @@ __global__ __launch_bounds__(256) void draft_split_kernel(DraftArgs a) {
     for (int i = 0; i < KPT; ++i) {
       const int p = tid + 256 * i;
       const int row = p / KPR, c = p % KPR;
-      const int blk = min(blk0 + (row >> 3), kBlkMax - 1);
-      const int si = s0 + row < p1 ? sm_bsi[blk] : -1;
-      const int64_t off = si >= 0 ? (static_cast<int64_t>(si) * vstride + sm_brow[blk] + (row & 7)) * D : 0;
+      const int64_t off = max(sm_koff[blk0 + (row >> 3)], int64_t{0}) + (row & 7) * D;
       if constexpr (FP8)
         stg[i] = *reinterpret_cast<const u32x4*>(kc8 + off + 16 * c);
       else
         stg[i] = *reinterpret_cast<const u32x4*>(kc + off + 8 * c);
     }
+    // the V pieces of a thread share one block (c is tid % VPR)
+    const int cv0 = tid % VPR;
+    const int64_t vb = max(sm_voff[blk0 + cv0 * EPV / 8], int64_t{0});
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int p = tid + 256 * i;
-      const int d = p / VPR, c = p % VPR;
-      const int e0 = c * EPV;                 // first entry of the piece in the sub-chunk
-      const int blk = min(blk0 + (e0 >> 3), kBlkMax - 1);
-      const int si = s0 + e0 < p1 ? sm_bsi[blk] : -1;
-      const int64_t off =
-          si >= 0 ? static_cast<int64_t>(si) * D * vstride + sm_brow[blk] + static_cast<int64_t>(d) * vstride : 0;
+      const int d = vdim<FP8>((tid + 256 * i) / VPR);
       if constexpr (FP8)
-        stg[KPT + i] = *reinterpret_cast<const u32x4*>(vc8 + off);
+        stg[KPT + i] = *reinterpret_cast<const u32x4*>(vc8 + vb + static_cast<int64_t>(d) * vstride);
       else
-        stg[KPT + i] = *reinterpret_cast<const u32x4*>(vc + off);
+        stg[KPT + i] = *reinterpret_cast<const u32x4*>(vc + vb + static_cast<int64_t>(d) * vstride);
     }
   };
   // 16-bit halves of a V chunk kept for entries e0 .. e0 + 7 in [lo, hi)
@@ -256,15 +271,22 @@ __global__ __launch_bounds__(256) void draft_split_kernel(DraftArgs a) {
     }
     return mk;
   };
+  // every block of the sub-chunk present and every entry in [lo_all, p1):
+  // nothing to mask (the same answer in every lane)
+  auto all_in = [&](int s0) {
+    const bool pres = sm_koff[((s0 - p0) >> 3) + (lane & 7)] >= 0;
+    return s0 >= lo_all && s0 + kSub <= p1 && __builtin_amdgcn_ballot_w64(!pres) == 0;
+  };
   auto stage_store = [&](int buf, int s0) {
     u32x4* img = sm_img[buf];
     const int blk0 = (s0 - p0) >> 3;
+    const bool full = all_in(s0);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int p = tid + 256 * i;
       const int row = p / KPR, c = p % KPR;
       const int e = s0 + row;
-      const bool ok = e >= lo_all && e < p1 && sm_bsi[min(blk0 + (row >> 3), kBlkMax - 1)] >= 0;
+      const bool ok = full || (e >= lo_all && e < p1 && sm_koff[blk0 + (row >> 3)] >= 0);
       const int at = kperm(row) * KS;
       if constexpr (FP8) {
         u32x4 lo, hi;
@@ -275,21 +297,23 @@ __global__ __launch_bounds__(256) void draft_split_kernel(DraftArgs a) {
         img[at + c] = ok ? stg[i] : u32x4{0, 0, 0, 0};
       }
     }
+    const int c = tid % VPR;
+    const int e0 = c * EPV;
+    u32x4 m0 = {~0u, ~0u, ~0u, ~0u}, m1 = m0;
+    if (!full) {
+      const bool bok = sm_koff[blk0 + (e0 >> 3)] >= 0;
+      m0 = bok ? keep8(s0 + e0, lo_all, p1) : u32x4{0, 0, 0, 0};
+      m1 = bok ? keep8(s0 + e0 + 8, lo_all, p1) : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int p = tid + 256 * i;
-      const int d = p / VPR, c = p % VPR;
-      const int e0 = c * EPV;
-      const bool bok = sm_bsi[min(blk0 + (e0 >> 3), kBlkMax - 1)] >= 0;
+      const int d = vdim<FP8>((tid + 256 * i) / VPR);
       if constexpr (FP8) {
         u32x4 lo, hi;
         e4m3x16_to_bf16(stg[KPT + i], lo, hi);
-        const u32x4 m0 = bok ? keep8(s0 + e0, lo_all, p1) : u32x4{0, 0, 0, 0};
-        const u32x4 m1 = bok ? keep8(s0 + e0 + 8, lo_all, p1) : u32x4{0, 0, 0, 0};
         img[KCH + d * kVS + 2 * c] = lo & m0;
         img[KCH + d * kVS + 2 * c + 1] = hi & m1;
       } else {
-        const u32x4 m0 = bok ? keep8(s0 + e0, lo_all, p1) : u32x4{0, 0, 0, 0};
         img[KCH + d * kVS + c] = stg[KPT + i] & m0;
       }
     }
@@ -315,17 +339,14 @@ __global__ __launch_bounds__(256) void draft_split_kernel(DraftArgs a) {
     const u32x4* Klo = sm_img[1];
     const u32x4* V = sm_img[buf] + KCH;
     const int blk0 = (s0 - p0) >> 3;
-    bool inner = false;
-    if (!own) {
-      const bool bpres = sm_bsi[min(blk0 + (lane & 7), kBlkMax - 1)] >= 0;
-      inner = s0 >= lot_max && s0 + kSub <= p1 && __builtin_amdgcn_ballot_w64(!bpres) == 0;
-    }
+    // past every column's first visible position, all blocks present: no masks
+    const bool inner = !own && s0 >= lot_max && all_in(s0);
     const int ehi = own ? hi_own : p1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // logits of entries s0 + 32 h + 8 g4 + 4 kt + i, i < 4: block 4 h + g4
-      const int blk = min(blk0 + 4 * h + g4, kBlkMax - 1);
-      const bool bok = own || sm_bsi[blk] >= 0;
+      const int blk = own ? 0 : blk0 + 4 * h + g4;   // the own keys have no block table
+      const bool bok = own || sm_koff[blk] >= 0;
       float ks = 1.f, vs = 1.f;
       if constexpr (FP8) {
         if (!own) {
@@ -350,11 +371,16 @@ __global__ __launch_bounds__(256) void draft_split_kernel(DraftArgs a) {
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qhi[ds], acc, 0, 0, 0);
           }
         }
+        if (inner) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int e = s0 + 32 * h + 8 * g4 + 4 * kt + i;
-          const bool vis = cok && (inner || (bok && e >= lot && e < ehi));
-          sv[kt][i] = vis ? acc[i] * ks : kNeg;
+          for (int i = 0; i < 4; ++i) sv[kt][i] = cok ? acc[i] * ks : kNeg;
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = s0 + 32 * h + 8 * g4 + 4 * kt + i;
+            const bool vis = cok && bok && e >= lot && e < ehi;
+            sv[kt][i] = vis ? acc[i] * ks : kNeg;
+          }
         }
       }
       float tmax = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),

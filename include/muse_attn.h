@@ -202,11 +202,20 @@ size_t muse_attn_prefill_chunk_workspace_size(const muse_attn_params* params, in
  * directions), and on a window-0 layer always, keys existing up to the
  * block's last position.  The block is not written into the cache (a
  * drafter drops it before the next block).
- * Arguments as for muse_attn_prefill_chunk (including its bound on logits
- * over cached keys), except that the cache only needs positions below
- * start[b] (a PAGED cache: max_start <= max_pages_per_seq * page_tokens) and
- * is left unchanged; a start outside [0, max_start] gives zero output.
- * workspace: at least muse_attn_draft_block_workspace_size() bytes. */
+ * Arguments as for muse_attn_prefill_chunk, except that the cache only
+ * needs positions below start[b] (a PAGED cache: max_start <=
+ * max_pages_per_seq * page_tokens) and is left unchanged; a start outside
+ * [0, max_start] gives zero output.
+ * Blocks of at most 64 tokens whose T * (Hq / Hkv) query columns number at
+ * most 128 per KV head run as a few-token decode: the cache is read as
+ * stored through LDS once per 64 columns, the softmax keeps a running
+ * maximum (cached keys of any RMS give exact results; key elements need
+ * only be finite), and the block's own keys are normalized and rotated in
+ * fp32.  Wider blocks go through the prefill kernel as a chunk does,
+ * including its bound on logits over cached keys.
+ * workspace: at least muse_attn_draft_block_workspace_size() bytes (few-token
+ * blocks: fp32 partial sums per context chunk; wider ones: the chunk's tile
+ * images). */
 int32_t muse_attn_draft_block(const muse_attn_params* params, int32_t B, int32_t T,
                               const void* q, const void* k, const void* v, const void* gate,
                               const int64_t* strides, const int32_t* start, int32_t max_start,

@@ -312,3 +312,13 @@ def test_history_keys_above_unit_rms(kind, window, draft):
         run_block_case(kind, layer, starts, 16, page_tokens=32, key_gain=gain)
     else:
         run_chunk_case(kind, layer, starts, 100, page_tokens=32, key_gain=gain)
+
+
+@pytest.mark.parametrize("kind,window", [("ring", 256), ("paged", 0)])
+def test_few_token_block_keys_of_any_rms(kind, window):
+    """A drafter block of at most 64 tokens keeps a running maximum over the
+    cached keys, so keys of RMS 4 and 8 (logits bounded by about 250 and 500
+    log2 units, beyond the fixed shift of the tile path) still give the
+    oracle's max-subtracted softmax within the tolerance."""
+    layer = Layer(window=window, theta=10000.0 if window else 0.0, **SPARK_SMALL)
+    run_block_case(kind, layer, [300, 700, 1000], 16, page_tokens=32, key_gain=[4.0, 8.0, 1.0])

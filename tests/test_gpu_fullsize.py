@@ -396,7 +396,7 @@ def test_attention_block_fullsize_sampled():
     starts at its window's first position (or at 0)."""
     from oracle import block as OB
     from synth.device import block_device_setup
-    from test_gpu_block import BLOCK_TOL
+    from test_gpu_block import beyond_half_ulp
     cfg = wl.SPARK_BLOCK_LOCAL
     L = cfg.layer
     W = L.window
@@ -427,11 +427,12 @@ def test_attention_block_fullsize_sampled():
     worst = 0.0
     t = time.time()
     ref = OB.attention_block(x[:W], Wt, L, rows=np.array(early))
-    worst = max(worst, max_err(y[early], ref))
+    worst = max(worst, beyond_half_ulp(y[early], ref))
     for r in late:
         lo = r - W + 1
         ref = OB.attention_block(x[lo:r + 1], Wt, L, positions=np.arange(lo, r + 1), rows=np.array([W - 1]))
-        worst = max(worst, max_err(y[[r]], ref))
-    print(f"{cfg.name}: {len(early) + len(late)} rows x {cfg.hidden}, max_abs_err={worst:.3e} "
+        worst = max(worst, beyond_half_ulp(y[[r]], ref))
+    # the block tests' bar: TOL on the error beyond the output's own bf16 rounding
+    print(f"{cfg.name}: {len(early) + len(late)} rows x {cfg.hidden}, max error beyond half an ulp={worst:.3e} "
           f"(oracle {time.time() - t:.1f} s)", flush=True)
-    assert worst <= BLOCK_TOL
+    assert worst <= TOL
