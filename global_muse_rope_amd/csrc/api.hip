@@ -283,6 +283,9 @@ CacheView cache_view(const muse_kv_cache* c) {
 // fp32; the residual gate's coefficients; the GEMM scratch; then the
 // layer's own workspace.
 constexpr size_t kBlockGemmScratch = size_t(64) << 20;
+// A hidden size the block kernels take: a positive multiple of 8 up to
+// kBlockMaxHidden.
+bool block_hidden_ok(int hidden) { return hidden > 0 && hidden % 8 == 0 && hidden <= kBlockMaxHidden; }
 struct BlockWs {
   size_t h, proj, lay, o, a, coef, gemm, attn, total;
 };
@@ -1021,7 +1024,7 @@ extern "C" {
 
 size_t muse_attn_block_prefill_workspace_size(const muse_attn_params* params, const muse_block_weights* weights,
                                               int32_t B, int32_t T) {
-  if (check_params(params) || !weights || B < 0 || T < 0) return 0;
+  if (check_params(params) || !weights || !block_hidden_ok(weights->hidden) || B < 0 || T < 0) return 0;
   return block_ws_layout(params, weights, B, T).total;
 }
 
@@ -1031,7 +1034,7 @@ int32_t muse_attn_block_prefill(const muse_attn_params* params, const muse_block
   if (rc) return rc;
   if (!w) return fail(MUSE_ERR_INVALID_ARG, "weights is NULL");
   if (B < 0 || T < 0) return fail(MUSE_ERR_INVALID_ARG, "B and T must be >= 0");
-  if (w->hidden <= 0 || w->hidden % 8 != 0 || w->hidden > kBlockMaxHidden)
+  if (!block_hidden_ok(w->hidden))
     return fail(MUSE_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 8 up to %d", w->hidden,
                 kBlockMaxHidden);
   if (!w->in_norm || !w->w_qkvg || !w->w_o) return fail(MUSE_ERR_INVALID_ARG, "a weight pointer is NULL");
@@ -1072,7 +1075,7 @@ int32_t muse_attn_block_tune(const muse_attn_params* params, const muse_block_we
   if (rc) return rc;
   if (!w) return fail(MUSE_ERR_INVALID_ARG, "weights is NULL");
   if (rows <= 0) return fail(MUSE_ERR_INVALID_ARG, "rows must be > 0");
-  if (w->hidden <= 0 || w->hidden % 8 != 0 || w->hidden > kBlockMaxHidden)
+  if (!block_hidden_ok(w->hidden))
     return fail(MUSE_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 8 up to %d", w->hidden,
                 kBlockMaxHidden);
   if (!w->w_qkvg || !w->w_o) return fail(MUSE_ERR_INVALID_ARG, "a weight pointer is NULL");
@@ -1102,7 +1105,8 @@ int32_t muse_attn_block_tune(const muse_attn_params* params, const muse_block_we
 
 size_t muse_attn_block_decode_workspace_size(const muse_attn_params* params, const muse_block_weights* weights,
                                              int32_t B, int32_t max_kv_len, const muse_kv_cache* cache) {
-  if (check_params(params) || !weights || !cache || B < 0 || max_kv_len < 1) return 0;
+  if (check_params(params) || !weights || !block_hidden_ok(weights->hidden) || !cache || B < 0 || max_kv_len < 1)
+    return 0;
   return block_decode_ws_layout(params, weights, B, max_kv_len, cache).total;
 }
 
@@ -1114,7 +1118,7 @@ int32_t muse_attn_block_decode(const muse_attn_params* params, const muse_block_
   if (!w) return fail(MUSE_ERR_INVALID_ARG, "weights is NULL");
   if (B < 0) return fail(MUSE_ERR_INVALID_ARG, "B must be >= 0");
   if (max_kv_len < 1) return fail(MUSE_ERR_INVALID_ARG, "max_kv_len must be >= 1");
-  if (w->hidden <= 0 || w->hidden % 8 != 0 || w->hidden > kBlockMaxHidden)
+  if (!block_hidden_ok(w->hidden))
     return fail(MUSE_ERR_UNSUPPORTED, "hidden %d must be a positive multiple of 8 up to %d", w->hidden,
                 kBlockMaxHidden);
   if (!w->in_norm || !w->w_qkvg || !w->w_o) return fail(MUSE_ERR_INVALID_ARG, "a weight pointer is NULL");
