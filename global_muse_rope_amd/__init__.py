@@ -410,6 +410,30 @@ def block_prefill_workspace_size(layer: LayerParams, weights: BlockWeights, batc
     return int(_capi.load().muse_attn_block_prefill_workspace_size(ctypes.byref(p), ctypes.byref(w), batch, seq))
 
 
+def _check_block_out(out, x):
+    """out of a block call: a contiguous bf16 tensor of x's shape on x's device."""
+    torch = _torch()
+    if out.dtype != torch.bfloat16 or out.device != x.device or not out.is_contiguous() or out.shape != x.shape:
+        raise ValueError(f"out must be a contiguous bf16 tensor of shape {tuple(x.shape)} on {x.device}")
+
+
+def _check_block_weights(layer, w, device):
+    """The block's weights: bf16 in_norm [hidden], w_qkvg [(2 Hq + 2 Hkv) D, hidden],
+    w_o [hidden, Hq D] and post_norm [hidden], fp32 residual_gate [hidden], all
+    contiguous on the call's device."""
+    torch = _torch()
+    h, hq, hkv, d = w.hidden, layer.num_q_heads, layer.num_kv_heads, layer.head_dim
+    numel = {"in_norm": h, "w_qkvg": (2 * hq + 2 * hkv) * d * h, "w_o": h * hq * d, "post_norm": h,
+             "residual_gate": h}
+    for name, n in numel.items():
+        t = getattr(w, name)
+        if t is None:
+            continue
+        want = torch.float32 if name == "residual_gate" else torch.bfloat16
+        if t.dtype != want or t.device != device or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"weights.{name} must be a contiguous {want} tensor of {n} elements on {device}")
+
+
 def attention_block_prefill(layer: LayerParams, weights: BlockWeights, x, out=None, workspace=None):
     """The attention half of a decoder block on x [B, T, hidden] (bf16, contiguous):
     input norm, projections, the layer, o_proj, post-norm and residual.  Returns
@@ -423,9 +447,12 @@ def attention_block_prefill(layer: LayerParams, weights: BlockWeights, x, out=No
         raise ValueError("x width does not match the weights")
     if out is None:
         out = torch.empty_like(x)
+    _check_block_out(out, x)
+    _check_block_weights(layer, weights, x.device)
     need = block_prefill_workspace_size(layer, weights, B, T)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check_workspace(workspace, need, x.device)
     p = layer.c()
     w = weights.c()
     _capi.check(lib.muse_attn_block_prefill(ctypes.byref(p), ctypes.byref(w), B, T, x.data_ptr(), out.data_ptr(),
@@ -440,6 +467,7 @@ def attention_block_tune(layer: LayerParams, weights: BlockWeights, rows: int, w
     device.  Waits for the stream: call it outside timed or captured regions."""
     torch = _torch()
     lib = _capi.load()
+    _check_block_weights(layer, weights, weights.w_qkvg.device)
     need = block_prefill_workspace_size(layer, weights, 1, rows)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=weights.w_qkvg.device)
@@ -473,11 +501,17 @@ def attention_block_decode(layer: LayerParams, weights: BlockWeights, x, kv_len,
         raise ValueError("x width does not match the weights")
     if kv_len.dtype != torch.int32 or not kv_len.is_cuda or kv_len.numel() != B:
         raise ValueError("kv_len must be a device int32 tensor of B entries")
+    if kv_len.device != x.device:
+        raise ValueError(f"kv_len must be on the device of x ({x.device})")
     if out is None:
         out = torch.empty_like(x)
+    _check_block_out(out, x)
+    _check_block_weights(layer, weights, x.device)
+    _check_cache(cache, x.device)
     need = block_decode_workspace_size(layer, weights, B, max_kv_len, cache)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check_workspace(workspace, need, x.device)
     p = layer.c()
     w = weights.c()
     c = cache.c()

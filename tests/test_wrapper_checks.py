@@ -46,3 +46,32 @@ def test_entry_points_reject_host_tensors():
         ma.decode(layer, q[0], k[0], k[0], q[0], torch.ones(1, dtype=torch.int32), 4,
                   ma.KvCache.ring(torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16),
                                   torch.zeros((1, 2, 64, 64), dtype=torch.bfloat16)))
+
+
+def test_block_output_and_weight_checks():
+    """The block calls' out must match x (a wrong shape would be written past
+    its end) and every weight must hold the layer's element count in its
+    element type on the call's device."""
+    layer = ma.LayerParams(8, 2, 64, 0, 0.0, 1.0)
+    h = 256
+    x = torch.zeros((1, 4, h), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out must be"):
+        ma._check_block_out(torch.zeros((1, 3, h), dtype=torch.bfloat16), x)
+    with pytest.raises(ValueError, match="out must be"):
+        ma._check_block_out(torch.zeros((1, 4, h), dtype=torch.float32), x)
+    with pytest.raises(ValueError, match="out must be"):
+        ma._check_block_out(torch.zeros((1, h, 4), dtype=torch.bfloat16).transpose(1, 2), x)
+    ma._check_block_out(torch.zeros((1, 4, h), dtype=torch.bfloat16), x)
+    n = (2 * 8 + 2 * 2) * 64
+    good = dict(in_norm=torch.zeros(h, dtype=torch.bfloat16), w_qkvg=torch.zeros((n, h), dtype=torch.bfloat16),
+                w_o=torch.zeros((h, 8 * 64), dtype=torch.bfloat16), residual_gate=torch.zeros(h))
+    cpu = torch.device("cpu")
+    ma._check_block_weights(layer, ma.BlockWeights(**good), cpu)
+    with pytest.raises(ValueError, match="w_qkvg"):
+        ma._check_block_weights(layer, ma.BlockWeights(**dict(good, w_qkvg=torch.zeros((n - 64, h),
+                                                                                          dtype=torch.bfloat16))), cpu)
+    with pytest.raises(ValueError, match="residual_gate"):
+        ma._check_block_weights(layer, ma.BlockWeights(**dict(good, residual_gate=torch.zeros(
+            h, dtype=torch.bfloat16))), cpu)
+    with pytest.raises(ValueError, match="in_norm"):
+        ma._check_block_weights(layer, ma.BlockWeights(**good), CUDA0)
