@@ -162,6 +162,49 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     }
   };
 
+  // Raw query words (and their rotation's (cos, sin) rows) of one query
+  // block.  The persistent loop loads the next block's while the current
+  // block's epilogue runs, so their latency is off the next prologue.
+  u32x4 qraw[MB][C::KS];
+  float2 traw[MB][C::KS / 2][8];
+  int qraw_lx = -1;  // the block whose rows qraw holds (uniform)
+  // Every call writes all of qraw and traw (zeros where nothing is loaded),
+  // so their registers are free again during the tile loop.
+  auto load_q = [&](int lx_q, bool any) {
+    int bh_q = 0, qb_q = 0;
+    if (any) block_of(lx_q, bh_q, qb_q);
+    const bool blk = any && qb_q < a.n_qblocks;  // not a padding block
+    const int b_q = bh_q / a.Hkv;
+    const int hk_q = bh_q - b_q * a.Hkv;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r = (w * MB + mb) * 32 + l32;
+      const int t = qb_q * C::BQ + r / G;
+      const int hq = hk_q * G + (r % G);
+      const bool valid = blk && t < a.T;
+      const uint16_t* qp =
+          a.q + b_q * a.q_sb + static_cast<int64_t>(t) * a.q_st + static_cast<int64_t>(hq) * D + 8 * h2;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        qraw[mb][ks] = u32x4{0u, 0u, 0u, 0u};
+        if (valid) qraw[mb][ks] = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::KS / 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) traw[mb][ks][e] = float2{1.f, 0.f};
+      if (a.rope && valid) {
+        const float2* rt =
+            a.rope + ((a.rope_batched ? static_cast<int64_t>(b_q) * a.T : 0) + t) * (D / 2) + 8 * h2;
+#pragma unroll
+        for (int ks = 0; ks < C::KS / 2; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) traw[mb][ks][e] = rt[16 * ks + e];
+      }
+    }
+    qraw_lx = blk ? lx_q : -1;
+  };
+
   for (int lx = lx_first; lx < lx_end; lx += lx_step) {
   int bh, qb;
   block_of(lx, bh, qb);
@@ -295,22 +338,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   if (tile_lo + 1 <= tile_hi) gload(tile_lo + 1, 1);
   if (tile_lo + 2 <= tile_hi) gload(tile_lo + 2, 2);
 
-  // ---- queries: load, weightless RMS norm, scale, RoPE, fp16 operands ----
+  // ---- queries: load (unless prefetched), weightless RMS norm, scale,
+  // RoPE, fp16 operands ----
+  if (qraw_lx != lx) load_q(lx, true);
   half8 qf[MB][C::KS];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int r = (w * MB + mb) * 32 + l32;
-    const int t = tq[mb];
-    const int hq = hk * G + (r % G);
+    const bool valid = tq[mb] < a.T;
     float x[C::KS][8];
-    const bool valid = t < a.T;
-    const uint16_t* qp = a.q + b * a.q_sb + static_cast<int64_t>(t) * a.q_st + static_cast<int64_t>(hq) * D + 8 * h2;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      u32x4 wv = {0, 0, 0, 0};
-      if (valid) wv = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-      unpack_16x8(wv, x[ks], a.in_f16);
-    }
+    for (int ks = 0; ks < C::KS; ++ks) unpack_16x8(qraw[mb][ks], x[ks], a.in_f16);
     float ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
@@ -323,12 +360,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[ks][e] *= rs;
     if (a.rope && valid) {
-      const float2* rt = a.rope + ((a.rope_batched ? static_cast<int64_t>(b) * a.T : 0) + t) * (D / 2) + 8 * h2;
 #pragma unroll
       for (int ks = 0; ks < C::KS / 2; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float2 cs = rt[16 * ks + e];
+          const float2 cs = traw[mb][ks][e];
           const float x0 = x[ks][e], x1 = x[ks + C::KS / 2][e];
           x[ks][e] = x0 * cs.x - x1 * cs.y;
           x[ks + C::KS / 2][e] = x1 * cs.x + x0 * cs.y;
@@ -421,14 +457,19 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < QD; ++j) fq[j] = frag(hb, j);
   };
+  // do_qk / do_pv (std::true_type or std::false_type) select the logit and
+  // the P V products; the exponentials run only in a half-step that has
+  // both (the pipeline's fill has no P yet, its drain no logits to turn).
   auto half_step = [&](const Half& cur, const Half& nxt, f32x16* s_out, bf16x8 (*p_in)[2], f32x16* s_in,
-                       bf16x8 (*p_out)[2]) {
+                       bf16x8 (*p_out)[2], auto do_qk, auto do_pv) {
+    constexpr bool QK = decltype(do_qk)::value, PV = decltype(do_pv)::value, EXP = QK && PV;
     constexpr bool SHIFTED = HMODE == 2;
     constexpr int NE = 16;  // logits per lane per row block
-    // Head width 128 has exponentials on every other matrix item and packs
-    // them one item late; at 64 every item has some, and packing at once
+    // Head width 128 has one exponential per matrix item and packs each
+    // pair one item late; at 64 every item has two, and packing at once
     // measured faster.
     constexpr bool kLagPack = D == 128;
+    static_assert(!kLagPack || NE == NI, "one exponential per matrix item");
     float pend0[MB], pend1[MB];
     int pend_e = -1;
     auto pack_pair = [&](int mb, int e, float y0, float y1) {
@@ -442,8 +483,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       p_out[mb][e >> 3][(e & 7) + 1] = pr[1];
       lsum[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[mb], false);
     };
+    if constexpr (EXP) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(s_in[mb]));
+      for (int mb = 0; mb < MB; ++mb) asm volatile("" : "+v"(s_in[mb]));
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -454,11 +497,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       const u32x4 f = fq[j % QD];
       const int i = j >> 1;
       if ((j & 1) == 0) {
-        const half8 kf = __builtin_bit_cast(half8, f);
+        if constexpr (QK) {
+          const half8 kf = __builtin_bit_cast(half8, f);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          s_out[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[mb][i], s_out[mb], 0, 0, 0);
-      } else {
+          for (int mb = 0; mb < MB; ++mb)
+            s_out[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[mb][i], s_out[mb], 0, 0, 0);
+        }
+      } else if constexpr (PV) {
         const int st = i / C::DB, db = i % C::DB;
         const bf16x8 vf = __builtin_bit_cast(bf16x8, f);
 #pragma unroll
@@ -473,29 +518,38 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
         for (int mb = 0; mb < MB; ++mb) pack_pair(mb, pend_e, pend0[mb], pend1[mb]);
         pend_e = -1;
       }
-      // this item's slice of the exponentials (pairs, so each pair's row sum
-      // is one packed dot product)
-#pragma unroll
-      for (int e = (j * NE / NI) & ~1; e < (((j + 1) * NE / NI) & ~1); e += 2) {
+      // this item's slice of the exponentials.  The empty asm statements pin
+      // them to this slot: the one on the whole S_in at the top of the
+      // half-step stops the edge-tile mask from being folded into exp2
+      // (exp2(-inf) = 0) and the exponentials from being hoisted; the one on
+      // each output stops machine sinking from moving them into the next
+      // block, past the matrix-core work they hide under.
+      if constexpr (EXP && kLagPack) {
+        // head width 128: one exponential per matrix item (16 per 16
+        // items), so no item carries more vector work than the other wave's
+        // MFMA covers; each pair is packed (and its row sum taken as one
+        // packed dot product) on the item after its second exponential
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          // The empty asm statements pin the exponentials to this slot: the
-          // one on the whole S_in at the top of the half-step stops the
-          // edge-tile mask from being folded into exp2 (exp2(-inf) = 0) and
-          // the exponentials from being hoisted; the one on each output stops
-          // machine sinking from moving them into the next block, past the
-          // matrix-core work they hide under.
-          float x0 = __builtin_amdgcn_exp2f(s_in[mb][e]);
-          float x1 = __builtin_amdgcn_exp2f(s_in[mb][e + 1]);
-          if constexpr (kLagPack) {
-            asm volatile("" : "+v"(x0), "+v"(x1));
-            pend0[mb] = x0;
-            pend1[mb] = x1;
-          } else {
+          float x = __builtin_amdgcn_exp2f(s_in[mb][j]);
+          asm volatile("" : "+v"(x));
+          if (j & 1)
+            pend1[mb] = x;
+          else
+            pend0[mb] = x;
+        }
+        if (j & 1) pend_e = j - 1;
+      } else if constexpr (EXP) {
+        // head width 64: two exponentials per item, packed at once
+#pragma unroll
+        for (int e = (j * NE / NI) & ~1; e < (((j + 1) * NE / NI) & ~1); e += 2) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const float x0 = __builtin_amdgcn_exp2f(s_in[mb][e]);
+            const float x1 = __builtin_amdgcn_exp2f(s_in[mb][e + 1]);
             pack_pair(mb, e, x0, x1);
           }
         }
-        if constexpr (kLagPack) pend_e = e;
       }
     }
     if (pend_e >= 0) {
@@ -509,9 +563,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // probabilities on the vector ALUs, and accumulates P V of half k-2.  Per
   // tile the two half-steps swap the roles of the S and P registers, so no
   // copies are needed.  One loop body serves every tile (a single copy keeps
-  // register pressure low): before the first tile, the "previous" P is zero
-  // over valid V data; the final drain step recomputes logits of the last
-  // tile that are never used.
+  // register pressure low): in the first tile the "previous" P is zero over
+  // valid V data.  The fill before the loop computes only the first logits,
+  // the drain after it only the last P V.
   f32x16 sc[MB], sn[MB];          // logits: current half, next half
   bf16x8 pc[MB][2], pp[MB][2];    // probabilities: current half, previous half
 #pragma unroll
@@ -526,24 +580,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
-  // S(first tile, 0..31); the "previous" P is zero, so this PV adds nothing
-  // (its exponentials of zero logits are discarded with the row sums)
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sn[mb][e] = 0.f;
   // A wave whose columns all lie past the last query row (the short block of
   // a drafter) only copies its share of each tile and meets the barriers.
   // Only the SKIP instance tests for it: in the others the branch would cost
   // the common path about 2 % (register allocation and scheduling).
   const bool idle = SKIP && t0 + (w * MB * 32) / G >= a.T;
+  // fill: S(first tile, 0..31) only
   if (!idle) {
     const Half h0 = half_at(tile_lo, 0, tile_lo, 0);
     prime(h0);
-    half_step(h0, half_at(tile_lo, 1, tile_lo, 1), sc, pp, sn, pc);
+    half_step(h0, half_at(tile_lo, 1, tile_lo, 1), sc, pp, sn, pc, std::true_type{}, std::false_type{});
   }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) lsum[mb] = 0.f;
   for (int t = tile_lo; t <= tile_hi; ++t) {
     if (idle) {
       advance(t);
@@ -558,23 +605,20 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     const Half hn = half_at(tnext, 1, t, 1);   // half A of the next tile (or the drain)
     mask_logits(sc, masked, k0);
     // S(t, 32..63) and O += P(t-1, 32..63) V  ||  P(t, 0..31)
-    half_step(ha, hb, sn, pp, sc, pc);
+    half_step(ha, hb, sn, pp, sc, pc, std::true_type{}, std::true_type{});
     mask_logits(sn, masked, k0 + 32);
     // S(t+1, 0..31) and O += P(t, 0..31) V  ||  P(t, 32..63)
-    half_step(hb, hn, sc, pc, sn, pp);
+    half_step(hb, hn, sc, pc, sn, pp, std::true_type{}, std::true_type{});
     advance(t);
   }
-  // drain: O += P(last, 32..63) V; the logits and exponentials computed
-  // alongside are unused, and the row sums are restored
-  float lkeep[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) lkeep[mb] = lsum[mb];
+  // drain: O += P(last, 32..63) V only
   if (!idle) {
     const Half hd = half_at(tile_hi, 1, tile_hi, 1);
-    half_step(hd, hd, sn, pp, sc, pc);
+    half_step(hd, hd, sn, pp, sc, pc, std::false_type{}, std::true_type{});
   }
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) lsum[mb] = lkeep[mb];
+  // (only head width 128 runs persistent grids; at 64 the prefetch would
+  // only cost the zeroing of the registers)
+  if constexpr (D == 128) load_q(lx + lx_step, persistent && lx + lx_step < lx_end);
 
   // ---- epilogue: 1/sum, per-head output norm, then through LDS to row-major
   // order for the sigmoid gate and coalesced bf16 stores.  In the MFMA layout
@@ -584,6 +628,23 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // and stores 8 consecutive outputs, and a wave covers whole lines. ----
   constexpr int OROW = D + 4;                  // floats per staged column (padded)
   static_assert(NW * MB * 32 * OROW * 4 <= NBUF * TL::CHUNKS * 16, "staging fits the tile buffers");
+  constexpr int CPC = D / 8;                     // 8-value chunks per column
+  constexpr int NCH = MB * 32 * CPC;             // chunks per wave
+  static_assert(NCH % kWave == 0, "whole chunk rounds");
+  // Gate rows of the chunks this lane stores below, loaded before the
+  // staging so their latency overlaps it.
+  u32x4 gpre[NCH / kWave];
+#pragma unroll
+  for (int it = 0; it < NCH / kWave; ++it) {
+    const int k = it * kWave + lane;
+    const int cl = k / CPC, d0 = (k % CPC) * 8;
+    const int r = w * MB * 32 + cl;
+    const int t = t0 + r / G;
+    gpre[it] = u32x4{0u, 0u, 0u, 0u};
+    if (!split && t < a.T)
+      gpre[it] = *reinterpret_cast<const u32x4*>(a.gate + b * a.g_sb + static_cast<int64_t>(t) * a.g_st +
+                                                 static_cast<int64_t>(hk * G + (r % G)) * D + d0);
+  }
   __syncthreads();                              // every wave is done with the tiles
   float* ost = reinterpret_cast<float*>(&smem[0][0]) + w * (MB * 32 * OROW);
 #pragma unroll
@@ -623,9 +684,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // LDS accesses of one wave execute in order; the fence keeps the compiler
   // from reordering the reads below above the writes
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  constexpr int CPC = D / 8;                     // 8-value chunks per column
-  constexpr int NCH = MB * 32 * CPC;             // chunks per wave
-  static_assert(NCH % kWave == 0, "whole chunk rounds");
 #pragma unroll
   for (int it = 0; it < NCH / kWave; ++it) {
     const int k = it * kWave + lane;
@@ -641,8 +699,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<f32x4*>(po + 4) = v1;
     } else if (t < a.T) {
       const int hq = hk * G + (r % G);
-      const u32x4 gw = *reinterpret_cast<const u32x4*>(a.gate + b * a.g_sb + static_cast<int64_t>(t) * a.g_st +
-                                                       static_cast<int64_t>(hq) * D + d0);
+      const u32x4 gw = gpre[it];
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(ost + cl * OROW + d0);
       const f32x4 v1 = *reinterpret_cast<const f32x4*>(ost + cl * OROW + d0 + 4);
       float g[8];

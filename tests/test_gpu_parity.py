@@ -143,13 +143,16 @@ def test_prefill_batch_and_positions():
     check_prefill(layer, B, T, seed=3, positions=pos)
 
 
-def test_prefill_local_many_blocks_per_workgroup():
+@pytest.mark.parametrize("T", [6001, 5000])
+def test_prefill_local_many_blocks_per_workgroup(T):
     """A local layer with more query blocks than resident workgroups, so one
-    workgroup walks several blocks (and their padding) in turn; two
-    sequences, a ragged length and positions offset per sequence.  Rows are
-    sampled for the oracle (each row depends only on its own window)."""
+    workgroup walks several blocks in turn, loading each next block's queries
+    ahead; two sequences, a ragged length and positions offset per sequence.
+    At T = 5000 the 313 query blocks per head are padded to 320, so some of the
+    blocks a workgroup loads ahead are padding.  Rows are sampled for the
+    oracle (each row depends only on its own window)."""
     layer = Layer(hq=32, hkv=2, d=128, window=512, theta=10000.0, scale=GLIMMER_SCALE)
-    B, T = 2, 6001
+    B = 2
     pos = np.stack([np.arange(T), np.arange(T) + 70000]).astype(np.int32)
     bits = prefill_inputs_host(layer, B, T, seed=17)
     y = run_prefill(layer, bits, positions=pos)
