@@ -19,23 +19,26 @@ constexpr int64_t kPagedChunkTarget = 2048;
 // Prefill tile image: one 64-key tile of one (sequence, KV head), written by
 // kv_prep_kernel and copied verbatim into LDS by the attention kernel, in
 // 16-byte chunks:
-//   K part: 64 key rows of k_hat (fp16), D/8 data chunks + 1 pad chunk each;
-//   V part: D head-dim rows of V (bf16) over the 64 keys, 8 data chunks + 1 pad
-//           chunk each; inside each 16-key group the keys are stored in the
-//           order 0-3, 8-11, 4-7, 12-15 so that one 16-byte read gives the
-//           eight keys an MFMA lane consumes.
-// A row stride of 2^n + 1 chunks puts any 16 consecutive rows, read at the
-// same chunk, on 16 distinct 16-byte bank groups, and keeps every MFMA
-// fragment address an immediate offset from one per-lane base.
+//   K part: 64 key rows of k_hat (fp16), D/8 chunks each;
+//   V part: D head-dim rows of V (bf16) over the 64 keys, 8 chunks each;
+//           inside each 16-key group the keys are stored in the order 0-3,
+//           8-11, 4-7, 12-15 so that one 16-byte read gives the eight keys an
+//           MFMA lane consumes.
+// Both parts are chunk-major: chunk c of every row, then chunk c + 1.  Lanes
+// that read one chunk of consecutive rows then touch consecutive 16-byte
+// chunks (16 distinct bank groups per 16 lanes, with no pad chunks), and
+// every MFMA fragment address is an immediate offset from one per-lane base.
 // ---------------------------------------------------------------------------
 template <int D>
 struct TileLayout {
-  static constexpr int KROW = D / 8 + 1;
-  static constexpr int VROW = kKeyTile / 8 + 1;
-  static constexpr int KCHUNKS = kKeyTile * KROW;
-  static constexpr int VCHUNKS = D * VROW;
+  static constexpr int KCHUNKS = kKeyTile * (D / 8);
+  static constexpr int VCHUNKS = D * (kKeyTile / 8);
   static constexpr int CHUNKS = KCHUNKS + VCHUNKS;
   static_assert(CHUNKS % 64 == 0, "a tile is copied in whole 64-lane wave instructions");
+  // chunk index of chunk c (head dims 8c .. 8c + 7) of key row r
+  __host__ __device__ static constexpr int k(int r, int c) { return c * kKeyTile + r; }
+  // chunk index of chunk c (eight keys, in the order above) of head-dim row d
+  __host__ __device__ static constexpr int v(int d, int c) { return KCHUNKS + c * D + d; }
 };
 
 inline int tile_chunks(int d) { return d == 128 ? TileLayout<128>::CHUNKS : TileLayout<64>::CHUNKS; }

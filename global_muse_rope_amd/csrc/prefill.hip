@@ -100,7 +100,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   using C = PrefillCfg<D, G, NW, MB>;
   using TL = TileLayout<D>;
   constexpr int NBUF = 4;
-  __shared__ u32x4 smem[NBUF][TL::CHUNKS];
+  // four tile buffers; the epilogue stages its fp32 outputs (padded columns)
+  // in the same memory
+  constexpr int OROW = D + 4;  // floats per staged column
+  constexpr int STAGE_CHUNKS = NW * MB * 32 * OROW / 4;
+  constexpr int SMEM_CHUNKS = NBUF * TL::CHUNKS > STAGE_CHUNKS ? NBUF * TL::CHUNKS : STAGE_CHUNKS;
+  __shared__ u32x4 smem[SMEM_CHUNKS];
+  auto tile_buf = [&](int buf) -> u32x4* { return smem + buf * TL::CHUNKS; };
 
 
   const int tid = threadIdx.x;
@@ -330,7 +336,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     const u32x4* src = tsrc + static_cast<int64_t>(tile) * TL::CHUNKS;
 #pragma unroll
     for (int c = 0; c < TL::CHUNKS; c += C::THREADS)
-      if (c + w * 64 < TL::CHUNKS) dma16_to_lds(src + c + w * 64 + lane, &smem[buf][c + w * 64]);
+      if (c + w * 64 < TL::CHUNKS) dma16_to_lds(src + c + w * 64 + lane, tile_buf(buf) + c + w * 64);
   };
   // The first three tiles of the range start streaming into LDS before the
   // query prologue, so their latency overlaps the query loads.
@@ -434,23 +440,27 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   static_assert(NK == 2 * C::DB, "K and V items alternate one to one");
   constexpr int QD = D == 128 ? kFragQueueD128 : kFragQueueD64;
   static_assert(NI % QD == 0, "queue slots line up across half-steps");
-  const int k_lane = (l32 * TL::KROW + h2) * 16;              // bytes
-  const int v_lane = (TL::KCHUNKS + l32 * TL::VROW + h2) * 16;  // bytes
+  const int k_lane = TL::k(l32, h2) * 16;  // bytes: key row l32, chunk h2
+  const int v_lane = TL::v(l32, h2) * 16;  // bytes: head-dim row l32, chunk h2
   struct Half {
     const char* k;
     const char* v;
   };
   auto half_at = [&](int tile_q, int kb_q, int tile_v, int kb_v) -> Half {
     Half hb;
-    hb.k = reinterpret_cast<const char*>(&smem[(tile_q - tile_lo) % NBUF][0]) + k_lane + 32 * kb_q * TL::KROW * 16;
-    hb.v = reinterpret_cast<const char*>(&smem[(tile_v - tile_lo) % NBUF][0]) + v_lane + 4 * kb_v * 16;
+    // key rows 32 kb_q on; V chunks (8 keys each) 4 kb_v on
+    hb.k = reinterpret_cast<const char*>(tile_buf((tile_q - tile_lo) % NBUF)) + k_lane + TL::k(32 * kb_q, 0) * 16;
+    hb.v = reinterpret_cast<const char*>(tile_buf((tile_v - tile_lo) % NBUF)) + v_lane +
+           (TL::v(0, 4 * kb_v) - TL::v(0, 0)) * 16;
     return hb;
   };
   auto frag = [&](const Half& hb, int j) -> u32x4 {
     const int i = j >> 1;
-    if ((j & 1) == 0) return *reinterpret_cast<const u32x4*>(hb.k + 2 * i * 16);
+    // K item i: head dims 16 i .. 16 i + 15 (chunks 2 i, 2 i + 1)
+    if ((j & 1) == 0) return *reinterpret_cast<const u32x4*>(hb.k + TL::k(0, 2 * i) * 16);
+    // V item (st, db): head-dim rows 32 db on, keys 16 st on (chunks 2 st, 2 st + 1)
     const int st = i / C::DB, db = i % C::DB;
-    return *reinterpret_cast<const u32x4*>(hb.v + (32 * db * TL::VROW + 2 * st) * 16);
+    return *reinterpret_cast<const u32x4*>(hb.v + (TL::v(32 * db, 2 * st) - TL::v(0, 0)) * 16);
   };
   u32x4 fq[QD];
   auto prime = [&](const Half& hb) {
@@ -626,8 +636,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // stores would leave every 128-byte line written in 16-byte pieces by
   // different instructions; staged, each lane loads 8 consecutive gate values
   // and stores 8 consecutive outputs, and a wave covers whole lines. ----
-  constexpr int OROW = D + 4;                  // floats per staged column (padded)
-  static_assert(NW * MB * 32 * OROW * 4 <= NBUF * TL::CHUNKS * 16, "staging fits the tile buffers");
   constexpr int CPC = D / 8;                     // 8-value chunks per column
   constexpr int NCH = MB * 32 * CPC;             // chunks per wave
   static_assert(NCH % kWave == 0, "whole chunk rounds");
@@ -646,7 +654,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
                                                  static_cast<int64_t>(hk * G + (r % G)) * D + d0);
   }
   __syncthreads();                              // every wave is done with the tiles
-  float* ost = reinterpret_cast<float*>(&smem[0][0]) + w * (MB * 32 * OROW);
+  float* ost = reinterpret_cast<float*>(smem) + w * (MB * 32 * OROW);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     const float ltot = lsum[mb] + __shfl_xor(lsum[mb], 32, kWave);

@@ -131,9 +131,8 @@ __device__ __forceinline__ void kv_prep_history_tile(const KvPrepArgs& a, int b,
   constexpr int KC = D / 8;
   const int tid = threadIdx.x;
   const CacheView& cv = a.cache;
-  // keys: KC consecutive lanes carry the KC data chunks of one row (their
-  // sum of squares is a reduction over the group); the pad chunks are
-  // written separately
+  // keys: KC consecutive lanes carry the KC chunks of one row (their sum of
+  // squares is a reduction over the group)
   float mrow = 0.f;
   for (int j = tid; j < BK * KC; j += 256) {
     const int r = j / KC, c = j - r * KC;
@@ -157,16 +156,14 @@ __device__ __forceinline__ void kv_prep_history_tile(const KvPrepArgs& a, int b,
       for (int i = 0; i < 4; ++i) out[i] = pack_f16x2(f[2 * i], f[2 * i + 1]);
     }
     mrow = fmaxf(mrow, group_sum<KC>(s2) * (1.0f / D));
-    tdst[r * (KC + 1) + c] = out;
+    tdst[TL::k(r, c)] = out;
   }
-  for (int r = tid; r < BK; r += 256) tdst[r * (KC + 1) + KC] = u32x4{0, 0, 0, 0};
   // the tile's largest key mean square (every row is visible history)
   mrow = wave_max(mrow);
   if ((tid & 63) == 0) kss[tid >> 6] = mrow;
   __syncthreads();
   if (tid == 0) a.tile_ms[tile_index] = fmaxf(fmaxf(kss[0], kss[1]), fmaxf(kss[2], kss[3]));
   // values: item (d, g16) writes image chunks 2 g16 and 2 g16 + 1 of head-dim row d
-  u32x4* vdst = tdst + TL::KCHUNKS;
   const int vstride = cache_vstride(cv);
   for (int it = tid; it < D * (BK / 16); it += 256) {
     const int d = it / (BK / 16), g16 = it - d * (BK / 16);
@@ -195,10 +192,9 @@ __device__ __forceinline__ void kv_prep_history_tile(const KvPrepArgs& a, int b,
         y = *reinterpret_cast<const u32x4*>(src + 8);
       }
     }
-    vdst[d * TL::VROW + 2 * g16] = u32x4{x[0], x[1], y[0], y[1]};
-    vdst[d * TL::VROW + 2 * g16 + 1] = u32x4{x[2], x[3], y[2], y[3]};
+    tdst[TL::v(d, 2 * g16)] = u32x4{x[0], x[1], y[0], y[1]};
+    tdst[TL::v(d, 2 * g16 + 1)] = u32x4{x[2], x[3], y[2], y[3]};
   }
-  for (int d = tid; d < D; d += 256) vdst[d * TL::VROW + BK / 8] = u32x4{0, 0, 0, 0};
 }
 
 // ---------------------------------------------------------------------------
@@ -352,7 +348,6 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
   }
   using TL = TileLayout<D>;
   u32x4* tdst = a.tiles + (bh * a.n_tiles + tile) * TL::CHUNKS;
-  u32x4* kdst = tdst + r * TL::KROW;
 #pragma unroll
   for (int c = 0; c < RUN / 8; ++c) {
     u32x4 w0, w1;
@@ -363,12 +358,9 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     }
     const int c0 = (qq * RUN) / 8 + c;             // logical chunk, first half
     const int c1 = (D / 2 + qq * RUN) / 8 + c;     // logical chunk, second half
-    kdst[c0] = w0;
-    kdst[c1] = w1;
+    tdst[TL::k(r, c0)] = w0;
+    tdst[TL::k(r, c1)] = w1;
   }
-  // the pad chunks are written too (zeros), so every line of the tile image
-  // is written whole
-  if (qq == 0) kdst[D / 8] = u32x4{0, 0, 0, 0};
 
   __syncthreads();
   if constexpr (CHUNK) {
@@ -416,10 +408,11 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
       __syncthreads();
     }
   }
-  u32x4* vdst = tdst + TL::KCHUNKS;
+  // consecutive lanes write consecutive head-dim rows of one chunk: whole
+  // lines of the chunk-major image
   for (int ci = tid; ci < CHUNKS; ci += 256) {
-    const int d = ci / (BK / 8);
-    const int pc = ci % (BK / 8);  // logical chunk: 16-key group g16 = pc/2, half hh = pc%2
+    const int d = ci % D;
+    const int pc = ci / D;  // chunk: 16-key group g16 = pc/2, half hh = pc%2
     const int g16 = pc >> 1, hh = pc & 1;
     uint16_t e[8];
 #pragma unroll
@@ -430,8 +423,7 @@ __global__ __launch_bounds__(256) void kv_prep_kernel(KvPrepArgs a) {
     u32x4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = static_cast<uint32_t>(e[2 * i]) | (static_cast<uint32_t>(e[2 * i + 1]) << 16);
-    vdst[d * TL::VROW + pc] = w;
-    if (pc == 0) vdst[d * TL::VROW + BK / 8] = u32x4{0, 0, 0, 0};
+    tdst[TL::v(d, pc)] = w;
   }
 }
 

@@ -229,7 +229,7 @@ def test_rope_qknorm_argument_checks():
     assert f(ctypes.byref(p), -1, FAKE, 4096, None, 0, None, FAKE, None, 0, None) == 1
 
 
-TILE_BYTES = {128: (64 * 17 + 128 * 9) * 16, 64: (64 * 9 + 64 * 9) * 16}  # one 64-key tile image
+TILE_BYTES = {128: (64 * 16 + 128 * 8) * 16, 64: (64 * 8 + 64 * 8) * 16}  # one 64-key tile image (K rows, V^T rows)
 
 
 def _align(x):
