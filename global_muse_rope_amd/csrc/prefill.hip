@@ -317,9 +317,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 
   f32x16 o[MB][C::DB];
   float lsum[MB];
+  f32x4 lacc[MB];  // head width 64: row sums on the matrix cores
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
     lsum[mb] = 0.f;
+    lacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -403,6 +405,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   bf16x2 ones;
   ones[0] = static_cast<bf16_t>(1.0f);
   ones[1] = static_cast<bf16_t>(1.0f);
+  // Head width 64 is bound by vector issue (two exponentials per matrix
+  // item), so its row sums go to the matrix cores instead of v_dot2: one
+  // v_mfma_f32_16x16x32_bf16 per 16-key P fragment, with a constant A of
+  // ones and zeros.  That MFMA reads lane l of the fragment as column l % 16,
+  // keys 8 (l / 16) ..: A row i takes k-blocks 0 and 2 (i < 8) or 1 and 3
+  // (i >= 8), so output rows 0-7 hold the sums of columns 0-15 and rows 8-15
+  // those of columns 16-31, over all 16 keys.  The epilogue picks each lane's
+  // column from the accumulator layout (lane l holds rows 4 (l / 16) ..).
+  constexpr bool kRowsumMfma = D == 64;
+  bf16x8 aones;
+  {
+    const bool on = ((lane >> 4) & 1) == ((lane & 15) >> 3);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) aones[e] = static_cast<bf16_t>(on ? 1.0f : 0.0f);
+  }
 
   // Edge tiles (a wave-uniform flag) overwrite the logits of invisible keys
   // with -inf, in a branch taken only on those tiles.
@@ -491,7 +508,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       pr = __builtin_bit_cast(bf16x2, pw);
       p_out[mb][e >> 3][e & 7] = pr[0];
       p_out[mb][e >> 3][(e & 7) + 1] = pr[1];
-      lsum[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[mb], false);
+      if constexpr (!kRowsumMfma) lsum[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[mb], false);
     };
     if constexpr (EXP) {
 #pragma unroll
@@ -519,6 +536,13 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           o[mb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_in[mb][st], o[mb][db], 0, 0, 0);
+        if constexpr (kRowsumMfma) {
+          if (db == 0) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+              lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aones, p_in[mb][st], lacc[mb], 0, 0, 0);
+          }
+        }
       }
       fq[j % QD] = j + QD < NI ? frag(cur, j + QD) : frag(nxt, j + QD - NI);
       // the previous item's exponentials, packed one matrix item after they
@@ -657,7 +681,16 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   float* ost = reinterpret_cast<float*>(smem) + w * (MB * 32 * OROW);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const float ltot = lsum[mb] + __shfl_xor(lsum[mb], 32, kWave);
+    float ltot;
+    if constexpr (kRowsumMfma) {
+      // column l32 of this lane: lanes 0-15 and 48-63 hold their own, lanes
+      // 32-47 the sums of columns 16-31 that lanes 16-31 need, lanes 0-15
+      // those of columns 0-15 that lanes 32-47 need
+      const int src = lane < 16 ? lane : lane < 32 ? lane + 16 : lane < 48 ? lane - 32 : lane;
+      ltot = __shfl(lacc[mb][0], src, kWave);
+    } else {
+      ltot = lsum[mb] + __shfl_xor(lsum[mb], 32, kWave);
+    }
     if (split) {
       // a key piece hands on its unnormalized sums
       const int r = (w * MB + mb) * 32 + l32;
