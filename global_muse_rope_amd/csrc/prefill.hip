@@ -316,11 +316,9 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   const u32x4* tsrc = a.tiles + static_cast<int64_t>(bh) * a.n_tiles * TL::CHUNKS;
 
   f32x16 o[MB][C::DB];
-  float lsum[MB];
-  f32x4 lacc[MB];  // head width 64: row sums on the matrix cores
+  f32x4 lacc[MB];  // row sums, accumulated on the matrix cores (layout below)
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    lsum[mb] = 0.f;
     lacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
@@ -402,18 +400,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     if (tile + 3 <= tile_hi) gload(tile + 3, (rel + 3) % NBUF);
   };
 
-  bf16x2 ones;
-  ones[0] = static_cast<bf16_t>(1.0f);
-  ones[1] = static_cast<bf16_t>(1.0f);
-  // Head width 64 is bound by vector issue (two exponentials per matrix
-  // item), so its row sums go to the matrix cores instead of v_dot2: one
+  // Row sums on the matrix cores instead of vector dot products (head width
+  // 64 is bound by vector issue, two exponentials per matrix item): one
   // v_mfma_f32_16x16x32_bf16 per 16-key P fragment, with a constant A of
   // ones and zeros.  That MFMA reads lane l of the fragment as column l % 16,
   // keys 8 (l / 16) ..: A row i takes k-blocks 0 and 2 (i < 8) or 1 and 3
   // (i >= 8), so output rows 0-7 hold the sums of columns 0-15 and rows 8-15
   // those of columns 16-31, over all 16 keys.  The epilogue picks each lane's
   // column from the accumulator layout (lane l holds rows 4 (l / 16) ..).
-  constexpr bool kRowsumMfma = D == 64;
   bf16x8 aones;
   {
     const bool on = ((lane >> 4) & 1) == ((lane & 15) >> 3);
@@ -440,11 +434,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // A half-step works on 32 keys.  Its matrix-core items alternate
   //   K item i:  S_out += K(tile_q, half kb_q) fragment i  x  q_hat fragment i
   //   V item i:  O     += V^T(tile_v, half kb_v) fragment i  x  P_in
+  //              (and, on the first head-dim block, the row sums of P_in)
   // (a dependent MFMA chain on one accumulator runs at half rate, so the QK
   // chain is interleaved with the independent PV accumulators); between them
   // the vector ALUs turn S_in into P_out = exp2(S_in) (logits are bounded by
-  // 63.2 in log2 units, so no running maximum is needed) and accumulate the
-  // row sums.  sched_barrier(0) walls keep this order.
+  // 63.2 in log2 units, so no running maximum is needed).  sched_barrier(0)
+  // walls keep this order.
   //
   // LDS fragments stream through a queue of QD registers that runs
   // continuously across half-steps and tiles: the fragment of item j is read
@@ -508,7 +503,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       pr = __builtin_bit_cast(bf16x2, pw);
       p_out[mb][e >> 3][e & 7] = pr[0];
       p_out[mb][e >> 3][(e & 7) + 1] = pr[1];
-      if constexpr (!kRowsumMfma) lsum[mb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[mb], false);
     };
     if constexpr (EXP) {
 #pragma unroll
@@ -536,12 +530,10 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
           o[mb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, p_in[mb][st], o[mb][db], 0, 0, 0);
-        if constexpr (kRowsumMfma) {
-          if (db == 0) {
+        if (db == 0) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aones, p_in[mb][st], lacc[mb], 0, 0, 0);
-          }
+          for (int mb = 0; mb < MB; ++mb)
+            lacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aones, p_in[mb][st], lacc[mb], 0, 0, 0);
         }
       }
       fq[j % QD] = j + QD < NI ? frag(cur, j + QD) : frag(nxt, j + QD - NI);
@@ -561,8 +553,8 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       if constexpr (EXP && kLagPack) {
         // head width 128: one exponential per matrix item (16 per 16
         // items), so no item carries more vector work than the other wave's
-        // MFMA covers; each pair is packed (and its row sum taken as one
-        // packed dot product) on the item after its second exponential
+        // MFMA covers; each pair is packed on the item after its second
+        // exponential
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           float x = __builtin_amdgcn_exp2f(s_in[mb][j]);
@@ -681,16 +673,11 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   float* ost = reinterpret_cast<float*>(smem) + w * (MB * 32 * OROW);
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    float ltot;
-    if constexpr (kRowsumMfma) {
-      // column l32 of this lane: lanes 0-15 and 48-63 hold their own, lanes
-      // 32-47 the sums of columns 16-31 that lanes 16-31 need, lanes 0-15
-      // those of columns 0-15 that lanes 32-47 need
-      const int src = lane < 16 ? lane : lane < 32 ? lane + 16 : lane < 48 ? lane - 32 : lane;
-      ltot = __shfl(lacc[mb][0], src, kWave);
-    } else {
-      ltot = lsum[mb] + __shfl_xor(lsum[mb], 32, kWave);
-    }
+    // column l32 of this lane: lanes 0-15 and 48-63 hold their own, lanes
+    // 32-47 the sums of columns 16-31 that lanes 16-31 need, lanes 0-15
+    // those of columns 0-15 that lanes 32-47 need
+    const int src = lane < 16 ? lane : lane < 32 ? lane + 16 : lane < 48 ? lane - 32 : lane;
+    const float ltot = __shfl(lacc[mb][0], src, kWave);
     if (split) {
       // a key piece hands on its unnormalized sums
       const int r = (w * MB + mb) * 32 + l32;
