@@ -58,21 +58,49 @@ constexpr int kFragQueueD64 = 2;
 // their maxima)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// One wave's 64 x 16-byte copy from global memory straight into LDS
-// (global_load_lds_dwordx4; the LDS address comes from M0, uniform over the
-// wave).  The copy is counted by VM_CNT alone: the kernel waits for it with
-// an explicit vmcnt(0) before the barrier that publishes the tile.  Issued
-// through the builtin, the compiler treats it as a flat access that may
+// One wave's share of a tile copy: R consecutive rounds of 64 lanes x 16
+// bytes (1 KB each) from global memory straight into LDS
+// (global_load_lds_dwordx4).  The LDS address comes from M0, uniform over the
+// wave, and the global address is a scalar base plus a per-lane offset; the
+// instruction's immediate offset advances the global and the LDS address
+// alike, so all rounds share one base, one lane offset and one M0 value (one
+// M0 write per tile instead of one per round, and no per-round address
+// arithmetic in the tile loop).
+// The copies are counted by VM_CNT alone: the kernel waits for them with an
+// explicit vmcnt(0) before the barrier that publishes the tile.  Issued
+// through the builtin, the compiler treats each as a flat access that may
 // also touch LDS and, while one is in flight, turns every wait on an LDS
 // fragment read into lgkmcnt(0), draining the fragment queue twice per
-// half-tile.  Written as an instruction of its own the compiler keeps its
+// half-tile.  Written as instructions of their own the compiler keeps its
 // exact lgkmcnt(7) waits; the statement has no register outputs, and its
 // memory clobber keeps LDS accesses from moving across it.
-__device__ __forceinline__ void dma16_to_lds(const u32x4* src, void* lds_wave_base) {
+template <int R>
+__device__ __forceinline__ void dma_wave_share(const u32x4* wave_src, uint32_t lane_off, void* lds_wave_base) {
+  static_assert(R == 2 || R == 4, "1 KB rounds within the 4 KB immediate offset range");
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_wave_base)));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
-               : "memory", "m0");
+  const uint64_t p = reinterpret_cast<uint64_t>(wave_src);
+  // readfirstlane returns int: each half goes through uint32_t, so the low
+  // half is zero-extended, not sign-extended, into the 64-bit address
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(p >> 32)));
+  const uint64_t sp = (static_cast<uint64_t>(hi) << 32) | lo;
+  if constexpr (R == 4)
+    asm volatile(
+        "s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:3072" ::"v"(lane_off),
+        "s"(sp), "s"(m0)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %2\n\ts_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1\n\t"
+        "global_load_lds_dwordx4 %0, %1 offset:1024" ::"v"(lane_off),
+        "s"(sp), "s"(m0)
+        : "memory", "m0");
 }
 
 template <int D, int G, int NW, int MB>
@@ -331,12 +359,14 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // straight from global memory into LDS (global_load_lds_dwordx4: no register
   // staging, no LDS store instructions).  Each wave instruction copies 64
   // consecutive 16-byte chunks, so the LDS image of a tile equals its
-  // workspace image. ----
+  // workspace image.  Wave w copies the tile's chunks [w R 64, (w + 1) R 64)
+  // in R rounds of 1 KB. ----
+  constexpr int RND = TL::CHUNKS / C::THREADS;
+  static_assert(TL::CHUNKS % C::THREADS == 0, "a tile is whole rounds of every wave");
+  const uint32_t dma_lane = static_cast<uint32_t>(lane) * 16;
   auto gload = [&](int tile, int buf) {
-    const u32x4* src = tsrc + static_cast<int64_t>(tile) * TL::CHUNKS;
-#pragma unroll
-    for (int c = 0; c < TL::CHUNKS; c += C::THREADS)
-      if (c + w * 64 < TL::CHUNKS) dma16_to_lds(src + c + w * 64 + lane, tile_buf(buf) + c + w * 64);
+    const u32x4* src = tsrc + static_cast<int64_t>(tile) * TL::CHUNKS + w * (RND * 64);
+    dma_wave_share<RND>(src, dma_lane, tile_buf(buf) + w * (RND * 64));
   };
   // The first three tiles of the range start streaming into LDS before the
   // query prologue, so their latency overlaps the query loads.
@@ -397,7 +427,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    if (tile + 3 <= tile_hi) gload(tile + 3, (rel + 3) % NBUF);
+    if (tile + 3 <= tile_hi) gload(tile + 3, static_cast<unsigned>(rel + 3) % NBUF);
   };
 
   // Row sums on the matrix cores instead of vector dot products (head width
@@ -461,9 +491,12 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   auto half_at = [&](int tile_q, int kb_q, int tile_v, int kb_v) -> Half {
     Half hb;
     // key rows 32 kb_q on; V chunks (8 keys each) 4 kb_v on
-    hb.k = reinterpret_cast<const char*>(tile_buf((tile_q - tile_lo) % NBUF)) + k_lane + TL::k(32 * kb_q, 0) * 16;
-    hb.v = reinterpret_cast<const char*>(tile_buf((tile_v - tile_lo) % NBUF)) + v_lane +
-           (TL::v(0, 4 * kb_v) - TL::v(0, 0)) * 16;
+    // tiles at or after tile_lo: an unsigned remainder is a mask (the signed
+    // one cost a dozen scalar instructions per half-step)
+    const unsigned bk = static_cast<unsigned>(tile_q - tile_lo) % NBUF;
+    const unsigned bv = static_cast<unsigned>(tile_v - tile_lo) % NBUF;
+    hb.k = reinterpret_cast<const char*>(tile_buf(bk)) + k_lane + TL::k(32 * kb_q, 0) * 16;
+    hb.v = reinterpret_cast<const char*>(tile_buf(bv)) + v_lane + (TL::v(0, 4 * kb_v) - TL::v(0, 0)) * 16;
     return hb;
   };
   auto frag = [&](const Half& hb, int j) -> u32x4 {
@@ -685,16 +718,17 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
       if (h2 == 0 && t < a.T) a.part_l[part_row(t, hk * G + (r % G))] = ltot;
     }
     const float inv = split ? 1.0f : __builtin_amdgcn_rcpf(ltot);
-    float ss = 0.f;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        o[mb][db][i] *= inv;
-        ss += o[mb][db][i] * o[mb][db][i];
-      }
+      for (int i = 0; i < 16; ++i) o[mb][db][i] *= inv;
     float rsn = 1.0f;
     if (a.out_norm && !split) {
+      float ss = 0.f;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ss += o[mb][db][i] * o[mb][db][i];
       ss += __shfl_xor(ss, 32, kWave);
       rsn = __builtin_amdgcn_rsqf(ss * (1.0f / D) + a.out_eps);
     }
