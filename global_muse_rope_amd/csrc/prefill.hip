@@ -499,6 +499,18 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     hb.v = reinterpret_cast<const char*>(tile_buf(bv)) + v_lane + (TL::v(0, 4 * kb_v) - TL::v(0, 0)) * 16;
     return hb;
   };
+  // The same from ring byte offsets (NBUF and the tile size are powers of
+  // two, so an offset wraps by masking): the tile loop steps three offsets
+  // instead of recomputing them from tile indices.
+  constexpr unsigned TB = TL::CHUNKS * 16;
+  constexpr unsigned RING = NBUF * TB - TB;
+  static_assert((NBUF & (NBUF - 1)) == 0 && (TB & (TB - 1)) == 0, "ring offsets wrap by masking");
+  auto half_off = [&](unsigned oq, int kb_q, unsigned ov, int kb_v) -> Half {
+    Half hb;
+    hb.k = reinterpret_cast<const char*>(smem) + oq + k_lane + TL::k(32 * kb_q, 0) * 16;
+    hb.v = reinterpret_cast<const char*>(smem) + ov + v_lane + (TL::v(0, 4 * kb_v) - TL::v(0, 0)) * 16;
+    return hb;
+  };
   auto frag = [&](const Half& hb, int j) -> u32x4 {
     const int i = j >> 1;
     // K item i: head dims 16 i .. 16 i + 15 (chunks 2 i, 2 i + 1)
@@ -650,18 +662,21 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     prime(h0);
     half_step(h0, half_at(tile_lo, 1, tile_lo, 1), sc, pp, sn, pc, std::true_type{}, std::false_type{});
   }
+  unsigned ocur = 0;  // ring offset of tile t's buffer
   for (int t = tile_lo; t <= tile_hi; ++t) {
     if (idle) {
       advance(t);
       continue;
     }
-    const bool masked = t < m_lo || t >= m_hi;
+    // edge tiles: t < m_lo or t >= m_hi (m_lo <= m_hi)
+    const bool masked = static_cast<unsigned>(t - m_lo) >= static_cast<unsigned>(m_hi - m_lo);
     const int k0 = t * kKeyTile;
-    const int tprev = t > tile_lo ? t - 1 : t;
-    const int tnext = t < tile_hi ? t + 1 : t;
-    const Half ha = half_at(t, 1, tprev, 1);
-    const Half hb = half_at(tnext, 0, t, 0);
-    const Half hn = half_at(tnext, 1, t, 1);   // half A of the next tile (or the drain)
+    // tiles t - 1 and t + 1, held at the range's ends
+    const unsigned oprev = t > tile_lo ? (ocur - TB) & RING : ocur;
+    const unsigned onext = t < tile_hi ? (ocur + TB) & RING : ocur;
+    const Half ha = half_off(ocur, 1, oprev, 1);
+    const Half hb = half_off(onext, 0, ocur, 0);
+    const Half hn = half_off(onext, 1, ocur, 1);   // half A of the next tile (or the drain)
     mask_logits(sc, masked, k0);
     // S(t, 32..63) and O += P(t-1, 32..63) V  ||  P(t, 0..31)
     half_step(ha, hb, sn, pp, sc, pc, std::true_type{}, std::true_type{});
@@ -669,6 +684,7 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     // S(t+1, 0..31) and O += P(t, 0..31) V  ||  P(t, 32..63)
     half_step(hb, hn, sc, pc, sn, pp, std::true_type{}, std::true_type{});
     advance(t);
+    ocur = (ocur + TB) & RING;
   }
   // drain: O += P(last, 32..63) V only
   if (!idle) {
