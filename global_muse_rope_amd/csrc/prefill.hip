@@ -686,6 +686,25 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
     advance(t);
     ocur = (ocur + TB) & RING;
   }
+  constexpr int CPC = D / 8;                     // 8-value chunks per column
+  constexpr int NCH = MB * 32 * CPC;             // chunks per wave
+  static_assert(NCH % kWave == 0, "whole chunk rounds");
+  // Gate rows of the chunks this lane stores in the epilogue, loaded before
+  // the drain (whose P V has no use for the query operands and logits, so
+  // their registers hold these) so that their latency overlaps the drain and
+  // the staging.
+  u32x4 gpre[NCH / kWave];
+#pragma unroll
+  for (int it = 0; it < NCH / kWave; ++it) {
+    const int k = it * kWave + lane;
+    const int cl = k / CPC, d0 = (k % CPC) * 8;
+    const int r = w * MB * 32 + cl;
+    const int t = t0 + r / G;
+    gpre[it] = u32x4{0u, 0u, 0u, 0u};
+    if (!split && t < a.T)
+      gpre[it] = *reinterpret_cast<const u32x4*>(a.gate + b * a.g_sb + static_cast<int64_t>(t) * a.g_st +
+                                                 static_cast<int64_t>(hk * G + (r % G)) * D + d0);
+  }
   // drain: O += P(last, 32..63) V only
   if (!idle) {
     const Half hd = half_at(tile_hi, 1, tile_hi, 1);
@@ -701,23 +720,6 @@ __global__ __launch_bounds__(NW * 64) void prefill_kernel(PrefillArgs a) {
   // stores would leave every 128-byte line written in 16-byte pieces by
   // different instructions; staged, each lane loads 8 consecutive gate values
   // and stores 8 consecutive outputs, and a wave covers whole lines. ----
-  constexpr int CPC = D / 8;                     // 8-value chunks per column
-  constexpr int NCH = MB * 32 * CPC;             // chunks per wave
-  static_assert(NCH % kWave == 0, "whole chunk rounds");
-  // Gate rows of the chunks this lane stores below, loaded before the
-  // staging so their latency overlaps it.
-  u32x4 gpre[NCH / kWave];
-#pragma unroll
-  for (int it = 0; it < NCH / kWave; ++it) {
-    const int k = it * kWave + lane;
-    const int cl = k / CPC, d0 = (k % CPC) * 8;
-    const int r = w * MB * 32 + cl;
-    const int t = t0 + r / G;
-    gpre[it] = u32x4{0u, 0u, 0u, 0u};
-    if (!split && t < a.T)
-      gpre[it] = *reinterpret_cast<const u32x4*>(a.gate + b * a.g_sb + static_cast<int64_t>(t) * a.g_st +
-                                                 static_cast<int64_t>(hk * G + (r % G)) * D + d0);
-  }
   __syncthreads();                              // every wave is done with the tiles
   float* ost = reinterpret_cast<float*>(smem) + w * (MB * 32 * OROW);
 #pragma unroll
